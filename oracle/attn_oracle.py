@@ -1,0 +1,320 @@
+"""Plain fp64 CPU oracle for masked multi-head attention and split-KV decode.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(the HIP library and its Python binding) never imports, links or calls it, and
+this module imports nothing from the product package: the two share no code.
+
+Everything here is written out from the definitions on the pages, slowly and
+plainly, in float64 NumPy:
+
+* the attention statement: the output is the softmax of the scaled, masked
+  query-key scores applied to the values (Tylo.jl "Primitives", ``attention!``;
+  vllm_mlx.attention, ``MLXAttentionImpl.forward`` calling
+  ``scaled_dot_product_attention`` with ``scale``);
+* the default scale 1/sqrt(Dk) (Tylo.jl "Primitives", ``flex_attention!``
+  keyword ``qk_scale``);
+* masks are additive, 0 where a pair attends and -inf where it is blocked, of
+  shape (1, 1, Sq, offset + Sq) (mlx-arsenal "Attention", ``causal_mask`` and
+  ``sliding_window_mask``, and the ``video_masks`` module note);
+* causal means key position <= query position, with absolute positions shifted
+  by ``input_pos`` (Tylo.jl "Primitives", ``CausalMask`` and ``attention!``
+  keyword ``input_pos``);
+* a sliding window of ``window_size`` lets a query see at most that many
+  previous positions, itself included (mlx-arsenal "Attention",
+  ``sliding_window_mask``);
+* keys at or past ``k_lengths[b]`` are invalid (Tylo.jl "Primitives",
+  ``attention!`` keyword ``k_lengths``);
+* grouped-query attention: Heads is a multiple of Heads_KV (Tylo.jl
+  "Primitives", ``flex_attention!``);
+* the saved softmax statistics M (row max) and L (row sum of exp) (Tylo.jl
+  "Primitives", ``attention!`` keyword ``checkpoints``), returned here as
+  LSE = M + ln L;
+* split-KV decode: one query per head and sequence, valid KV length per
+  sequence, the cache processed as ``n_splits`` slices (Tylo.jl "Primitives",
+  ``decode_attention!``).
+
+Readings taken where the pages are silent or disagree (each is listed in the
+repository's design notes):
+
+* window width: the mlx-arsenal reading (at most ``window`` keys, itself
+  included), i.e. keys j with p - window + 1 <= j <= p.  Tylo's
+  ``SlidingWindowMask(w)`` (q - w <= kv <= q) is this mask with window = w + 1;
+* GQA grouping: query head h reads KV head h // (H // Hkv);
+* a window is only defined together with causal masking; window > 0 without
+  causal is rejected;
+* a row with no allowed key has output 0 and LSE = -inf;
+* ``k_lengths`` / ``lengths`` values are clamped to [0, Sk];
+* the decode slices hold C = ceil(ceil(len / TILE_N) / n_splits) * TILE_N keys
+  each; the slice merge weighs each slice by exp(LSE_s - max LSE).
+
+Layouts are row-major: Q/O (B, H, Sq, D), K/V (B, Hkv, Sk, D), LSE (B, H, Sq);
+decode Q/O (B, H, D), K/V (B, Hkv, Smax, D).  This is Tylo's column-major
+(D, S, H, B) read in row-major order.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+# Tile classes of the block plan (Tylo.jl "Primitives", ``BlockMask``: per
+# query block, the KV blocks holding any unmasked element, and which of those
+# are fully unmasked).
+TILE_EMPTY = 0
+TILE_PARTIAL = 1
+TILE_FULL = 2
+
+
+# ---------------------------------------------------------------------------
+# masks
+# ---------------------------------------------------------------------------
+
+def _check_mask_args(causal: bool, window: int) -> None:
+    if window > 0 and not causal:
+        raise ValueError("a sliding window is defined only for causal attention")
+
+
+def allowed_mask(Sq: int, Sk: int, causal: bool = False, window: int = 0,
+                 input_pos: int = 0, k_len: int | None = None) -> np.ndarray:
+    """Boolean (Sq, Sk) matrix: True where query i may attend to key j.
+
+    Query i sits at absolute position p = input_pos + i (Tylo ``attention!``
+    keyword ``input_pos``; mlx-arsenal ``causal_mask`` offset = cached KV
+    length).  Conditions, all of which must hold:
+
+    * j < k_len                 (``k_lengths``, clamped to [0, Sk])
+    * j <= p        if causal   (``CausalMask``: q >= kv)
+    * j >= p - window + 1  if window > 0  (``sliding_window_mask``: at most
+      ``window`` positions including itself)
+    """
+    _check_mask_args(causal, window)
+    kl = Sk if k_len is None else min(max(int(k_len), 0), Sk)
+    i = np.arange(Sq, dtype=np.int64)[:, None]
+    j = np.arange(Sk, dtype=np.int64)[None, :]
+    p = input_pos + i
+    ok = j < kl
+    if causal:
+        ok = ok & (j <= p)
+    if window > 0:
+        ok = ok & (j >= p - window + 1)
+    return np.broadcast_to(ok, (Sq, Sk)).copy()
+
+
+def additive_mask(seq_len: int, offset: int = 0, window: int = 0) -> np.ndarray:
+    """The mlx-arsenal causal / sliding-window mask as an additive array.
+
+    Shape (1, 1, seq_len, offset + seq_len); 0.0 where attention is allowed and
+    -inf where it is blocked (mlx-arsenal "Attention", ``causal_mask`` and
+    ``sliding_window_mask``).  The queries are the last ``seq_len`` positions
+    of an ``offset + seq_len`` long key sequence.
+    """
+    ok = allowed_mask(seq_len, offset + seq_len, causal=True, window=window,
+                      input_pos=offset)
+    m = np.where(ok, 0.0, NEG_INF)
+    return m.reshape(1, 1, seq_len, offset + seq_len)
+
+
+def tile_plan_ref(Sq: int, Sk: int, causal: bool, window: int, input_pos: int,
+                  k_len: int | None, tile_m: int, tile_n: int) -> np.ndarray:
+    """Per (query tile, key tile) class: empty, partial or full.
+
+    A tile covers the existing query rows [qt*tile_m, min(Sq, (qt+1)*tile_m))
+    and the nominal key range [kt*tile_n, (kt+1)*tile_n); keys at or past Sk do
+    not exist and so are never allowed.  Empty: no allowed pair.  Full: every
+    (existing row, nominal key) pair allowed.  Partial: anything else.  This is
+    Tylo's ``BlockMask`` notion evaluated by brute force from the element mask.
+    """
+    nqt = -(-Sq // tile_m)
+    nkt = -(-Sk // tile_n)
+    pad_k = nkt * tile_n
+    ok = np.zeros((Sq, pad_k), dtype=bool)
+    ok[:, :Sk] = allowed_mask(Sq, Sk, causal, window, input_pos, k_len)
+    plan = np.empty((nqt, nkt), dtype=np.int8)
+    for qt in range(nqt):
+        rows = ok[qt * tile_m:min(Sq, (qt + 1) * tile_m)]
+        for kt in range(nkt):
+            blk = rows[:, kt * tile_n:(kt + 1) * tile_n]
+            if not blk.any():
+                plan[qt, kt] = TILE_EMPTY
+            elif blk.all():
+                plan[qt, kt] = TILE_FULL
+            else:
+                plan[qt, kt] = TILE_PARTIAL
+    return plan
+
+
+# ---------------------------------------------------------------------------
+# attention, step by step
+# ---------------------------------------------------------------------------
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S = scale * q @ k^T for q (n, D), k (Sk, D)."""
+    return scale * (q @ k.T)
+
+
+def apply_mask(s: np.ndarray, ok: np.ndarray) -> np.ndarray:
+    """Blocked pairs get -inf (additive 0 / -inf mask)."""
+    return np.where(ok, s, NEG_INF)
+
+
+def softmax_stats(s: np.ndarray):
+    """Numerically stable row softmax of masked scores.
+
+    Returns (P, M, L): M the row max, L = sum exp(s - M), P = exp(s - M) / L.
+    A row with no finite score has M = -inf, L = 0 and P = 0 (the reading for
+    fully masked rows).
+    """
+    M = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], NEG_INF)
+    finite = np.isfinite(M)
+    M_safe = np.where(finite, M, 0.0)
+    E = np.exp(s - M_safe[:, None])          # exp(-inf) = 0 for blocked pairs
+    E[~finite] = 0.0
+    L = E.sum(axis=1)
+    P = np.zeros_like(E)
+    P[finite] = E[finite] / L[finite, None]
+    return P, M, L
+
+
+def combine(P: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """O = P @ V."""
+    return P @ v
+
+
+def lse_from_stats(M: np.ndarray, L: np.ndarray) -> np.ndarray:
+    """LSE = M + ln L; -inf for a row without allowed keys."""
+    out = np.full(M.shape, NEG_INF)
+    ok = L > 0
+    out[ok] = M[ok] + np.log(L[ok])
+    return out
+
+
+def attn_ref(Q, K, V, causal: bool = False, window: int = 0, input_pos: int = 0,
+             k_lengths=None, scale: float | None = None, heads=None, rows=None,
+             row_chunk: int = 1024):
+    """Masked grouped-query attention forward in float64.
+
+    Q (B, H, Sq, D); K, V (B, Hkv, Sk, D); returns (O, LSE) with O (B, H, Sq, D)
+    float64 and LSE (B, H, Sq) float64.  ``heads`` (iterable of (b, h)) and
+    ``rows`` (array of query indices) restrict the work to a sample; entries
+    not computed are left as NaN.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, Sq, D = Q.shape
+    Bk, Hkv, Sk, Dk = K.shape
+    if Bk != B or Dk != D or V.shape[:3] != K.shape[:3]:
+        raise ValueError("shape mismatch between Q, K and V")
+    if Hkv <= 0 or H % Hkv != 0:
+        raise ValueError("Heads must be a multiple of Heads_KV")
+    _check_mask_args(causal, window)
+    G = H // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    Dv = V.shape[3]
+    O = np.full((B, H, Sq, Dv), np.nan)
+    LSE = np.full((B, H, Sq), np.nan)
+    row_idx = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    masks = {}
+    for b, h in pairs:
+        if b not in masks:
+            kl = None if k_lengths is None else int(k_lengths[b])
+            masks[b] = allowed_mask(Sq, Sk, causal, window, input_pos, kl)
+        g = h // G
+        for c0 in range(0, len(row_idx), row_chunk):
+            r = row_idx[c0:c0 + row_chunk]
+            s = apply_mask(scores(Q[b, h, r], K[b, g], scale), masks[b][r])
+            P, M, L = softmax_stats(s)
+            O[b, h, r] = combine(P, V[b, g])
+            LSE[b, h, r] = lse_from_stats(M, L)
+    return O, LSE
+
+
+def decode_ref(Q, K, V, lengths, scale: float | None = None, batches=None):
+    """Single-query decode attention in float64: the plain definition.
+
+    Q (B, H, D); K, V (B, Hkv, Smax, D); lengths (B,).  Sequence b attends to
+    its keys j < clamp(lengths[b], 0, Smax) (Tylo ``decode_attention!``;
+    vllm_mlx ``MLXAttentionMetadata.seq_lens``).  The result does not depend on
+    how the cache is split.  Returns (O (B, H, D), LSE (B, H)).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, D = Q.shape
+    _, Hkv, Smax, _ = K.shape
+    if H % Hkv != 0:
+        raise ValueError("Heads must be a multiple of Heads_KV")
+    G = H // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    O = np.full((B, H, V.shape[3]), np.nan)
+    LSE = np.full((B, H), np.nan)
+    for b in (range(B) if batches is None else batches):
+        n = min(max(int(lengths[b]), 0), Smax)
+        for h in range(H):
+            g = h // G
+            s = scores(Q[b, h][None, :], K[b, g, :n], scale)
+            P, M, L = softmax_stats(s)
+            O[b, h] = combine(P, V[b, g, :n])[0] if n else 0.0
+            LSE[b, h] = lse_from_stats(M, L)[0]
+    return O, LSE
+
+
+def split_bounds(length: int, n_splits: int, tile_n: int):
+    """Key ranges of the decode slices: C = ceil(ceil(len/TILE_N)/n_splits)*TILE_N."""
+    tiles = -(-length // tile_n)
+    per = -(-tiles // n_splits) * tile_n
+    return [(s * per, min((s + 1) * per, length)) for s in range(n_splits)]
+
+
+def decode_split_ref(Q, K, V, lengths, n_splits: int, tile_n: int = 64,
+                     scale: float | None = None):
+    """Flash-Decoding in float64: per-slice softmax, then an LSE-weighted merge.
+
+    Each slice s yields a normalised partial output O_s and LSE_s over its keys
+    (LSE_s = -inf for an empty slice).  The merge takes M = max_s LSE_s,
+    w_s = exp(LSE_s - M) and O = sum_s w_s O_s / sum_s w_s, which is the
+    softmax over the union of the slices.  Used to pin the merge algebra.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, D = Q.shape
+    _, Hkv, Smax, _ = K.shape
+    G = H // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    O = np.zeros((B, H, V.shape[3]))
+    LSE = np.full((B, H), NEG_INF)
+    for b in range(B):
+        n = min(max(int(lengths[b]), 0), Smax)
+        for h in range(H):
+            g = h // G
+            parts = []
+            for lo, hi in split_bounds(n, n_splits, tile_n):
+                if hi <= lo:
+                    parts.append((np.zeros(V.shape[3]), NEG_INF))
+                    continue
+                s = scores(Q[b, h][None, :], K[b, g, lo:hi], scale)
+                P, M, L = softmax_stats(s)
+                parts.append((combine(P, V[b, g, lo:hi])[0], lse_from_stats(M, L)[0]))
+            lses = np.array([p[1] for p in parts])
+            Mx = lses.max()
+            if not np.isfinite(Mx):
+                continue
+            w = np.exp(lses - Mx)
+            O[b, h] = sum(wi * oi for wi, (oi, _) in zip(w, parts)) / w.sum()
+            LSE[b, h] = Mx + np.log(w.sum())
+    return O, LSE
+
+
+def allowed_pairs(Sq: int, Sk: int, causal: bool, window: int, input_pos: int,
+                  k_len: int | None) -> int:
+    """Number of allowed (query, key) pairs, by counting the mask."""
+    return int(allowed_mask(Sq, Sk, causal, window, input_pos, k_len).sum())

@@ -1,0 +1,475 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+None of these compare the oracle with itself through a retyped formula: each
+check comes from a hand-worked example (tests/golden/), a closed form, an
+invariant the pages state, an independent route (pure-Python / mpmath brute
+force, torch's own SDPA in float64), or a special case with a known answer.
+``test_planted_mistakes`` plants plausible bugs in the oracle and checks that
+at least one pin catches each.
+"""
+
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+from oracle import attn_oracle as ora
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _num(x):
+    """Golden fixtures spell irrational entries as short expressions."""
+    if x is None:
+        return -math.inf
+    if isinstance(x, (int, float)):
+        return float(x)
+    e = math.e
+    table = {
+        "2ln3": 2 * math.log(3.0), "ln4": math.log(4.0), "ln(e+1)": math.log(e + 1),
+        "4e/(e+1)": 4 * e / (e + 1), "4/(e+1)": 4 / (e + 1), "8e/(e+1)": 8 * e / (e + 1),
+    }
+    return table[x]
+
+
+# ---------------------------------------------------------------------------
+# masks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", _load("masks.json")["cases"], ids=lambda c: c["name"])
+def test_mask_golden(case):
+    m = ora.additive_mask(case["seq_len"], case["offset"], case["window"])
+    want = np.array([[_num(x) for x in row] for row in case["mask"]])
+    assert m.shape == (1, 1, case["seq_len"], case["offset"] + case["seq_len"])
+    np.testing.assert_array_equal(m[0, 0], want)
+
+
+@pytest.mark.parametrize("seq_len,offset", [(1, 0), (7, 0), (5, 3), (16, 100)])
+def test_mask_shape_values_lower_triangular(seq_len, offset):
+    m = ora.additive_mask(seq_len, offset)
+    assert m.shape == (1, 1, seq_len, offset + seq_len)
+    assert set(np.unique(m[0, 0]).tolist()) <= {0.0, -math.inf}
+    if offset == 0:
+        np.testing.assert_array_equal(m[0, 0] == 0, np.tri(seq_len, dtype=bool))
+
+
+def _row_count_closed_form(p, kl, causal, window):
+    hi = min(p, kl - 1) if causal else kl - 1
+    lo = max(0, p - window + 1) if window > 0 else 0
+    return max(0, hi - lo + 1)
+
+
+@pytest.mark.parametrize("Sq,Sk,causal,window,ip,kl", [
+    (33, 33, True, 0, 0, 33), (20, 50, True, 7, 30, 50), (20, 50, True, 7, 30, 41),
+    (9, 9, False, 0, 0, 5), (40, 64, True, 1, 24, 64), (16, 16, True, 100, 0, 16),
+    (12, 30, True, 5, -3, 30), (12, 30, True, 0, 40, 30), (8, 8, True, 4, 0, 0),
+])
+def test_mask_row_counts(Sq, Sk, causal, window, ip, kl):
+    ok = ora.allowed_mask(Sq, Sk, causal, window, ip, kl)
+    for i in range(Sq):
+        n = int(ok[i].sum())
+        assert n == _row_count_closed_form(ip + i, kl, causal, window)
+        if window > 0:
+            assert n <= window
+        if ok[i].any():  # allowed keys form one contiguous run
+            js = np.nonzero(ok[i])[0]
+            assert js[-1] - js[0] + 1 == len(js)
+
+
+def test_window_equals_tylo_form():
+    # Tylo's SlidingWindowMask(w) attends q - w <= kv <= q: our window w + 1.
+    for w in range(0, 6):
+        ok = ora.allowed_mask(12, 20, True, w + 1, 8, 20)
+        q = 8 + np.arange(12)[:, None]
+        kv = np.arange(20)[None, :]
+        np.testing.assert_array_equal(ok, (q - w <= kv) & (kv <= q))
+
+
+def test_window_requires_causal():
+    with pytest.raises(ValueError):
+        ora.allowed_mask(4, 4, causal=False, window=2)
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def _closed_form_inputs():
+    g = _load("closed_form.json")
+    q = np.array([[_num(x) for x in r] for r in g["q"]])
+    k = np.array([[_num(x) for x in r] for r in g["k"]])
+    v = np.array([[_num(x) for x in r] for r in g["v"]])
+    return g, q, k, v
+
+
+@pytest.mark.parametrize("mode", ["noncausal", "causal"])
+def test_closed_form_attention(mode):
+    g, q, k, v = _closed_form_inputs()
+    O, LSE = ora.attn_ref(q[None, None], k[None, None], v[None, None],
+                          causal=(mode == "causal"))
+    want_o = np.array([[_num(x) for x in r] for r in g[mode]["O"]])
+    want_l = np.array([_num(x) for x in g[mode]["LSE"]])
+    np.testing.assert_allclose(O[0, 0], want_o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(LSE[0, 0], want_l, rtol=0, atol=1e-13)
+
+
+def test_closed_form_gqa_two_heads_share_kv():
+    g, q, k, v = _closed_form_inputs()
+    Q = np.stack([q, q[::-1]])[None]            # H = 2 query heads
+    O, LSE = ora.attn_ref(Q, k[None, None], v[None, None], causal=False)
+    want = np.array([[_num(x) for x in r] for r in g["noncausal"]["O"]])
+    np.testing.assert_allclose(O[0, 0], want, atol=1e-13)
+    np.testing.assert_allclose(O[0, 1], want[::-1], atol=1e-13)
+
+
+def test_closed_form_decode():
+    g, q, k, v = _closed_form_inputs()
+    Q = np.stack([q[1], q[1]])[:, None, :]       # (B=2, H=1, D)
+    K = np.stack([k, k])[:, None]                # (B=2, Hkv=1, Smax=2, D)
+    V = np.stack([v, v])[:, None]
+    lengths = np.array(g["decode"]["lengths"])
+    want_o = np.array([[_num(x) for x in r] for r in g["decode"]["O"]])
+    want_l = np.array([_num(x) for x in g["decode"]["LSE"]])
+    for fn in (lambda: ora.decode_ref(Q, K, V, lengths),
+               lambda: ora.decode_split_ref(Q, K, V, lengths, n_splits=2, tile_n=1)):
+        O, LSE = fn()
+        np.testing.assert_allclose(O[:, 0], want_o, atol=1e-13)
+        np.testing.assert_allclose(LSE[:, 0], want_l, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# brute force (pure Python, mpmath at 50 digits)
+# ---------------------------------------------------------------------------
+
+def _brute(Q, K, V, causal, window, ip, k_lengths):
+    """Attention by explicit loops: for every query, sum exp(score) over the
+    keys the masks allow, weights = exp(score) / sum, no max subtraction."""
+    mpmath.mp.dps = 50
+    B, H, Sq, D = Q.shape
+    Hkv, Sk = K.shape[1], K.shape[2]
+    G = H // Hkv
+    O = np.zeros((B, H, Sq, V.shape[3]))
+    L = np.zeros((B, H, Sq))
+    for b in range(B):
+        kl = Sk if k_lengths is None else min(max(int(k_lengths[b]), 0), Sk)
+        for h in range(H):
+            kvh = h // G
+            for i in range(Sq):
+                pos = ip + i
+                keys = [j for j in range(Sk)
+                        if j < kl and (not causal or j <= pos)
+                        and (window <= 0 or pos - j < window)]
+                if not keys:
+                    L[b, h, i] = -math.inf
+                    continue
+                sc = {j: mpmath.mpf(mpmath.fsum(mpmath.mpf(float(Q[b, h, i, d])) * mpmath.mpf(float(K[b, kvh, j, d]))
+                                                for d in range(D))) / mpmath.sqrt(D)
+                      for j in keys}
+                w = {j: mpmath.exp(sc[j]) for j in keys}
+                tot = mpmath.fsum(w.values())
+                for d in range(V.shape[3]):
+                    O[b, h, i, d] = float(mpmath.fsum(w[j] * mpmath.mpf(float(V[b, kvh, j, d]))
+                                                      for j in keys) / tot)
+                L[b, h, i] = float(mpmath.log(tot))
+    return O, L
+
+
+BRUTE_CASES = [
+    dict(B=1, H=2, Hkv=1, Sq=5, Sk=5, D=4, causal=True, window=0, ip=0, kl=None),
+    dict(B=2, H=4, Hkv=2, Sq=3, Sk=9, D=8, causal=True, window=4, ip=6, kl=[9, 8]),
+    dict(B=1, H=3, Hkv=3, Sq=6, Sk=7, D=3, causal=False, window=0, ip=0, kl=[5]),
+    dict(B=2, H=2, Hkv=1, Sq=4, Sk=6, D=5, causal=True, window=0, ip=-2, kl=[6, 0]),
+]
+
+
+@pytest.mark.parametrize("c", BRUTE_CASES, ids=lambda c: f"S{c['Sq']}x{c['Sk']}w{c['window']}")
+def test_bruteforce_mpmath(c):
+    rng = np.random.default_rng(11)
+    Q = rng.standard_normal((c["B"], c["H"], c["Sq"], c["D"]))
+    K = rng.standard_normal((c["B"], c["Hkv"], c["Sk"], c["D"]))
+    V = rng.standard_normal((c["B"], c["Hkv"], c["Sk"], c["D"]))
+    O, LSE = ora.attn_ref(Q, K, V, c["causal"], c["window"], c["ip"], c["kl"])
+    Ob, Lb = _brute(Q, K, V, c["causal"], c["window"], c["ip"], c["kl"])
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isinf(LSE), np.isinf(Lb))
+    fin = np.isfinite(Lb)
+    np.testing.assert_allclose(LSE[fin], Lb[fin], rtol=0, atol=1e-12)
+    # rows with nothing allowed: zero output (reading for empty rows)
+    assert np.all(O[~fin] == 0.0)
+
+
+def test_decode_bruteforce():
+    rng = np.random.default_rng(12)
+    B, H, Hkv, S, D = 3, 4, 2, 9, 6
+    Q = rng.standard_normal((B, H, D))
+    K = rng.standard_normal((B, Hkv, S, D))
+    V = rng.standard_normal((B, Hkv, S, D))
+    lengths = np.array([9, 1, 4])
+    O, LSE = ora.decode_ref(Q, K, V, lengths)
+    for b in range(B):
+        Ob, Lb = _brute(Q[b][None, :, None], K[b][None], V[b][None], False, 0, 0, [lengths[b]])
+        np.testing.assert_allclose(O[b], Ob[0, :, 0], atol=1e-12)
+        np.testing.assert_allclose(LSE[b], Lb[0, :, 0], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# library cross-check: torch SDPA in float64 on CPU
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,Hkv,Sq,Sk,D,causal,window,ip", [
+    (1, 4, 4, 128, 128, 64, True, 0, 0),
+    (2, 8, 2, 64, 96, 32, True, 0, 32),
+    (1, 4, 1, 48, 80, 16, True, 20, 32),
+    (1, 2, 2, 64, 64, 32, False, 0, 0),
+])
+def test_against_torch_sdpa_fp64(B, H, Hkv, Sq, Sk, D, causal, window, ip):
+    gen = torch.Generator().manual_seed(3)
+    q = torch.randn(B, H, Sq, D, generator=gen, dtype=torch.float64)
+    k = torch.randn(B, Hkv, Sk, D, generator=gen, dtype=torch.float64)
+    v = torch.randn(B, Hkv, Sk, D, generator=gen, dtype=torch.float64)
+    i = torch.arange(Sq)[:, None] + ip
+    j = torch.arange(Sk)[None, :]
+    m = torch.ones(Sq, Sk, dtype=torch.bool)
+    if causal:
+        m &= j <= i
+    if window:
+        m &= j > i - window
+    G = H // Hkv
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k.repeat_interleave(G, 1), v.repeat_interleave(G, 1), attn_mask=m)
+    O, _ = ora.attn_ref(q.numpy(), k.numpy(), v.numpy(), causal, window, ip)
+    np.testing.assert_allclose(O, ref.numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# invariants and special cases
+# ---------------------------------------------------------------------------
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_gqa_equals_repeated_kv_heads():
+    Q, K, V = _rand((2, 8, 17, 16), 1), _rand((2, 2, 23, 16), 2), _rand((2, 2, 23, 16), 3)
+    O, L = ora.attn_ref(Q, K, V, True, 5, 6, [23, 11])
+    Od, Ld = ora.attn_ref(Q, np.repeat(K, 4, axis=1), np.repeat(V, 4, axis=1), True, 5, 6, [23, 11])
+    np.testing.assert_allclose(O, Od, atol=1e-14)
+    np.testing.assert_allclose(L, Ld, atol=1e-14)
+
+
+def test_constant_v_gives_constant_output():
+    Q, K = _rand((1, 2, 20, 8), 4), _rand((1, 2, 20, 8), 5)
+    V = np.broadcast_to(np.arange(8.0) - 3.5, (1, 2, 20, 8))
+    O, _ = ora.attn_ref(Q, K, V, True, 6, 0)
+    np.testing.assert_allclose(O, V[:, :, :20], atol=1e-13)
+
+
+def test_zero_query_uniform_weights():
+    Sq, Sk, W, ip = 10, 30, 7, 15
+    Q = np.zeros((1, 1, Sq, 8))
+    K, V = _rand((1, 1, Sk, 8), 6), _rand((1, 1, Sk, 8), 7)
+    O, L = ora.attn_ref(Q, K, V, True, W, ip)
+    for i in range(Sq):
+        p = ip + i
+        js = list(range(max(0, p - W + 1), min(p, Sk - 1) + 1))
+        np.testing.assert_allclose(O[0, 0, i], V[0, 0, js].mean(axis=0), atol=1e-13)
+        np.testing.assert_allclose(L[0, 0, i], math.log(len(js)), atol=1e-13)
+
+
+def test_single_allowed_key():
+    Q, K, V = _rand((1, 2, 6, 8), 8), _rand((1, 2, 12, 8), 9), _rand((1, 2, 12, 8), 10)
+    O, L = ora.attn_ref(Q, K, V, True, 1, 3)          # window 1: only key p
+    for h in range(2):
+        for i in range(6):
+            j = 3 + i
+            np.testing.assert_allclose(O[0, h, i], V[0, h, j], atol=1e-14)
+            np.testing.assert_allclose(L[0, h, i], Q[0, h, i] @ K[0, h, j] / math.sqrt(8), atol=1e-13)
+
+
+def test_identity_v_exposes_probabilities():
+    # With V = I (Sk == D) the output rows are the softmax probabilities.
+    Sk = D = 16
+    Q, K = _rand((1, 1, 16, D), 11), _rand((1, 1, Sk, D), 12)
+    V = np.eye(Sk)[None, None]
+    for causal, W, ip in [(True, 0, 0), (True, 5, 0), (False, 0, 0)]:
+        P, L = ora.attn_ref(Q, K, V, causal, W, ip)
+        ok = ora.allowed_mask(16, Sk, causal, W, ip)
+        assert np.all(P[0, 0] >= 0)
+        np.testing.assert_allclose(P[0, 0].sum(axis=1), 1.0, atol=1e-14)
+        assert np.all(P[0, 0][~ok] == 0.0)
+        # LSE is the log of the plain (unshifted) exponential sum
+        s = Q[0, 0] @ K[0, 0].T / math.sqrt(D)
+        want = np.log(np.where(ok, np.exp(s), 0.0).sum(axis=1))
+        np.testing.assert_allclose(L[0, 0], want, atol=1e-13)
+
+
+def test_k_lengths_equal_truncation():
+    Q, K, V = _rand((2, 2, 9, 8), 13), _rand((2, 2, 20, 8), 14), _rand((2, 2, 20, 8), 15)
+    O, L = ora.attn_ref(Q, K, V, False, 0, 0, [20, 7])
+    Ot, Lt = ora.attn_ref(Q[1:], K[1:, :, :7], V[1:, :, :7])
+    np.testing.assert_allclose(O[1:], Ot, atol=1e-14)
+    np.testing.assert_allclose(L[1:], Lt, atol=1e-14)
+
+
+def test_decode_equals_single_query_prefill():
+    rng = np.random.default_rng(16)
+    B, H, Hkv, S, D = 4, 8, 2, 40, 16
+    Q = rng.standard_normal((B, H, D))
+    K, V = rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    lengths = np.array([40, 1, 17, 33])
+    O, L = ora.decode_ref(Q, K, V, lengths)
+    for b in range(B):
+        n = int(lengths[b])
+        Op, Lp = ora.attn_ref(Q[b][None, :, None], K[b][None], V[b][None], True, 0, n - 1)
+        np.testing.assert_allclose(O[b], Op[0, :, 0], atol=1e-13)
+        np.testing.assert_allclose(L[b], Lp[0, :, 0], atol=1e-13)
+
+
+@pytest.mark.parametrize("n_splits", [1, 2, 3, 8, 64])
+def test_decode_split_merge_invariant(n_splits):
+    rng = np.random.default_rng(17)
+    B, H, Hkv, S, D = 3, 4, 2, 300, 8
+    Q = rng.standard_normal((B, H, D))
+    K, V = rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    lengths = np.array([300, 65, 0])
+    O, L = ora.decode_ref(Q, K, V, lengths)
+    Os, Ls = ora.decode_split_ref(Q, K, V, lengths, n_splits, tile_n=64)
+    np.testing.assert_allclose(Os, O, atol=1e-13)
+    np.testing.assert_allclose(Ls[:2], L[:2], atol=1e-13)
+    assert np.all(Os[2] == 0) and np.all(np.isneginf(Ls[2]))
+
+
+def test_split_bounds_cover_once():
+    for n in [0, 1, 63, 64, 65, 512, 32768, 1000]:
+        for ns in [1, 3, 8]:
+            b = ora.split_bounds(n, ns, 64)
+            assert len(b) == ns
+            covered = [j for lo, hi in b for j in range(lo, hi)]
+            assert covered == list(range(n))
+            assert all(lo % 64 == 0 for lo, hi in b if hi > lo)
+
+
+@pytest.mark.parametrize("case", _load("tile_plans.json")["cases"], ids=lambda c: c["name"])
+def test_tile_plan_golden(case):
+    plan = ora.tile_plan_ref(case["Sq"], case["Sk"], case["causal"], case["window"],
+                             case["input_pos"], case["k_len"], case["tile_m"], case["tile_n"])
+    np.testing.assert_array_equal(plan, np.array(case["plan"], dtype=np.int8))
+
+
+def test_allowed_pairs_closed_forms():
+    # causal square: S(S+1)/2; window W on a long enough history: Sq*W.
+    assert ora.allowed_pairs(4096, 4096, True, 0, 0, 4096) == 4096 * 4097 // 2
+    assert ora.allowed_pairs(2048, 16384, True, 4096, 14336, 16384) == 2048 * 4096
+    assert ora.allowed_pairs(64, 64, False, 0, 0, 64) == 64 * 64
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must be caught by at least one pin above
+# ---------------------------------------------------------------------------
+
+def _pins_pass():
+    checks = [
+        lambda: [test_mask_golden(c) for c in _load("masks.json")["cases"]],
+        lambda: [test_closed_form_attention(m) for m in ("noncausal", "causal")],
+        test_closed_form_gqa_two_heads_share_kv,
+        test_closed_form_decode,
+        lambda: test_bruteforce_mpmath(BRUTE_CASES[1]),
+        test_zero_query_uniform_weights,
+        test_single_allowed_key,
+        lambda: test_decode_split_merge_invariant(3),
+        lambda: [test_tile_plan_golden(c) for c in _load("tile_plans.json")["cases"]],
+    ]
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError, TypeError):
+            return False
+    return True
+
+
+def _mutant_scale(q, k, scale):
+    return (q @ k.T) / q.shape[1]
+
+
+def _mutant_transposed_scores(q, k, scale):
+    return scale * (k @ q.T)
+
+
+def _mutant_no_normalise(s):
+    P, M, L = ORIG_SOFTMAX(s)
+    return P * np.maximum(L, 1e-300)[:, None], M, L
+
+
+def _mutant_lse_no_max(M, L):
+    out = np.full(M.shape, -np.inf)
+    ok = L > 0
+    out[ok] = np.log(L[ok])
+    return out
+
+
+def _mutant_combine_transposed(P, v):
+    return P.T @ v
+
+
+ORIG_SOFTMAX = ora.softmax_stats
+
+
+def _mutant_allowed_window_tylo(Sq, Sk, causal=False, window=0, input_pos=0, k_len=None):
+    return ORIG_ALLOWED(Sq, Sk, causal, window + 1 if window > 0 else 0, input_pos, k_len)
+
+
+def _mutant_allowed_strict_causal(Sq, Sk, causal=False, window=0, input_pos=0, k_len=None):
+    ok = ORIG_ALLOWED(Sq, Sk, causal, window, input_pos, k_len)
+    if causal:
+        i = np.arange(Sq)[:, None] + input_pos
+        ok &= np.arange(Sk)[None, :] < i
+    return ok
+
+
+def _mutant_allowed_ignore_klen(Sq, Sk, causal=False, window=0, input_pos=0, k_len=None):
+    return ORIG_ALLOWED(Sq, Sk, causal, window, input_pos, None)
+
+
+ORIG_ALLOWED = ora.allowed_mask
+
+
+@pytest.mark.parametrize("target,mutant", [
+    ("scores", _mutant_scale),
+    ("scores", _mutant_transposed_scores),
+    ("softmax_stats", _mutant_no_normalise),
+    ("lse_from_stats", _mutant_lse_no_max),
+    ("combine", _mutant_combine_transposed),
+    ("allowed_mask", _mutant_allowed_window_tylo),
+    ("allowed_mask", _mutant_allowed_strict_causal),
+    ("allowed_mask", _mutant_allowed_ignore_klen),
+])
+def test_planted_mistakes(monkeypatch, target, mutant):
+    assert _pins_pass()
+    monkeypatch.setattr(ora, target, mutant)
+    assert not _pins_pass(), f"no pin caught the planted mistake in {target}"
+
+
+def test_planted_gqa_mapping_mistake(monkeypatch):
+    # Query head h reading KV head h % Hkv instead of h // G must be caught.
+    real = ora.attn_ref
+
+    def mutant(Q, K, V, *a, **kw):
+        Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
+        H, Hkv = Q.shape[1], K.shape[1]
+        outs = [real(Q[:, h:h + 1], K[:, h % Hkv:h % Hkv + 1], V[:, h % Hkv:h % Hkv + 1], *a, **kw)
+                for h in range(H)]
+        return (np.concatenate([o for o, _ in outs], axis=1),
+                np.concatenate([l for _, l in outs], axis=1))
+
+    monkeypatch.setattr(ora, "attn_ref", mutant)
+    with pytest.raises(AssertionError):
+        test_bruteforce_mpmath(BRUTE_CASES[1])
