@@ -1,0 +1,161 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention library
+ * (libattn_mi355x.so).
+ *
+ * Operations, as the pages define them:
+ *
+ *   O = softmax(scale * Q K^T + mask) V,  scale = 1/sqrt(D)
+ *
+ * (Tylo.jl "Primitives": attention! -- fused multi-head attention with GQA,
+ * causal, input_pos, k_lengths, saved softmax statistics M/L, Float32
+ * accumulation; flex_attention! -- qk_scale = 1/sqrt(Dk) and "Heads must be a
+ * multiple of Heads_KV"; decode_attention! -- split-KV single-query decode;
+ * mlx-arsenal "Attention": causal_mask / sliding_window_mask, additive masks
+ * with -inf at blocked positions; vllm_mlx.attention: MLXAttentionImpl.forward
+ * computing scaled_dot_product_attention(q, k, v, scale).)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layouts: all tensors are contiguous, row-major.
+ *   prefill  Q, O : (B, H,   Sq, D)      K, V : (B, Hkv, Sk, D)
+ *            LSE  : (B, H, Sq) float32
+ *   decode   Q, O : (B, H, D)            K, V : (B, Hkv, Smax, D)
+ * (Tylo's column-major (D, S, H, B) read in row-major order.)
+ *
+ * Heads: H must be a multiple of Hkv; query head h reads KV head
+ *   h / (H / Hkv) (contiguous groups).
+ *
+ * Mask: query row i sits at absolute position p = input_pos + i and may attend
+ *   to key j iff   j < kl                                (k_lengths)
+ *             and (causal == 0 or j <= p)                (CausalMask: q >= kv)
+ *             and (window <= 0 or j >= p - window + 1)   (at most `window`
+ *                                           previous positions, itself included)
+ *   where kl = clamp(k_lengths[b], 0, Sk), or Sk when k_lengths is NULL.
+ *   A window requires causal = 1.  Blocked pairs contribute exactly nothing
+ *   (masked K/V values are never multiplied into the result).
+ *   A row with no allowed key gets O = 0 and LSE = -inf.
+ *
+ * LSE: natural-log row logsumexp of the masked scaled scores (M + ln L in
+ *   the pages' M/L terms), float32.  Pass NULL to skip it.
+ *
+ * Ownership: every pointer is a caller-owned DEVICE pointer (except where
+ *   stated); the library keeps none after the call returns.  Work is enqueued
+ *   asynchronously on `stream` (0 = the null stream); inputs and outputs must
+ *   stay alive until the stream has passed it.  No entry point synchronises,
+ *   and the host never reads device arrays (k_lengths, lengths).  The library
+ *   holds no mutable global state; calls from several host threads are safe.
+ *
+ * Errors: every int-returning entry point returns
+ *   ATTN_OK (0), ATTN_EINVAL (1, a bad argument: shape, H % Hkv, window
+ *   without causal, n_splits < 1, a NULL required pointer, too small a
+ *   workspace), ATTN_EUNSUPPORTED (2, D not in {64, 128}, or sizes beyond the
+ *   32-bit index range), or ATTN_EHIP (3, a HIP launch or allocation error;
+ *   the HIP error is cleared).  Nothing is printed and nothing is enqueued when
+ *   an argument check fails.  attn_status_string() names a code.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_OK 0
+#define ATTN_EINVAL 1
+#define ATTN_EUNSUPPORTED 2
+#define ATTN_EHIP 3
+
+/* Prefill tile sizes used by attn_fwd (rows of Q per workgroup, keys per
+ * K/V tile); attn_tile_plan reports the plan at these sizes. */
+#define ATTN_FWD_TILE_M 128
+#define ATTN_FWD_TILE_N 64
+
+/* Prefill forward, bfloat16 Q/K/V/O, float32 accumulation and LSE.
+ *   O         out (B, H, Sq, D) bf16
+ *   Q         in  (B, H, Sq, D) bf16
+ *   K, V      in  (B, Hkv, Sk, D) bf16
+ *   LSE       out (B, H, Sq) float32, or NULL
+ *   B, H, Hkv, Sq, Sk   >= 1 (Sq or Sk = 0 is a no-op returning ATTN_OK)
+ *   D         64 or 128
+ *   causal    0 or 1
+ *   window    <= 0: none; > 0: sliding window (requires causal = 1)
+ *   input_pos absolute position of query row 0 (any int)
+ *   k_lengths device int32 (B,), or NULL (= Sk for every batch)
+ * Defined by: Tylo.jl "Primitives", attention! (layouts, GQA, input_pos,
+ * k_lengths, checkpoints M/L, Float32 accumulation); mlx-arsenal "Attention",
+ * causal_mask and sliding_window_mask (offset, window, -inf masking). */
+int attn_fwd(void* O, const void* Q, const void* K, const void* V, float* LSE,
+             int B, int H, int Hkv, int Sq, int Sk, int D, int causal,
+             int window, int input_pos, const int32_t* k_lengths,
+             hipStream_t stream);
+
+/* Prefill forward, float32 Q/K/V/O, exact float32 products (no reduced
+ * precision inside).  Same arguments and semantics as attn_fwd; the element
+ * type is carried by the symbol.  Defined by: Tylo.jl "Primitives",
+ * attention! (compute precision follows the element type of Q). */
+int attn_fwd_f32(void* O, const void* Q, const void* K, const void* V,
+                 float* LSE, int B, int H, int Hkv, int Sq, int Sk, int D,
+                 int causal, int window, int input_pos,
+                 const int32_t* k_lengths, hipStream_t stream);
+
+/* Split-KV (Flash-Decoding) single-query decode, bf16 Q/K/V/O.
+ *   O        out (B, H, D) bf16
+ *   Q        in  (B, H, D) bf16
+ *   K, V     in  (B, Hkv, Smax, D) bf16; slots at or past lengths[b] are
+ *            never read
+ *   lengths  device int32 (B,): valid KV length per sequence, clamped to
+ *            [0, Smax]; a zero length gives O = 0
+ *   n_splits >= 1: the valid keys of each (sequence, KV head) are cut into
+ *            n_splits slices of C = ceil(ceil(len/64)/n_splits)*64 keys that
+ *            run in parallel; their partial results are merged with LSE
+ *            weights.  The result does not depend on n_splits beyond rounding.
+ *   B, H, Hkv, Smax >= 1, D in {64, 128}
+ * Allocates its partial-result scratch stream-ordered on `stream`
+ * (hipMallocAsync / hipFreeAsync).  Defined by: Tylo.jl "Primitives",
+ * decode_attention! (layouts, lengths, n_splits = 8, TILE_N = 64). */
+int attn_decode(void* O, const void* Q, const void* K, const void* V,
+                const int32_t* lengths, int n_splits, int B, int H, int Hkv,
+                int Smax, int D, hipStream_t stream);
+
+/* Bytes of scratch attn_decode_ws needs for these sizes (host-only, no HIP
+ * call).  Returns 0 for invalid sizes. */
+size_t attn_decode_workspace_bytes(int B, int H, int n_splits, int D);
+
+/* attn_decode with a caller-provided device scratch buffer `workspace` of
+ * `ws_bytes` >= attn_decode_workspace_bytes(B, H, n_splits, D) bytes,
+ * 256-byte aligned.  Allocates nothing.  Concurrent calls must not share a
+ * workspace. */
+int attn_decode_ws(void* O, const void* Q, const void* K, const void* V,
+                   const int32_t* lengths, int n_splits, int B, int H, int Hkv,
+                   int Smax, int D, void* workspace, size_t ws_bytes,
+                   hipStream_t stream);
+
+/* Debug export: evaluates the kernels' own mask predicate into M (device,
+ * uint8 (Sq, Sk), 1 = attend, 0 = blocked) for one batch with valid key
+ * length k_len (clamped to [0, Sk]).  Tylo.jl "Primitives", hmask: host and
+ * device masks must agree. */
+int attn_mask_dump(uint8_t* M, int Sq, int Sk, int causal, int window,
+                   int input_pos, int k_len, hipStream_t stream);
+
+/* Debug export: the tile plan attn_fwd uses, int8 (ceil(Sq/ATTN_FWD_TILE_M),
+ * ceil(Sk/ATTN_FWD_TILE_N)) in P (device): 0 = empty (skipped), 1 = partial
+ * (masked per element), 2 = full (no per-element mask).  Tylo.jl
+ * "Primitives", BlockMask / build_block_mask. */
+int attn_tile_plan(int8_t* P, int Sq, int Sk, int causal, int window,
+                   int input_pos, int k_len, hipStream_t stream);
+
+/* Static string naming a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,193 @@
+"""MI355X (gfx950) fused attention: a thin Python binding over libattn_mi355x.so.
+
+The functions below carry the names of the C entry points declared in
+``include/attn.h`` and only marshal arguments: they read shapes from torch
+tensors, pass raw device pointers and the current HIP stream, and turn a
+non-zero status into ``RuntimeError`` (like vllm_mlx.attention's forward,
+which logs and re-raises).  Every step of the computation runs in the HIP
+kernels; there is no fallback.  ``sdpa`` and ``decode`` are allocating
+conveniences on top.
+
+Layouts (row-major, contiguous): prefill Q/O (B, H, Sq, D), K/V (B, Hkv, Sk, D),
+LSE (B, H, Sq) float32; decode Q/O (B, H, D), K/V (B, Hkv, Smax, D).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+TILE_M, TILE_N = 128, 64  # prefill tile sizes (ATTN_FWD_TILE_M / _N)
+
+_lib = None
+
+_I = ctypes.c_int
+_P = ctypes.c_void_p
+_SIGS = {
+    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "attn_decode_ws": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
+    "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "attn_mask_dump": (_I, [_P, _I, _I, _I, _I, _I, _I, _P]),
+    "attn_tile_plan": (_I, [_P, _I, _I, _I, _I, _I, _I, _P]),
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+    "attn_version": (_I, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn_mi355x.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m scaled_dot_product_attn_amd._build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(status).decode()
+
+
+def attn_version() -> int:
+    return lib().attn_version()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != ATTN_OK:
+        raise RuntimeError(f"{what}: {attn_status_string(rc)} (status {rc})")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _fwd(name, dtype, O, Q, K, V, LSE, causal, window, input_pos, k_lengths, stream):
+    B, H, Sq, D = Q.shape
+    _, Hkv, Sk, _ = K.shape
+    for t in (O, Q, K, V):
+        if t.dtype != dtype:
+            raise ValueError(f"{name} takes {dtype} tensors")
+    if LSE is not None and LSE.dtype != torch.float32:
+        raise ValueError("LSE must be float32")
+    if k_lengths is not None and k_lengths.dtype != torch.int32:
+        raise ValueError("k_lengths must be int32")
+    rc = getattr(lib(), name)(_ptr(O), _ptr(Q), _ptr(K), _ptr(V), _ptr(LSE),
+                              B, H, Hkv, Sq, Sk, D, int(bool(causal)), int(window),
+                              int(input_pos), _ptr(k_lengths), _stream(stream))
+    _check(rc, name)
+
+
+def attn_fwd(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
+             k_lengths=None, stream=None) -> None:
+    """bf16 prefill forward into O (and LSE if given); see include/attn.h."""
+    _fwd("attn_fwd", torch.bfloat16, O, Q, K, V, LSE, causal, window, input_pos,
+         k_lengths, stream)
+
+
+def attn_fwd_f32(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
+                 k_lengths=None, stream=None) -> None:
+    """float32 prefill forward into O (and LSE if given); see include/attn.h."""
+    _fwd("attn_fwd_f32", torch.float32, O, Q, K, V, LSE, causal, window, input_pos,
+         k_lengths, stream)
+
+
+def attn_decode_workspace_bytes(B: int, H: int, n_splits: int, D: int) -> int:
+    return lib().attn_decode_workspace_bytes(B, H, n_splits, D)
+
+
+def _dec_args(O, Q, K, V, lengths):
+    B, H, D = Q.shape
+    _, Hkv, Smax, _ = K.shape
+    for t in (O, Q, K, V):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("decode takes bfloat16 tensors")
+    if lengths.dtype != torch.int32:
+        raise ValueError("lengths must be int32")
+    return B, H, Hkv, Smax, D
+
+
+def attn_decode(O, Q, K, V, lengths, n_splits=8, stream=None) -> None:
+    """Split-KV decode into O; the library allocates its scratch stream-ordered."""
+    B, H, Hkv, Smax, D = _dec_args(O, Q, K, V, lengths)
+    rc = lib().attn_decode(_ptr(O), _ptr(Q), _ptr(K), _ptr(V), _ptr(lengths),
+                           int(n_splits), B, H, Hkv, Smax, D, _stream(stream))
+    _check(rc, "attn_decode")
+
+
+def attn_decode_ws(O, Q, K, V, lengths, n_splits, workspace, stream=None) -> None:
+    """Split-KV decode using a caller-owned uint8 device workspace."""
+    B, H, Hkv, Smax, D = _dec_args(O, Q, K, V, lengths)
+    ws = _ptr(workspace) if workspace is not None else None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().attn_decode_ws(_ptr(O), _ptr(Q), _ptr(K), _ptr(V), _ptr(lengths),
+                              int(n_splits), B, H, Hkv, Smax, D, ws, nbytes,
+                              _stream(stream))
+    _check(rc, "attn_decode_ws")
+
+
+def attn_mask_dump(M, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
+                   stream=None) -> None:
+    """The kernels' own mask predicate into M (uint8 (Sq, Sk))."""
+    rc = lib().attn_mask_dump(_ptr(M), Sq, Sk, int(bool(causal)), int(window),
+                              int(input_pos), Sk if k_len is None else int(k_len),
+                              _stream(stream))
+    _check(rc, "attn_mask_dump")
+
+
+def attn_tile_plan(P, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
+                   stream=None) -> None:
+    """The prefill kernel's tile plan into P (int8 (ceil(Sq/128), ceil(Sk/64)))."""
+    rc = lib().attn_tile_plan(_ptr(P), Sq, Sk, int(bool(causal)), int(window),
+                              int(input_pos), Sk if k_len is None else int(k_len),
+                              _stream(stream))
+    _check(rc, "attn_tile_plan")
+
+
+# ---------------------------------------------------------------------------
+# allocating conveniences
+# ---------------------------------------------------------------------------
+
+def sdpa(q, k, v, causal=False, window=0, input_pos=0, k_lengths=None,
+         return_lse=True, stream=None):
+    """Allocate O (and LSE) and run the forward matching q's dtype."""
+    B, H, Sq, D = q.shape
+    O = torch.empty_like(q)
+    LSE = torch.empty(B, H, Sq, dtype=torch.float32, device=q.device) if return_lse else None
+    fn = attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_f32
+    fn(O, q, k, v, LSE, causal, window, input_pos, k_lengths, stream)
+    return (O, LSE) if return_lse else O
+
+
+def decode(q, k, v, lengths, n_splits=8, stream=None):
+    """Allocate O and run split-KV decode."""
+    O = torch.empty_like(q)
+    attn_decode(O, q, k, v, lengths, n_splits, stream)
+    return O

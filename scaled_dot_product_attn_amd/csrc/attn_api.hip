@@ -1,0 +1,213 @@
+// C ABI of the attention library: argument checks, launches, status codes,
+// and the two debug exports (the device mask predicate and the tile plan).
+//
+// Argument errors are reported as status codes before anything is enqueued,
+// in the spirit of vllm_mlx.attention's validate_configuration returning its
+// errors rather than raising; the calls write their outputs in place and
+// return no tensor (Tylo.jl "Primitives", attention! "Returns nothing").
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_common.h"
+
+namespace attn {
+
+template <int D>
+hipError_t launch_fwd_bf16(void*, const void*, const void*, const void*,
+                           float*, int, int, int, int, int, int, int, int,
+                           const int32_t*, hipStream_t);
+template <int D>
+hipError_t launch_fwd_f32(void*, const void*, const void*, const void*,
+                          float*, int, int, int, int, int, int, int, int,
+                          const int32_t*, hipStream_t);
+hipError_t launch_decode(void*, const void*, const void*, const void*,
+                         const int32_t*, int, int, int, int, int, int, void*,
+                         hipStream_t);
+size_t decode_workspace_bytes(int B, int H, int n_splits, int D);
+
+__global__ void mask_dump_kernel(uint8_t* __restrict__ M, int Sq, int Sk,
+                                 int causal, int window, int input_pos,
+                                 int kl) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)Sq * Sk) return;
+  const int i = (int)(idx / Sk), j = (int)(idx % Sk);
+  const RowRange r = row_range(i, kl, causal, window, input_pos);
+  M[idx] = (j >= r.lo && j < r.hi) ? 1 : 0;
+}
+
+__global__ void tile_plan_kernel(int8_t* __restrict__ P, int Sq, int Sk,
+                                 int causal, int window, int input_pos,
+                                 int kl, int nqt, int nkt) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)nqt * nkt) return;
+  const int qt = (int)(idx / nkt), kt = (int)(idx % nkt);
+  const int i0 = qt * ATTN_FWD_TILE_M;
+  const int i1 = min(i0 + ATTN_FWD_TILE_M, Sq);
+  const KvGeometry g = kv_geometry(i0, i1, kl, causal, window, input_pos);
+  P[idx] = (int8_t)tile_class(g, kt * ATTN_FWD_TILE_N, ATTN_FWD_TILE_N);
+}
+
+static int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  (void)hipGetLastError();  // clear the sticky launch error
+  return ATTN_EHIP;
+}
+
+// Checks shared by the prefill entry points.  Sizes must keep every key and
+// row index (plus one tile of overshoot) inside int32.
+static int check_fwd(const void* O, const void* Q, const void* K,
+                     const void* V, int B, int H, int Hkv, int Sq, int Sk,
+                     int D, int causal, int window) {
+  if (B < 1 || H < 1 || Hkv < 1 || Sq < 0 || Sk < 0) return ATTN_EINVAL;
+  if (H % Hkv != 0) return ATTN_EINVAL;
+  if (causal != 0 && causal != 1) return ATTN_EINVAL;
+  if (window > 0 && !causal) return ATTN_EINVAL;
+  if (D != 64 && D != 128) return ATTN_EUNSUPPORTED;
+  if (Sq > INT_MAX - 256 || Sk > INT_MAX - 256) return ATTN_EUNSUPPORTED;
+  const long long nqt = ((long long)Sq + 127) / 64;  // finest row tiling used
+  if (nqt * H * B > INT_MAX) return ATTN_EUNSUPPORTED;
+  if ((long long)B * H > INT_MAX / 2 || (long long)B * Hkv > INT_MAX / 2)
+    return ATTN_EUNSUPPORTED;
+  if (Sq > 0 && (!O || !Q)) return ATTN_EINVAL;
+  if (Sq > 0 && Sk > 0 && (!K || !V)) return ATTN_EINVAL;
+  return ATTN_OK;
+}
+
+static int check_decode(const void* O, const void* Q, const void* K,
+                        const void* V, const int32_t* lengths, int n_splits,
+                        int B, int H, int Hkv, int Smax, int D) {
+  if (B < 1 || H < 1 || Hkv < 1 || Smax < 1 || n_splits < 1)
+    return ATTN_EINVAL;
+  if (H % Hkv != 0) return ATTN_EINVAL;
+  if (D != 64 && D != 128) return ATTN_EUNSUPPORTED;
+  if (Smax > INT_MAX - 256) return ATTN_EUNSUPPORTED;
+  if ((long long)B * H * n_splits > INT_MAX / 2) return ATTN_EUNSUPPORTED;
+  if ((long long)B * Hkv * H * n_splits > INT_MAX) return ATTN_EUNSUPPORTED;
+  if (!O || !Q || !K || !V || !lengths) return ATTN_EINVAL;
+  return ATTN_OK;
+}
+
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" {
+
+int attn_fwd(void* O, const void* Q, const void* K, const void* V, float* LSE,
+             int B, int H, int Hkv, int Sq, int Sk, int D, int causal,
+             int window, int input_pos, const int32_t* k_lengths,
+             hipStream_t stream) {
+  int rc = check_fwd(O, Q, K, V, B, H, Hkv, Sq, Sk, D, causal, window);
+  if (rc != ATTN_OK || Sq == 0) return rc;
+  hipError_t e =
+      D == 64 ? launch_fwd_bf16<64>(O, Q, K, V, LSE, B, H, Hkv, Sq, Sk, causal,
+                                    window, input_pos, k_lengths, stream)
+              : launch_fwd_bf16<128>(O, Q, K, V, LSE, B, H, Hkv, Sq, Sk,
+                                     causal, window, input_pos, k_lengths,
+                                     stream);
+  return hip_status(e);
+}
+
+int attn_fwd_f32(void* O, const void* Q, const void* K, const void* V,
+                 float* LSE, int B, int H, int Hkv, int Sq, int Sk, int D,
+                 int causal, int window, int input_pos,
+                 const int32_t* k_lengths, hipStream_t stream) {
+  int rc = check_fwd(O, Q, K, V, B, H, Hkv, Sq, Sk, D, causal, window);
+  if (rc != ATTN_OK || Sq == 0) return rc;
+  hipError_t e =
+      D == 64 ? launch_fwd_f32<64>(O, Q, K, V, LSE, B, H, Hkv, Sq, Sk, causal,
+                                   window, input_pos, k_lengths, stream)
+              : launch_fwd_f32<128>(O, Q, K, V, LSE, B, H, Hkv, Sq, Sk, causal,
+                                    window, input_pos, k_lengths, stream);
+  return hip_status(e);
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int n_splits, int D) {
+  if (B < 1 || H < 1 || n_splits < 1 || (D != 64 && D != 128)) return 0;
+  return decode_workspace_bytes(B, H, n_splits, D);
+}
+
+int attn_decode_ws(void* O, const void* Q, const void* K, const void* V,
+                   const int32_t* lengths, int n_splits, int B, int H, int Hkv,
+                   int Smax, int D, void* workspace, size_t ws_bytes,
+                   hipStream_t stream) {
+  int rc = check_decode(O, Q, K, V, lengths, n_splits, B, H, Hkv, Smax, D);
+  if (rc != ATTN_OK) return rc;
+  if (n_splits > 1) {
+    if (!workspace || ((uintptr_t)workspace & 255) != 0) return ATTN_EINVAL;
+    if (ws_bytes < decode_workspace_bytes(B, H, n_splits, D))
+      return ATTN_EINVAL;
+  }
+  return hip_status(launch_decode(O, Q, K, V, lengths, n_splits, B, H, Hkv,
+                                  Smax, D, workspace, stream));
+}
+
+int attn_decode(void* O, const void* Q, const void* K, const void* V,
+                const int32_t* lengths, int n_splits, int B, int H, int Hkv,
+                int Smax, int D, hipStream_t stream) {
+  int rc = check_decode(O, Q, K, V, lengths, n_splits, B, H, Hkv, Smax, D);
+  if (rc != ATTN_OK) return rc;
+  void* ws = nullptr;
+  if (n_splits > 1) {
+    const size_t bytes = decode_workspace_bytes(B, H, n_splits, D);
+    if (hipMallocAsync(&ws, bytes, stream) != hipSuccess) {
+      (void)hipGetLastError();
+      return ATTN_EHIP;
+    }
+  }
+  rc = hip_status(launch_decode(O, Q, K, V, lengths, n_splits, B, H, Hkv, Smax,
+                                D, ws, stream));
+  if (ws && hipFreeAsync(ws, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    rc = ATTN_EHIP;
+  }
+  return rc;
+}
+
+int attn_mask_dump(uint8_t* M, int Sq, int Sk, int causal, int window,
+                   int input_pos, int k_len, hipStream_t stream) {
+  if (Sq < 0 || Sk < 0 || (causal != 0 && causal != 1)) return ATTN_EINVAL;
+  if (window > 0 && !causal) return ATTN_EINVAL;
+  if ((long long)Sq * Sk > (long long)INT_MAX * 256) return ATTN_EUNSUPPORTED;
+  if ((long long)Sq * Sk == 0) return ATTN_OK;
+  if (!M) return ATTN_EINVAL;
+  const int kl = k_len < 0 ? 0 : (k_len > Sk ? Sk : k_len);
+  const long long n = (long long)Sq * Sk;
+  hipLaunchKernelGGL(mask_dump_kernel, dim3((unsigned)((n + 255) / 256)),
+                     dim3(256), 0, stream, M, Sq, Sk, causal, window,
+                     input_pos, kl);
+  return hip_status(hipGetLastError());
+}
+
+int attn_tile_plan(int8_t* P, int Sq, int Sk, int causal, int window,
+                   int input_pos, int k_len, hipStream_t stream) {
+  if (Sq < 0 || Sk < 0 || (causal != 0 && causal != 1)) return ATTN_EINVAL;
+  if (window > 0 && !causal) return ATTN_EINVAL;
+  if (Sq > INT_MAX - 256 || Sk > INT_MAX - 256) return ATTN_EUNSUPPORTED;
+  const int nqt = (Sq + ATTN_FWD_TILE_M - 1) / ATTN_FWD_TILE_M;
+  const int nkt = (Sk + ATTN_FWD_TILE_N - 1) / ATTN_FWD_TILE_N;
+  const long long n = (long long)nqt * nkt;
+  if (n == 0) return ATTN_OK;
+  if (!P) return ATTN_EINVAL;
+  const int kl = k_len < 0 ? 0 : (k_len > Sk ? Sk : k_len);
+  hipLaunchKernelGGL(tile_plan_kernel, dim3((unsigned)((n + 255) / 256)),
+                     dim3(256), 0, stream, P, Sq, Sk, causal, window,
+                     input_pos, kl, nqt, nkt);
+  return hip_status(hipGetLastError());
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_EUNSUPPORTED: return "unsupported size or head dimension";
+    case ATTN_EHIP: return "HIP launch or allocation error";
+    default: return "unknown status";
+  }
+}
+
+int attn_version(void) { return 10000; }
+
+}  // extern "C"

@@ -1,0 +1,371 @@
+// Fused attention forward for bf16 Q/K/V/O on gfx950 (MI355X).
+//
+// O = softmax(scale * Q K^T + mask) V with Float32 accumulation and the row
+// logsumexp saved (Tylo.jl "Primitives", attention!: GQA, causal, input_pos,
+// k_lengths, checkpoints M/L; flex_attention!: qk_scale = 1/sqrt(Dk), in-kernel
+// block skipping for analytic masks; mlx-arsenal "Attention": causal_mask /
+// sliding_window_mask with -inf at blocked positions).
+//
+// Work decomposition
+//   One workgroup = 4 waves = 128 query rows of one (batch, head); each wave
+//   owns 32 rows.  The workgroup walks the key tiles of TILE_N = 64 keys that
+//   its rows can see (empty tiles are never visited), staging K and V^T
+//   through LDS with a register double buffer: tile t+1 is fetched from HBM
+//   while tile t is multiplied.
+//
+// Contractions on the matrix cores (v_mfma_f32_32x32x16_bf16), transposed so
+// that one lane owns one query row:
+//   S^T (32 keys x 32 queries) = K (32 x 16 d) * Q^T (16 d x 32 queries)
+//     -> lane l holds query l%32 and 16 of the 32 keys, so the row max and
+//        row sum are in-lane reductions plus one exchange with lane l^32.
+//   O^T (32 d x 32 queries) += V^T (32 d x 16 keys) * P^T (16 keys x 32 q)
+//     -> P^T is the S^T accumulator itself, rounded to bf16: no shuffle.
+//   The key order inside V^T's LDS rows is permuted to match the order in
+//   which the S^T accumulator registers hold the keys.
+//
+// Online softmax in base 2: t = s * log2(e) / sqrt(D), p = exp2(t - m).  The
+// running max m is only raised when a tile's max exceeds it by more than
+// 2^8 (p <= 256 otherwise), so the O rescale is skipped on almost all tiles;
+// O / l and m + log2 l are unchanged by which m is used.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_common.h"
+
+namespace attn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kFwdWaves = 4;
+constexpr int kFwdThreads = kFwdWaves * 64;
+constexpr int kFwdTileM = kFwdWaves * 32;  // query rows per workgroup
+constexpr int kFwdTileN = 64;              // keys per tile
+constexpr float kLazyRescale = 8.0f;       // log2 headroom before m is raised
+static_assert(kFwdTileM == ATTN_FWD_TILE_M && kFwdTileN == ATTN_FWD_TILE_N,
+              "the exported tile plan must use the kernel's tile sizes");
+
+template <int D>
+struct FwdLds {
+  // K tile: kFwdTileN rows of D bf16, each row padded by 16 bytes so that the
+  // 16-byte operand reads of 16 consecutive rows fall on distinct banks.
+  static constexpr int kRowK = D * 2 + 16;
+  static constexpr int kBytesK = kFwdTileN * kRowK;
+  // V^T tile: D rows of kFwdTileN bf16 keys (permuted order), padded likewise.
+  static constexpr int kRowV = kFwdTileN * 2 + 16;
+  static constexpr int kBytesV = D * kRowV;
+  static constexpr int kBuf = kBytesK + kBytesV;
+  static constexpr int kTotal = 2 * kBuf;
+};
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  bf16x2_t r = __builtin_convertvector(v, bf16x2_t);  // v_cvt_pk_bf16_f32, RNE
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ inline float wave_max_pair(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+// Position of a key inside its 16-key group in the V^T rows: keys 4..7 and
+// 8..11 swap places, which is the order the S^T accumulator holds them in.
+__device__ inline int vt_group_pos(int quad_in_group) {
+  return ((quad_in_group & 1) << 3) | ((quad_in_group >> 1) << 2);
+}
+
+template <int D>
+__global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
+    __bf16* __restrict__ O, const __bf16* __restrict__ Q,
+    const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    float* __restrict__ LSE, int B, int H, int Hkv, int Sq, int Sk, int causal,
+    int window, int input_pos, const int32_t* __restrict__ k_lengths,
+    float scale_log2) {
+  using L = FwdLds<D>;
+  constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
+  constexpr int DBLK = D / 32;     // 32-wide blocks of the head dimension
+  constexpr int KLOADS = kFwdTileN * D / 8 / kFwdThreads;  // 16B K loads/thread
+  constexpr int VTHREADS = (kFwdTileN / 4) * (D / 8);      // threads staging V
+
+  __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lrow = lane & 31;  // query row (within the wave) this lane owns
+  const int half = lane >> 5;  // which half of each MFMA k-slice this lane feeds
+
+  // ---- work item: heaviest query tiles first, XCD-grouped by KV head ----
+  const int G = H / Hkv;
+  const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
+  const int total = nqt * H * B;
+  const int lid = blockIdx.x;
+  int wid = lid;
+  {
+    // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
+    // contiguous range of work so the query heads sharing a KV head (and
+    // their K/V tiles) stay in one L2.
+    const int per = total >> 3;
+    if (lid < (per << 3)) wid = (lid & 7) * per + (lid >> 3);
+  }
+  const int per_pair = nqt * G;
+  const int pair = wid / per_pair;
+  const int rem = wid - pair * per_pair;
+  const int qt_rank = rem / G;
+  const int hg = rem - qt_rank * G;
+  const int b = pair / Hkv;
+  const int g = pair - b * Hkv;
+  const int h = g * G + hg;
+  const int qt = causal ? (nqt - 1 - qt_rank) : qt_rank;
+
+  const int i0 = qt * kFwdTileM;
+  const int i1 = min(i0 + kFwdTileM, Sq);
+  const int kl = k_lengths ? min(max(k_lengths[b], 0), Sk) : Sk;
+  const KvGeometry geo = kv_geometry(i0, i1, kl, causal, window, input_pos);
+
+  const size_t q_base = ((size_t)(b * H + h) * Sq) * D;
+  const size_t kv_base = ((size_t)(b * Hkv + g) * Sk) * D;
+  const __bf16* Kp = K + kv_base;
+  const __bf16* Vp = V + kv_base;
+
+  // ---- my query row ----
+  const int qi = i0 + wave * 32 + lrow;  // global query row of this lane
+  const RowRange rr = row_range(qi, kl, causal, window, input_pos);
+
+  bf16x8_t qreg[KSTEPS];
+  {
+    const bool ok = qi < Sq;
+    const __bf16* qp = Q + q_base + (size_t)(ok ? qi : 0) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4_t v = ok ? *(const u32x4_t*)(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
+      qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x16_t oacc[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16_t{};
+  float m_run = -INFINITY;  // running max (base-2 scaled domain)
+  float l_run = 0.f;        // this lane's half of the running row sum
+
+  int kt_first = 0, kt_last = -1;
+  if (geo.any) {
+    kt_first = geo.union_lo / kFwdTileN;
+    kt_last = (geo.union_hi - 1) / kFwdTileN;
+  }
+
+  // ---- staging: global -> registers -> LDS ----
+  u32x4_t kst[KLOADS];
+  u32x4_t vst[4];
+  const int vkq = tid & 15;  // key quad within the tile (V staging)
+  const int vdc = tid >> 4;  // 8-wide d chunk (V staging)
+
+  auto fetch = [&](int kt) {
+    const int j0 = kt * kFwdTileN;
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int c = i * kFwdThreads + tid;
+      const int key = j0 + c / (D / 8);
+      const int dch = c % (D / 8);
+      const bool ok = key >= geo.union_lo && key < geo.union_hi;
+      kst[i] = ok ? *(const u32x4_t*)(Kp + (size_t)key * D + dch * 8)
+                  : u32x4_t{0, 0, 0, 0};
+    }
+    if (VTHREADS == kFwdThreads || tid < VTHREADS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = j0 + vkq * 4 + i;
+        const bool ok = key >= geo.union_lo && key < geo.union_hi;
+        vst[i] = ok ? *(const u32x4_t*)(Vp + (size_t)key * D + vdc * 8)
+                    : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+
+  auto stash = [&](int buf) {
+    char* kb = smem + buf * L::kBuf;
+    char* vb = kb + L::kBytesK;
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int c = i * kFwdThreads + tid;
+      const int key = c / (D / 8);
+      const int dch = c % (D / 8);
+      *(u32x4_t*)(kb + key * L::kRowK + dch * 16) = kst[i];
+    }
+    if (VTHREADS == kFwdThreads || tid < VTHREADS) {
+      // 4 keys x 8 d  ->  8 rows of V^T, 4 keys (8 bytes) each
+      const int grp = vkq >> 2;
+      const int pos = grp * 16 + vt_group_pos(vkq & 3);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t r0 = vst[0][m], r1 = vst[1][m], r2 = vst[2][m],
+                       r3 = vst[3][m];
+        u32x2_t even = {__builtin_amdgcn_perm(r1, r0, 0x05040100u),
+                        __builtin_amdgcn_perm(r3, r2, 0x05040100u)};
+        u32x2_t odd = {__builtin_amdgcn_perm(r1, r0, 0x07060302u),
+                       __builtin_amdgcn_perm(r3, r2, 0x07060302u)};
+        const int d = vdc * 8 + 2 * m;
+        *(u32x2_t*)(vb + d * L::kRowV + pos * 2) = even;
+        *(u32x2_t*)(vb + (d + 1) * L::kRowV + pos * 2) = odd;
+      }
+    }
+  };
+
+  if (kt_first <= kt_last) {
+    fetch(kt_first);
+    stash(0);
+    __syncthreads();
+  }
+
+  int buf = 0;
+  for (int kt = kt_first; kt <= kt_last; ++kt) {
+    if (kt < kt_last) fetch(kt + 1);
+
+    const char* kb = smem + buf * L::kBuf;
+    const char* vb = kb + L::kBytesK;
+    const int j0 = kt * kFwdTileN;
+    const int cls = tile_class(geo, j0, kFwdTileN);
+
+    // ---- S^T = K Q^T for two 32-key blocks ----
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      s[kb2] = f32x16_t{};
+      const char* arow = kb + (kb2 * 32 + lrow) * L::kRowK + half * 16;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        bf16x8_t a = *(const bf16x8_t*)(arow + ks * 32);
+        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb2],
+                                                         0, 0, 0);
+      }
+    }
+
+    // ---- mask (partial tiles only) ----
+    if (cls == kTilePartial) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + kb2 * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          if (j < rr.lo || j >= rr.hi) s[kb2][r] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax ----
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    mx = wave_max_pair(mx);
+    const float mt = mx * scale_log2;
+    const bool need = mt > m_run + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? mt : m_run;
+      // need == false leaves the lane unchanged (and avoids -inf - -inf)
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+
+    uint32_t pb[2][2][4];  // [key block][k-step][packed pair]
+    float psum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], scale_log2, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(
+            __builtin_fmaf(s[kb2][r + 1], scale_log2, -mref));
+        psum += p0 + p1;
+        pb[kb2][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+      }
+    l_run += psum;
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const char* arow = vb + (db * 32 + lrow) * L::kRowV + half * 16;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          bf16x8_t a = *(const bf16x8_t*)(arow + (kb2 * 2 + st) * 32);
+          u32x4_t bw = {pb[kb2][st][0], pb[kb2][st][1], pb[kb2][st][2],
+                        pb[kb2][st][3]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a, __builtin_bit_cast(bf16x8_t, bw), oacc[db], 0, 0, 0);
+        }
+    }
+
+    if (kt < kt_last) {
+      stash(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // ---- epilogue ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qi < Sq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __bf16* op = O + q_base + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + r4 * 8 + half * 4;
+        u32x2_t w = {pack_bf16x2(oacc[db][r4 * 4 + 0] * inv,
+                                 oacc[db][r4 * 4 + 1] * inv),
+                     pack_bf16x2(oacc[db][r4 * 4 + 2] * inv,
+                                 oacc[db][r4 * 4 + 3] * inv)};
+        *(u32x2_t*)(op + d) = w;
+      }
+    if (LSE && half == 0) {
+      const float lse = l_tot > 0.f
+                            ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994530942f
+                            : -INFINITY;
+      LSE[(size_t)(b * H + h) * Sq + qi] = lse;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_fwd_bf16(void* O, const void* Q, const void* K,
+                           const void* V, float* LSE, int B, int H, int Hkv,
+                           int Sq, int Sk, int causal, int window,
+                           int input_pos, const int32_t* k_lengths,
+                           hipStream_t stream) {
+  const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
+  const long long total = (long long)nqt * H * B;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)total),
+                     dim3(kFwdThreads), 0, stream, (__bf16*)O,
+                     (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
+                     B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
+                     scale_log2);
+  return hipGetLastError();
+}
+
+template hipError_t launch_fwd_bf16<64>(void*, const void*, const void*,
+                                        const void*, float*, int, int, int,
+                                        int, int, int, int, int,
+                                        const int32_t*, hipStream_t);
+template hipError_t launch_fwd_bf16<128>(void*, const void*, const void*,
+                                         const void*, float*, int, int, int,
+                                         int, int, int, int, int,
+                                         const int32_t*, hipStream_t);
+
+}  // namespace attn

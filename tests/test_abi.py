@@ -1,0 +1,162 @@
+"""CPU checks of the C ABI and host logic (no GPU needed).
+
+* the library loads and exports every entry point include/attn.h declares;
+* argument validation returns the documented status codes before any HIP call;
+* the kernels' mask geometry and tile classifier, compiled for the host,
+  agree bit-exactly with the oracle's brute-force mask and tile plan.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import scaled_dot_product_attn_amd as attn
+from scaled_dot_product_attn_amd import _build
+from oracle import attn_oracle as ora
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.LIB_PATH):
+        _build.build()
+    return attn.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\*]+\s+\**)+\**(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared()
+    for n in ("attn_fwd", "attn_fwd_f32", "attn_decode", "attn_decode_ws",
+              "attn_decode_workspace_bytes", "attn_mask_dump", "attn_tile_plan",
+              "attn_status_string", "attn_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, re.M))
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_status_strings(lib):
+    assert attn.attn_version() == 10000
+    assert attn.attn_status_string(0) == "ok"
+    assert "invalid" in attn.attn_status_string(1)
+    assert "unsupported" in attn.attn_status_string(2)
+    assert "HIP" in attn.attn_status_string(3)
+    assert attn.attn_status_string(99) == "unknown status"
+
+
+def _fwd(lib, fn="attn_fwd", O=1, Q=1, K=1, V=1, B=1, H=4, Hkv=2, Sq=8, Sk=8,
+         D=128, causal=1, window=0, ip=0):
+    return getattr(lib, fn)(O, Q, K, V, None, B, H, Hkv, Sq, Sk, D, causal, window,
+                            ip, None, None)
+
+
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_f32"])
+def test_fwd_argument_errors(lib, fn):
+    assert _fwd(lib, fn, H=3, Hkv=2) == attn.ATTN_EINVAL
+    assert _fwd(lib, fn, Hkv=0) == attn.ATTN_EINVAL
+    assert _fwd(lib, fn, B=0) == attn.ATTN_EINVAL
+    assert _fwd(lib, fn, Sq=-1) == attn.ATTN_EINVAL
+    assert _fwd(lib, fn, causal=0, window=4) == attn.ATTN_EINVAL
+    assert _fwd(lib, fn, causal=2) == attn.ATTN_EINVAL
+    assert _fwd(lib, fn, D=96) == attn.ATTN_EUNSUPPORTED
+    assert _fwd(lib, fn, D=256) == attn.ATTN_EUNSUPPORTED
+    assert _fwd(lib, fn, O=None) == attn.ATTN_EINVAL
+    assert _fwd(lib, fn, K=None) == attn.ATTN_EINVAL
+    assert _fwd(lib, fn, Sq=2**31 - 10) == attn.ATTN_EUNSUPPORTED
+    # nothing to do: returns before touching the device
+    assert _fwd(lib, fn, Sq=0, O=None, Q=None) == attn.ATTN_OK
+
+
+def test_decode_argument_errors(lib):
+    def dec(O=1, Q=1, K=1, V=1, L=1, ns=8, B=2, H=8, Hkv=2, S=64, D=128):
+        return lib.attn_decode(O, Q, K, V, L, ns, B, H, Hkv, S, D, None)
+    assert dec(ns=0) == attn.ATTN_EINVAL
+    assert dec(H=6, Hkv=4) == attn.ATTN_EINVAL
+    assert dec(S=0) == attn.ATTN_EINVAL
+    assert dec(L=None) == attn.ATTN_EINVAL
+    assert dec(D=80) == attn.ATTN_EUNSUPPORTED
+    ws_need = lib.attn_decode_workspace_bytes(2, 8, 8, 128)
+    assert ws_need == 2 * 8 * 8 * 128 * 4 + 512
+    # too small or misaligned workspace: rejected before any launch
+    assert lib.attn_decode_ws(1, 1, 1, 1, 1, 8, 2, 8, 2, 64, 128, 256, ws_need - 1,
+                              None) == attn.ATTN_EINVAL
+    assert lib.attn_decode_ws(1, 1, 1, 1, 1, 8, 2, 8, 2, 64, 128, 260, ws_need,
+                              None) == attn.ATTN_EINVAL
+    assert lib.attn_decode_workspace_bytes(0, 8, 8, 128) == 0
+    assert lib.attn_decode_workspace_bytes(2, 8, 8, 96) == 0
+
+
+def test_debug_export_argument_errors(lib):
+    assert lib.attn_mask_dump(None, 4, 4, 0, 2, 0, 4, None) == attn.ATTN_EINVAL
+    assert lib.attn_mask_dump(None, 4, 4, 1, 0, 0, 4, None) == attn.ATTN_EINVAL
+    assert lib.attn_mask_dump(None, 0, 4, 1, 0, 0, 4, None) == attn.ATTN_OK
+    assert lib.attn_tile_plan(None, 4, 4, 1, 0, 0, 4, None) == attn.ATTN_EINVAL
+    assert lib.attn_tile_plan(None, 0, 0, 1, 0, 0, 0, None) == attn.ATTN_OK
+
+
+@pytest.fixture(scope="module")
+def plan_check(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("host") / "plan_check")
+    subprocess.run([_build.HIPCC, "-O1", "-std=c++17",
+                    "-I", os.path.join(ROOT, "scaled_dot_product_attn_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "host", "plan_check.cpp"), "-o", exe],
+                   check=True, capture_output=True)
+    return exe
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Sq = int(rng.integers(1, 300))
+        Sk = int(rng.integers(0, 400))
+        causal = int(rng.integers(0, 2))
+        window = int(rng.choice([0, 0, 1, 2, 5, 64, 100, 500])) if causal else 0
+        ip = int(rng.integers(-100, 500))
+        kl = int(rng.integers(-5, Sk + 6))
+        tm, tn = [(128, 64), (64, 32), (16, 16), (7, 5)][int(rng.integers(0, 4))]
+        cases.append((Sq, Sk, causal, window, ip, kl, tm, tn))
+    return cases
+
+
+def test_host_geometry_matches_oracle(plan_check):
+    cases = _random_cases(400, 1) + [
+        (4096, 4096, 1, 0, 0, 4096, 128, 64), (2048, 16384, 1, 4096, 14336, 16384, 128, 64),
+        (256, 256, 1, 0, 0, 256, 128, 64), (256, 256, 1, 64, 0, 256, 128, 64),
+        (100, 100, 0, 0, 0, 100, 64, 64), (10, 0, 0, 0, 0, 0, 128, 64),
+    ]
+    inp = "\n".join(" ".join(map(str, c)) for c in cases) + "\n"
+    out = subprocess.run([plan_check], input=inp, capture_output=True, text=True,
+                         check=True).stdout.split("\n")
+    pos = 0
+    for (Sq, Sk, causal, window, ip, kl, tm, tn) in cases:
+        _, nqt, nkt = out[pos].split()
+        pos += 1
+        plan = np.array([[int(ch) for ch in out[pos + r]] for r in range(int(nqt))],
+                        dtype=np.int8).reshape(int(nqt), int(nkt))
+        pos += int(nqt)
+        want = ora.tile_plan_ref(Sq, Sk, bool(causal), window, ip, kl, tm, tn)
+        np.testing.assert_array_equal(plan, want, err_msg=str((Sq, Sk, causal, window, ip, kl, tm, tn)))
+        assert out[pos] == f"rows {Sq}"
+        pos += 1
+        rows = np.array([list(map(int, out[pos + i].split())) for i in range(Sq)])
+        pos += Sq
+        j = np.arange(Sk)[None, :]
+        got = (j >= rows[:, :1]) & (j < rows[:, 1:])
+        np.testing.assert_array_equal(got, ora.allowed_mask(Sq, Sk, bool(causal), window, ip, kl))

@@ -1,0 +1,345 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the fp64 oracle.
+
+Tolerances: max-abs error <= 2e-2 on bf16 outputs, <= 1e-5 on float32
+outputs, LSE within 1e-3; mask dump and tile plan bit-exact.  Inputs are the
+seeded generators of ``scaled_dot_product_attn_amd.workloads``; the oracle is
+fed the exact values that went to the GPU.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_dot_product_attn_amd as attn
+from scaled_dot_product_attn_amd import workloads as wl
+from oracle import attn_oracle as ora
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_F32 = 1e-5
+TOL_LSE = 1e-3
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _run_prefill(w, lse=True):
+    q, k, v = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV)
+    kl = None if w.k_lengths is None else w.k_lengths.to(DEV)
+    O, L = attn.sdpa(q, k, v, w.causal, w.window, w.input_pos, kl, return_lse=True)
+    torch.cuda.synchronize()
+    return O, L
+
+
+def _check_prefill(w, O, L, tol, heads=None, rows=None):
+    kl = None if w.k_lengths is None else w.k_lengths.cpu().numpy()
+    Or, Lr = ora.attn_ref(_np(w.q), _np(w.k), _np(w.v), w.causal, w.window,
+                          w.input_pos, kl, heads=heads, rows=rows)
+    On, Ln = _np(O), _np(L)
+    sel = ~np.isnan(Lr)
+    if heads is not None or rows is not None:
+        On, Ln = np.where(np.isnan(Or), np.nan, On), np.where(sel, Ln, np.nan)
+    err = np.nanmax(np.abs(On - Or))
+    assert err <= tol, f"O max-abs error {err} > {tol}"
+    inf_ref = np.isneginf(Lr[sel])
+    np.testing.assert_array_equal(np.isneginf(Ln[sel]), inf_ref)
+    fin = sel & np.isfinite(Lr)
+    if fin.any():
+        lerr = np.max(np.abs(Ln[fin] - Lr[fin]))
+        assert lerr <= TOL_LSE, f"LSE error {lerr}"
+    return err
+
+
+# ---------------------------------------------------------------------------
+# mask predicate and tile plan: bit-exact
+# ---------------------------------------------------------------------------
+
+MASK_CASES = [
+    (128, 128, 1, 0, 0, 128), (257, 257, 1, 0, 0, 257), (100, 300, 1, 0, 200, 300),
+    (300, 300, 1, 64, 0, 300), (192, 1000, 1, 100, 800, 1000), (64, 64, 0, 0, 0, 64),
+    (130, 130, 0, 0, 0, 77), (50, 90, 1, 7, -20, 90), (333, 333, 1, 1, 0, 333),
+    (129, 700, 1, 0, 600, 650), (64, 64, 1, 0, 0, 0), (200, 64, 1, 3, 100, 64),
+    (256, 256, 1, 300, 0, 256), (77, 5000, 1, 129, 4900, 4950),
+]
+
+
+@pytest.mark.parametrize("Sq,Sk,causal,window,ip,kl", MASK_CASES)
+def test_mask_dump_bitexact(Sq, Sk, causal, window, ip, kl):
+    M = torch.empty(Sq, Sk, dtype=torch.uint8, device=DEV)
+    attn.attn_mask_dump(M, Sq, Sk, causal, window, ip, kl)
+    want = ora.allowed_mask(Sq, Sk, bool(causal), window, ip, kl)
+    np.testing.assert_array_equal(M.cpu().numpy().astype(bool), want)
+
+
+@pytest.mark.parametrize("Sq,Sk,causal,window,ip,kl", MASK_CASES + [
+    (4096, 4096, 1, 0, 0, 4096), (2048, 16384, 1, 4096, 14336, 16384), (4096, 4096, 0, 0, 0, 4096)])
+def test_tile_plan_bitexact(Sq, Sk, causal, window, ip, kl):
+    nqt, nkt = -(-Sq // attn.TILE_M), -(-Sk // attn.TILE_N)
+    P = torch.empty(nqt, nkt, dtype=torch.int8, device=DEV)
+    attn.attn_tile_plan(P, Sq, Sk, causal, window, ip, kl)
+    want = ora.tile_plan_ref(Sq, Sk, bool(causal), window, ip, kl, attn.TILE_M, attn.TILE_N)
+    np.testing.assert_array_equal(P.cpu().numpy(), want)
+
+
+# ---------------------------------------------------------------------------
+# prefill, bf16
+# ---------------------------------------------------------------------------
+
+BF16_CASES = [
+    # B, H, Hkv, Sq, Sk, D, causal, window, input_pos, k_lengths
+    (1, 4, 1, 256, 256, 128, True, 0, 0, None),
+    (2, 4, 2, 257, 257, 128, True, 0, 0, None),
+    (1, 2, 2, 300, 300, 128, False, 0, 0, None),
+    (1, 4, 4, 100, 400, 128, True, 0, 300, None),
+    (1, 8, 2, 384, 1000, 128, True, 128, 616, None),
+    (2, 4, 1, 200, 333, 128, True, 0, 133, [333, 250]),
+    (2, 2, 1, 130, 190, 128, False, 0, 0, [190, 1]),
+    (1, 4, 2, 256, 256, 64, True, 0, 0, None),
+    (1, 2, 1, 65, 129, 64, True, 33, 64, None),
+    (1, 2, 2, 1, 1, 128, True, 0, 0, None),
+    (1, 2, 2, 7, 3, 128, False, 0, 0, None),
+    (1, 3, 3, 128, 128, 128, True, 1, 0, None),
+    (1, 2, 1, 96, 96, 128, True, 0, -40, None),           # leading rows see nothing
+    (1, 2, 1, 64, 256, 128, True, 16, 300, [200]),         # window past k_len: empty rows
+    (1, 8, 1, 512, 512, 128, True, 0, 0, None),           # MQA
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"c{int(c[6])}w{c[7]}p{c[8]}")
+def test_prefill_bf16_parity(case):
+    B, H, Hkv, Sq, Sk, D, causal, window, ip, kl = case
+    _say(f"prefill bf16 {case}")
+    w = wl.prefill_random(B, H, Hkv, Sq, Sk, D, torch.bfloat16, seed=7, causal=causal,
+                          window=window, input_pos=ip, k_lengths=kl)
+    O, L = _run_prefill(w)
+    _check_prefill(w, O, L, TOL_BF16)
+
+
+def test_prefill_bf16_no_lse_matches():
+    w = wl.prefill_random(1, 4, 2, 200, 200, 128, torch.bfloat16, seed=8, causal=True)
+    O1, _ = _run_prefill(w)
+    O2 = attn.sdpa(w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), True, return_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+
+
+def test_prefill_sk_zero_gives_zero_and_neg_inf():
+    q = torch.randn(1, 2, 70, 128, device=DEV).bfloat16()
+    k = torch.empty(1, 1, 0, 128, device=DEV, dtype=torch.bfloat16)
+    O, L = attn.sdpa(q, k, k, False)
+    torch.cuda.synchronize()
+    assert torch.all(O == 0) and torch.all(torch.isneginf(L))
+
+
+def test_identity_v_exposes_probabilities():
+    # V = I (Sk = D): O = P, so the zero pattern of O is exactly the mask.
+    Sq = Sk = D = 128
+    for causal, window, ip in [(True, 0, 0), (True, 37, 0), (False, 0, 0)]:
+        w = wl.prefill_random(1, 2, 1, Sq, Sk, D, torch.bfloat16, seed=9, causal=causal,
+                              window=window, input_pos=ip)
+        w.v = torch.eye(Sk, D).bfloat16()[None, None]
+        O, L = _run_prefill(w)
+        P = O.float().cpu().numpy()[0]
+        ok = ora.allowed_mask(Sq, Sk, causal, window, ip)
+        for h in range(2):
+            np.testing.assert_array_equal(P[h] != 0, ok)
+            np.testing.assert_allclose(P[h].sum(axis=1), 1.0, atol=2e-2)
+        _check_prefill(w, O, L, TOL_BF16)
+
+
+def test_nan_poison_outside_valid_keys():
+    # K/V past k_lengths (and past the causal frontier) hold NaN: never read.
+    B, H, Hkv, Sq, Sk, D = 2, 4, 2, 200, 512, 128
+    kls = [300, 137]
+    w = wl.prefill_random(B, H, Hkv, Sq, Sk, D, torch.bfloat16, seed=10, causal=True,
+                          input_pos=100, k_lengths=kls)
+    O_clean, L_clean = _run_prefill(w)
+    for b, n in enumerate(kls):
+        w.k[b, :, n:] = float("nan")
+        w.v[b, :, n:] = float("nan")
+    w.k[:, :, 100 + Sq:] = float("nan")   # beyond every query's position
+    w.v[:, :, 100 + Sq:] = float("nan")
+    O, L = _run_prefill(w)
+    assert torch.isfinite(O.float()).all()
+    assert torch.equal(O, O_clean) and torch.equal(L, L_clean)
+
+
+def test_prefill_deterministic_and_stream():
+    w = wl.prefill_random(2, 8, 2, 333, 333, 128, torch.bfloat16, seed=11, causal=True)
+    q, k, v = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV)
+    O1, L1 = attn.sdpa(q, k, v, True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        O2, L2 = attn.sdpa(q, k, v, True)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+def test_gqa_equals_repeated_heads_on_gpu():
+    w = wl.prefill_random(1, 8, 2, 256, 256, 128, torch.bfloat16, seed=12, causal=True)
+    O, L = _run_prefill(w)
+    wd = wl.Prefill("dense", w.q, w.k.repeat_interleave(4, 1), w.v.repeat_interleave(4, 1), True)
+    Od, Ld = _run_prefill(wd)
+    assert torch.equal(O, Od) and torch.equal(L, Ld)
+
+
+# ---------------------------------------------------------------------------
+# prefill, float32
+# ---------------------------------------------------------------------------
+
+F32_CASES = [
+    (1, 4, 4, 128, 128, 64, True, 0, 0, None),            # the tiny fp32 workload's shape
+    (2, 4, 2, 130, 200, 128, True, 0, 70, [200, 99]),
+    (1, 2, 1, 77, 77, 64, False, 0, 0, None),
+    (1, 2, 2, 90, 300, 128, True, 50, 210, None),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "x".join(map(str, c[:6])))
+def test_prefill_f32_parity(case):
+    B, H, Hkv, Sq, Sk, D, causal, window, ip, kl = case
+    _say(f"prefill f32 {case}")
+    w = wl.prefill_random(B, H, Hkv, Sq, Sk, D, torch.float32, seed=13, causal=causal,
+                          window=window, input_pos=ip, k_lengths=kl)
+    O, L = _run_prefill(w)
+    _check_prefill(w, O, L, TOL_F32)
+
+
+def test_tiny_f32_workload():
+    _say("workload tiny_f32")
+    w = wl.make("tiny_f32")
+    O, L = _run_prefill(w)
+    _check_prefill(w, O, L, TOL_F32)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: sampled rows against the oracle
+# ---------------------------------------------------------------------------
+
+def _sample_rows(Sq, rng, n=48):
+    fixed = [0, 1, 63, 64, 127, 128, Sq // 2, Sq - 129, Sq - 2, Sq - 1]
+    extra = rng.choice(Sq, size=n, replace=False).tolist()
+    return np.unique(np.clip(fixed + extra, 0, Sq - 1))
+
+
+@pytest.mark.parametrize("name", ["gqa_causal", "window_offset", "image_clustered"])
+def test_full_size_workload_sampled(name):
+    _say(f"workload {name}")
+    w = wl.make(name)
+    O, L = _run_prefill(w)
+    assert torch.isfinite(O.float()).all()
+    rng = np.random.default_rng(5)
+    B, H = w.q.shape[:2]
+    heads = sorted({(int(rng.integers(B)), int(rng.integers(H))) for _ in range(6)} |
+                   {(0, 0), (B - 1, H - 1)})
+    rows = _sample_rows(w.q.shape[2], rng)
+    err = _check_prefill(w, O, L, TOL_BF16, heads=heads, rows=rows)
+    _say(f"  {name}: sampled max-abs error {err:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# split-KV decode
+# ---------------------------------------------------------------------------
+
+def _check_decode(w, O, tol=TOL_BF16, batches=None):
+    Or, _ = ora.decode_ref(_np(w.q), _np(w.k), _np(w.v), w.lengths.cpu().numpy(),
+                           batches=batches)
+    On = _np(O)
+    sel = ~np.isnan(Or)
+    err = np.max(np.abs(On[sel] - Or[sel]))
+    assert err <= tol, f"decode max-abs error {err}"
+    return err
+
+
+DEC_CASES = [
+    # B, H, Hkv, D, smin, smax, n_splits
+    (4, 8, 2, 128, 1, 300, 8),
+    (3, 4, 4, 128, 60, 70, 3),
+    (5, 16, 2, 128, 100, 2000, 1),
+    (2, 8, 1, 64, 1, 500, 4),
+    (6, 32, 8, 128, 512, 4096, 8),
+    (2, 4, 4, 64, 64, 64, 64),
+]
+
+
+@pytest.mark.parametrize("case", DEC_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_decode_parity(case):
+    B, H, Hkv, D, smin, smax, ns = case
+    _say(f"decode {case}")
+    w = wl.decode_random(B, H, Hkv, D, smin, smax, ns, seed=21)
+    w.q, w.k, w.v, w.lengths = (t.to(DEV) for t in (w.q, w.k, w.v, w.lengths))
+    O = attn.decode(w.q, w.k, w.v, w.lengths, ns)
+    torch.cuda.synchronize()
+    _check_decode(w, O)
+
+
+def test_decode_edge_lengths_and_poison():
+    B, H, Hkv, D, Smax = 6, 8, 2, 128, 256
+    w = wl.decode_random(B, H, Hkv, D, 1, Smax, 8, seed=22, pad_value=float("nan"))
+    w.lengths = torch.tensor([0, 1, 63, 64, 65, 256], dtype=torch.int32)
+    g = torch.Generator().manual_seed(3)
+    for b, n in enumerate(w.lengths.tolist()):
+        w.k[b] = float("nan")
+        w.v[b] = float("nan")
+        w.k[b, :, :n] = torch.randn(Hkv, n, D, generator=g).bfloat16()
+        w.v[b, :, :n] = torch.randn(Hkv, n, D, generator=g).bfloat16()
+    w.q, w.k, w.v, w.lengths = (t.to(DEV) for t in (w.q, w.k, w.v, w.lengths))
+    for ns in (1, 2, 8, 64):
+        O = attn.decode(w.q, w.k, w.v, w.lengths, ns)
+        torch.cuda.synchronize()
+        assert torch.isfinite(O.float()).all()
+        assert torch.all(O[0] == 0)          # zero length -> zero output
+        _check_decode(w, O)
+
+
+def test_decode_splits_invariant_and_ws():
+    w = wl.decode_random(8, 16, 4, 128, 10, 3000, 8, seed=23)
+    w.q, w.k, w.v, w.lengths = (t.to(DEV) for t in (w.q, w.k, w.v, w.lengths))
+    outs = [attn.decode(w.q, w.k, w.v, w.lengths, ns) for ns in (1, 2, 3, 8, 64)]
+    nb = attn.attn_decode_workspace_bytes(8, 16, 8, 128)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    O_ws = torch.empty_like(w.q)
+    attn.attn_decode_ws(O_ws, w.q, w.k, w.v, w.lengths, 8, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(O_ws, outs[3])
+    for O in outs:
+        assert (O.float() - outs[0].float()).abs().max().item() <= TOL_BF16
+        _check_decode(w, O)
+
+
+def test_decode_matches_single_query_prefill():
+    w = wl.decode_random(4, 8, 2, 128, 1, 700, 8, seed=24)
+    w.q, w.k, w.v, w.lengths = (t.to(DEV) for t in (w.q, w.k, w.v, w.lengths))
+    O = attn.decode(w.q, w.k, w.v, w.lengths, 8)
+    for b, n in enumerate(w.lengths.tolist()):
+        Op, _ = attn.sdpa(w.q[b][None, :, None].contiguous(), w.k[b][None].contiguous(),
+                          w.v[b][None].contiguous(), True, 0, n - 1)
+        torch.cuda.synchronize()
+        assert (Op[0, :, 0].float() - O[b].float()).abs().max().item() <= TOL_BF16
+
+
+def test_decode_full_size_workload_sampled():
+    _say("workload decode_split")
+    w = wl.make("decode_split", device=DEV)
+    O = attn.decode(w.q, w.k, w.v, w.lengths, w.n_splits)
+    torch.cuda.synchronize()
+    assert torch.isfinite(O.float()).all()
+    lengths = w.lengths.cpu()
+    order = torch.argsort(lengths)
+    picks = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 0, 63})
+    sub = wl.Decode("sub", w.q[picks].cpu(), w.k[picks].cpu(), w.v[picks].cpu(),
+                    lengths[picks], w.n_splits)
+    err = _check_decode(sub, O[picks])
+    _say(f"  decode_split: sampled max-abs error {err:.3e}")
