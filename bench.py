@@ -1,0 +1,254 @@
+"""Throughput of the attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over resident synthetic inputs:
+  * prefill: causal GQA bf16 attention forward with LSE,
+    B=2, H=32, Hkv=8, Sq=Sk=4096, D=128                      (attn_fwd)
+  * decode:  split-KV bf16 decode, B=64, H=32, Hkv=8, D=128, lengths uniform
+    in [512, 32768] (cache 32768), n_splits=8               (attn_decode_ws)
+both launched on the same stream.  ``value`` is the prefill rate in TFLOP/s of
+algorithmic work (4*D flops per allowed (query, key) pair) divided by the
+prefill kernel's mean duration from HIP events over the timed steps; the
+decode rate in GB/s (K/V bytes of the valid keys, once per KV head, plus Q and
+O) is reported beside it.  The window/offset and clustered-image workloads are
+timed too, as extra lines of context.  ``cpu_baseline`` times the fp64 oracle
+on the host on a bounded sample (whole heads) of the prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("attn fwd bf16 TFLOP/s (prefill) + decode KV GB/s, % of roofline, 1 MI355X")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "prefill": ["scaled_dot_product_attn_amd/csrc/attn_fwd_bf16.hip",
+                "scaled_dot_product_attn_amd/csrc/attn_common.h"],
+    "decode": ["scaled_dot_product_attn_amd/csrc/attn_decode.hip"],
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def allowed_pairs(Sq, Sk, causal, window, input_pos, k_len):
+    """Allowed (query, key) pairs of one (batch, head), counted row by row."""
+    import numpy as np
+    p = input_pos + np.arange(Sq, dtype=np.int64)
+    kl = min(max(k_len, 0), Sk)
+    hi = np.clip(p + 1, 0, kl) if causal else np.full(Sq, kl)
+    lo = np.clip(p - window + 1, 0, kl) if window > 0 else np.zeros(Sq, dtype=np.int64)
+    return int(np.maximum(hi - lo, 0).sum())
+
+
+def prefill_flops(w) -> int:
+    B, H, Sq, D = w.q.shape
+    Sk = w.k.shape[2]
+    total = 0
+    for b in range(B):
+        kl = Sk if w.k_lengths is None else int(w.k_lengths[b])
+        total += H * allowed_pairs(Sq, Sk, w.causal, w.window, w.input_pos, kl)
+    return 4 * D * total
+
+
+def decode_bytes(w) -> int:
+    B, H, D = w.q.shape
+    Hkv = w.k.shape[1]
+    lens = w.lengths.cpu().clamp(0, w.k.shape[2]).long().sum().item()
+    return int(lens) * Hkv * D * 2 * 2 + B * H * D * 2 * 2
+
+
+def traffic_for(kind: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash(kind):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float):
+    """The fp64 oracle on whole (batch, head) pairs of the prefill workload."""
+    import numpy as np
+    from oracle import attn_oracle as ora
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    q = w.q.float().cpu().numpy().astype(np.float64)
+    k = w.k.float().cpu().numpy().astype(np.float64)
+    v = w.v.float().cpu().numpy().astype(np.float64)
+    B, H, Sq, D = q.shape
+    per_head = 4 * D * allowed_pairs(Sq, w.k.shape[2], w.causal, w.window, w.input_pos,
+                                     w.k.shape[2])
+    done, t0 = 0, time.perf_counter()
+    for b in range(B):
+        for h in range(H):
+            ora.attn_ref(q, k, v, w.causal, w.window, w.input_pos, None, heads=[(b, h)])
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": per_head * done / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} of {B * H} (batch, head) pairs of the causal GQA prefill "
+                      f"(Sq=Sk={Sq}, D={D}), fp64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernels run on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import scaled_dot_product_attn_amd as attn
+    from scaled_dot_product_attn_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating inputs")
+    pre = wl.make("gqa_causal", device=dev)
+    dec = wl.make("decode_split", device=dev)
+    extra = {} if args.no_extra else {n: wl.make(n, device=dev)
+                                     for n in ("window_offset", "image_clustered")}
+    B, H, Sq, D = pre.q.shape
+    O = torch.empty_like(pre.q)
+    LSE = torch.empty(B, H, Sq, dtype=torch.float32, device=dev)
+    Od = torch.empty_like(dec.q)
+    Bd, Hd, Dd = dec.q.shape
+    ws = torch.empty(attn.attn_decode_workspace_bytes(Bd, Hd, dec.n_splits, Dd),
+                     dtype=torch.uint8, device=dev)
+    ext_out = {n: (torch.empty_like(w.q),
+                   torch.empty(w.q.shape[:3], dtype=torch.float32, device=dev))
+               for n, w in extra.items()}
+    stream = torch.cuda.current_stream()
+
+    def run_prefill(w, o, l):
+        attn.attn_fwd(o, w.q, w.k, w.v, l, w.causal, w.window, w.input_pos, w.k_lengths)
+
+    def run_decode():
+        attn.attn_decode_ws(Od, dec.q, dec.k, dec.v, dec.lengths, dec.n_splits, ws)
+
+    names = ["prefill", "decode"] + list(extra)
+    ev = {n: [] for n in names}
+
+    def step(record):
+        marks = {}
+        for n in names:
+            if record:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record(stream)
+            if n == "prefill":
+                run_prefill(pre, O, LSE)
+            elif n == "decode":
+                run_decode()
+            else:
+                run_prefill(extra[n], *ext_out[n])
+            if record:
+                e.record(stream)
+                marks[n] = (s, e)
+        if record:
+            for n in names:
+                ev[n].append(marks[n])
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: sum(s.elapsed_time(e) for s, e in ev[n]) / args.steps for n in names}
+    log("kernel ms: " + ", ".join(f"{n}={ms[n]:.4f}" for n in names))
+
+    fl = prefill_flops(pre)
+    pre_tf = fl / (ms["prefill"] * 1e-3) / 1e12
+    db = decode_bytes(dec)
+    dec_gbs = db / (ms["decode"] * 1e-3) / 1e9
+
+    def roof(bound, achieved, peak, unit, traffic):
+        return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic}
+
+    out = {
+        "metric": METRIC,
+        "value": round(pre_tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gqa_causal prefill + decode_split decode",
+            "prefill": "B=2 H=32 Hkv=8 Sq=Sk=4096 D=128 causal, LSE saved",
+            "decode": "B=64 H=32 Hkv=8 D=128 len~U[512,32768] cache 32768 n_splits=8",
+            "prefill_flops": fl,
+            "decode_bytes": db,
+        },
+        "roofline": roof("mfma", pre_tf, PEAK_BF16_TFLOPS, "TFLOP/s", traffic_for("prefill")),
+        "prefill_ms": round(ms["prefill"], 4),
+        "decode": {
+            "value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(ms["decode"], 4),
+            "roofline": roof("hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", traffic_for("decode")),
+        },
+    }
+    if extra:
+        out["extra"] = {}
+        for n, w in extra.items():
+            f = prefill_flops(w)
+            tf = f / (ms[n] * 1e-3) / 1e12
+            out["extra"][n] = {"ms": round(ms[n], 4), "TFLOP/s": round(tf, 2),
+                               "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": f}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        out["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

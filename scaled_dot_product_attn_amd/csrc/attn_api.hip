@@ -66,6 +66,8 @@ static int check_fwd(const void* O, const void* Q, const void* K,
   if (window > 0 && !causal) return ATTN_EINVAL;
   if (D != 64 && D != 128) return ATTN_EUNSUPPORTED;
   if (Sq > INT_MAX - 256 || Sk > INT_MAX - 256) return ATTN_EUNSUPPORTED;
+  // K/V rows of one KV head are addressed through 32-bit buffer offsets
+  if ((long long)Sk * D * 4 + 65536 > INT_MAX) return ATTN_EUNSUPPORTED;
   const long long nqt = ((long long)Sq + 127) / 64;  // finest row tiling used
   if (nqt * H * B > INT_MAX) return ATTN_EUNSUPPORTED;
   if ((long long)B * H > INT_MAX / 2 || (long long)B * Hkv > INT_MAX / 2)
@@ -83,6 +85,8 @@ static int check_decode(const void* O, const void* Q, const void* K,
   if (H % Hkv != 0) return ATTN_EINVAL;
   if (D != 64 && D != 128) return ATTN_EUNSUPPORTED;
   if (Smax > INT_MAX - 256) return ATTN_EUNSUPPORTED;
+  // K/V rows of one KV head are addressed through 32-bit buffer offsets
+  if ((long long)Smax * D * 2 + 65536 > INT_MAX) return ATTN_EUNSUPPORTED;
   if ((long long)B * H * n_splits > INT_MAX / 2) return ATTN_EUNSUPPORTED;
   if ((long long)B * Hkv * H * n_splits > INT_MAX) return ATTN_EUNSUPPORTED;
   if (!O || !Q || !K || !V || !lengths) return ATTN_EINVAL;

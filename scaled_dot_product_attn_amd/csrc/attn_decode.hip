@@ -10,11 +10,13 @@
 // built for streaming, not for the matrix cores:
 //   * one workgroup = (sequence, KV head, slice[, head chunk]); it serves every
 //     query head of the GQA group, so each K/V byte is read from HBM once;
-//   * D/16 lanes share a key, each holding 16 of its d values (32 contiguous
-//     bytes of K and of V); a wave reads whole 256-byte key rows;
+//   * D/8 lanes share a key, each holding one 16-byte chunk (8 d values) of
+//     K and of V; a wave reads whole 256-byte key rows;
 //   * dot products with v_dot2c_f32_bf16 straight from the bf16 words, the
-//     per-key sum by butterfly exchanges across the D/16 lanes;
-//   * two key tiles in flight per thread (register double buffer);
+//     per-key sum by butterfly exchanges across the D/8 lanes;
+//   * a ring of four key passes in flight per thread, loaded through buffer
+//     resources that cover exactly the slice's keys, and about 100 VGPRs so
+//     four waves share each SIMD: enough bytes in flight to cover HBM latency;
 //   * nothing past lengths[b] is ever read;
 //   * the longest sequences are dealt first (rank by length) so the long
 //     slices do not form the tail.
@@ -32,11 +34,32 @@ constexpr int kDecThreads = 256;
 constexpr int kDecTileN = 64;
 constexpr float kDecLazy = 8.0f;
 constexpr int kDecSortMaxB = 256;
+constexpr int kDecStages = 4;              // key passes in flight per thread
+// Word 3 of a gfx9-family raw buffer resource: out-of-range reads return 0.
+constexpr int kDecRsrcWord3 = 0x00020000;
 
 __device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c,
                                          false);
+}
+
+// Sum over aligned groups of LPK lanes (LPK in {2, 4, 8, 16}) with DPP moves:
+// swap neighbours, swap pairs, mirror within 8 lanes, mirror within 16 lanes.
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int LPK>
+__device__ inline float group_sum(float x) {
+  static_assert(LPK == 2 || LPK == 4 || LPK == 8 || LPK == 16, "group size");
+  x += dpp_mov<0xB1>(x);                  // quad_perm [1,0,3,2]
+  if (LPK >= 4) x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  if (LPK >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror
+  if (LPK >= 16) x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
 }
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -62,17 +85,16 @@ __device__ inline void split_range(int len, int n_splits, int s, int* k_begin,
 }
 
 template <int D, int GM>
-__global__ __launch_bounds__(kDecThreads) void attn_decode_split_kernel(
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void attn_decode_split_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, const int32_t* __restrict__ lengths,
     float* __restrict__ Opart, float* __restrict__ Lpart,
     __bf16* __restrict__ O, int B, int H, int Hkv, int Smax, int n_splits,
     int n_hchunks, float scale_log2) {
-  constexpr int LPK = D / 16;                 // lanes per key
-  constexpr int NG = kDecThreads / LPK;       // keys per pass
-  constexpr int KPT = kDecTileN / NG;         // keys per thread per tile
-  constexpr int NGW = 64 / LPK;               // key groups per wave
-  static_assert(KPT >= 1, "tile smaller than a pass");
+  constexpr int LPK = D / 8;               // lanes per key, 8 d (16 bytes) each
+  constexpr int KPP = kDecThreads / LPK;   // keys per pass of the workgroup
+  constexpr int NS = kDecStages;           // passes in flight per thread
 
   __shared__ int s_b;
   __shared__ float s_m[4][GM];
@@ -82,8 +104,8 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_split_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int li = tid % LPK;  // which 16-wide d slice
-  const int gi = tid / LPK;  // key group within the workgroup
+  const int li = tid % LPK;  // which 8-wide d chunk
+  const int gi = tid / LPK;  // key slot within a pass
 
   // ---- work item: (rank, kv head, head chunk, slice) ----
   const int lid = blockIdx.x;
@@ -119,121 +141,110 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_split_kernel(
   const int h0 = g * G + hc * GM;
   const int nh = min(GM, G - hc * GM);
 
-  // query slices, bf16 pairs
-  uint32_t q[GM][8];
+  // query chunks, bf16 pairs
+  uint32_t q[GM][4];
 #pragma unroll
   for (int hh = 0; hh < GM; ++hh) {
     const int hq = h0 + (hh < nh ? hh : 0);
-    const u32x4_t* qp =
-        (const u32x4_t*)(Q + ((size_t)b * H + hq) * D + li * 16);
-    const u32x4_t a = qp[0], c = qp[1];
+    const u32x4_t a = *(const u32x4_t*)(Q + ((size_t)b * H + hq) * D + li * 8);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      q[hh][w] = a[w];
-      q[hh][4 + w] = c[w];
-    }
+    for (int w = 0; w < 4; ++w) q[hh][w] = a[w];
   }
 
-  float m[GM], l[GM], acc[GM][16];
+  float m[GM], l[GM], acc[GM][8];
 #pragma unroll
   for (int hh = 0; hh < GM; ++hh) {
     m[hh] = -INFINITY;
     l[hh] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[hh][e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
   }
 
-  const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Smax * D;
-  const __bf16* Kp = K + kv_base + li * 16;
-  const __bf16* Vp = V + kv_base + li * 16;
+  // Buffer resources covering exactly this slice's keys: reads past k_end
+  // (the padded part of the cache included) return zeros without a branch.
+  const size_t kv_base =
+      ((size_t)b * Hkv + g) * (size_t)Smax * D + (size_t)k_begin * D;
+  const int nbytes = (k_end - k_begin) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(K + kv_base), (short)0, nbytes, kDecRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(V + kv_base), (short)0, nbytes, kDecRsrcWord3);
+  const int lane_off = (gi * D + li * 8) * 2;
 
-  u32x4_t kr[2][KPT][2], vr[2][KPT][2];
-  auto fetch = [&](int slot, int base) {
+  const int nkeys = k_end - k_begin;
+  const int npass = (nkeys + KPP - 1) / KPP;
+  const int nround = (npass + NS - 1) / NS;
+  // Ring of NS passes in flight, refilled one round (NS passes) ahead.  Round
+  // -1 runs on zeros and only issues the first loads, and the body has no
+  // branch, so the wait before each use counts exactly the loads issued after
+  // it.  K for round r+1 is requested once round r's scores are done, V once
+  // round r's P.V is done.
+  u32x4_t kr[NS], vr[NS];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int key = base + gi + NG * u;
-      if (key < k_end) {
-        const u32x4_t* kp = (const u32x4_t*)(Kp + (size_t)key * D);
-        const u32x4_t* vp = (const u32x4_t*)(Vp + (size_t)key * D);
-        kr[slot][u][0] = kp[0];
-        kr[slot][u][1] = kp[1];
-        vr[slot][u][0] = vp[0];
-        vr[slot][u][1] = vp[1];
-      } else {
-        kr[slot][u][0] = kr[slot][u][1] = u32x4_t{0, 0, 0, 0};
-        vr[slot][u][0] = vr[slot][u][1] = u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
+  for (int st = 0; st < NS; ++st) kr[st] = vr[st] = u32x4_t{0, 0, 0, 0};
 
-  const int ntiles = (k_end - k_begin + kDecTileN - 1) / kDecTileN;
-  if (ntiles > 0) fetch(0, k_begin);
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
-    const int base = k_begin + it * kDecTileN;
-    if (it + 1 < ntiles) fetch(cur ^ 1, base + kDecTileN);
-
-    float tsc[KPT][GM];
+  for (int rd = -1; rd < nround; ++rd) {
+    float tsc[NS][GM];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const bool valid = base + gi + NG * u < k_end;
+    for (int st = 0; st < NS; ++st) {
+      const bool valid = rd >= 0 && (rd * NS + st) * KPP + gi < nkeys;
 #pragma unroll
       for (int hh = 0; hh < GM; ++hh) {
         float a = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          a = dot2_bf16(q[hh][w], kr[cur][u][0][w], a);
-          a = dot2_bf16(q[hh][4 + w], kr[cur][u][1][w], a);
-        }
-#pragma unroll
-        for (int x = 1; x < LPK; x <<= 1) a += __shfl_xor(a, x);
-        tsc[u][hh] = valid ? a * scale_log2 : -INFINITY;
+        for (int w = 0; w < 4; ++w) a = dot2_bf16(q[hh][w], kr[st][w], a);
+        a = group_sum<LPK>(a);
+        tsc[st][hh] = valid ? a * scale_log2 : -INFINITY;
       }
     }
-
-    bool need_any = false;
-    float tmax[GM];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int off = lane_off + ((rd + 1) * NS + st) * KPP * D * 2;
+      kr[st] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+    }
+    // keep the refills here: the scheduler would otherwise sink them next to
+    // their use a round later and expose the memory latency
+    __builtin_amdgcn_sched_barrier(0);
+    // Lazy running max, once per round and without a branch: m moves only
+    // when the round's max exceeds it by more than 2^8.
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh) {
-      tmax[hh] = tsc[0][hh];
+      float mx = tsc[0][hh];
 #pragma unroll
-      for (int u = 1; u < KPT; ++u) tmax[hh] = fmaxf(tmax[hh], tsc[u][hh]);
-      need_any |= tmax[hh] > m[hh] + kDecLazy;
+      for (int st = 1; st < NS; ++st) mx = fmaxf(mx, tsc[st][hh]);
+      const bool need = mx > m[hh] + kDecLazy;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m[hh] - mx) : 1.f;
+      m[hh] = need ? mx : m[hh];
+      l[hh] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
     }
-    if (__builtin_amdgcn_ballot_w64(need_any)) {
 #pragma unroll
-      for (int hh = 0; hh < GM; ++hh) {
-        const bool need = tmax[hh] > m[hh] + kDecLazy;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m[hh] - tmax[hh]) : 1.f;
-        m[hh] = need ? tmax[hh] : m[hh];
-        l[hh] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[hh][e] *= alpha;
-      }
-    }
-
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      float vf[16];
+    for (int st = 0; st < NS; ++st) {
+      float vf[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        vf[2 * w] = bf16_lo(vr[cur][u][0][w]);
-        vf[2 * w + 1] = bf16_hi(vr[cur][u][0][w]);
-        vf[8 + 2 * w] = bf16_lo(vr[cur][u][1][w]);
-        vf[8 + 2 * w + 1] = bf16_hi(vr[cur][u][1][w]);
+        vf[2 * w] = bf16_lo(vr[st][w]);
+        vf[2 * w + 1] = bf16_hi(vr[st][w]);
       }
 #pragma unroll
       for (int hh = 0; hh < GM; ++hh) {
         const float mref = m[hh] == -INFINITY ? 0.f : m[hh];
-        const float p = __builtin_amdgcn_exp2f(tsc[u][hh] - mref);
-        l[hh] += p;
+        const float pr = __builtin_amdgcn_exp2f(tsc[st][hh] - mref);
+        l[hh] += pr;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[hh][e] = __builtin_fmaf(p, vf[e], acc[hh][e]);
+        for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(pr, vf[e], acc[hh][e]);
       }
     }
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int off = lane_off + ((rd + 1) * NS + st) * KPP * D * 2;
+      vr[st] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- merge the key groups of the workgroup ----
+  // ---- merge the key slots of the workgroup ----
 #pragma unroll
   for (int hh = 0; hh < GM; ++hh) {
     float mw = m[hh];
@@ -251,7 +262,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_split_kernel(
 #pragma unroll
     for (int x = LPK; x < 64; x <<= 1) lw += __shfl_xor(lw, x);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 8; ++e) {
       float a = acc[hh][e] * f;
 #pragma unroll
       for (int x = LPK; x < 64; x <<= 1) a += __shfl_xor(a, x);
@@ -259,7 +270,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_split_kernel(
     }
     if (lane < LPK) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s_acc[wave][hh][li * 16 + e] = acc[hh][e];
+      for (int e = 0; e < 8; ++e) s_acc[wave][hh][li * 8 + e] = acc[hh][e];
       if (li == 0) s_l[wave][hh] = lw;
     }
   }

@@ -47,6 +47,9 @@ constexpr int kFwdThreads = kFwdWaves * 64;
 constexpr int kFwdTileM = kFwdWaves * 32;  // query rows per workgroup
 constexpr int kFwdTileN = 64;              // keys per tile
 constexpr float kLazyRescale = 8.0f;       // log2 headroom before m is raised
+// Word 3 of a gfx9-family buffer resource (32-bit data format, no swizzle):
+// a raw buffer whose out-of-range reads return zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 static_assert(kFwdTileM == ATTN_FWD_TILE_M && kFwdTileN == ATTN_FWD_TILE_N,
               "the exported tile plan must use the kernel's tile sizes");
 
@@ -80,7 +83,8 @@ __device__ inline int vt_group_pos(int quad_in_group) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(kFwdThreads)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     __bf16* __restrict__ O, const __bf16* __restrict__ Q,
     const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     float* __restrict__ LSE, int B, int H, int Hkv, int Sq, int Sk, int causal,
@@ -130,8 +134,6 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
 
   const size_t q_base = ((size_t)(b * H + h) * Sq) * D;
   const size_t kv_base = ((size_t)(b * Hkv + g) * Sk) * D;
-  const __bf16* Kp = K + kv_base;
-  const __bf16* Vp = V + kv_base;
 
   // ---- my query row ----
   const int qi = i0 + wave * 32 + lrow;  // global query row of this lane
@@ -166,24 +168,36 @@ __global__ __launch_bounds__(kFwdThreads) void attn_fwd_bf16_kernel(
   const int vkq = tid & 15;  // key quad within the tile (V staging)
   const int vdc = tid >> 4;  // 8-wide d chunk (V staging)
 
+  // K/V are read through buffer resources whose range is exactly the keys
+  // some row of this workgroup may attend, [union_lo, union_hi): the hardware
+  // range check returns zeros for any other key, so keys that no row may see
+  // (past k_lengths, past the causal frontier, before the window) are never
+  // read and the loads need no branches.
+  const int nvalid = geo.union_hi - geo.union_lo;
+  const size_t valid_base = kv_base + (size_t)geo.union_lo * D;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(K + valid_base), (short)0, nvalid * D * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(V + valid_base), (short)0, nvalid * D * 2, kBufferRsrcWord3);
+
   auto fetch = [&](int kt) {
-    const int j0 = kt * kFwdTileN;
+    const int rel0 = kt * kFwdTileN - geo.union_lo;  // tile start, in valid keys
 #pragma unroll
     for (int i = 0; i < KLOADS; ++i) {
       const int c = i * kFwdThreads + tid;
-      const int key = j0 + c / (D / 8);
+      const int key = rel0 + c / (D / 8);
       const int dch = c % (D / 8);
-      const bool ok = key >= geo.union_lo && key < geo.union_hi;
-      kst[i] = ok ? *(const u32x4_t*)(Kp + (size_t)key * D + dch * 8)
-                  : u32x4_t{0, 0, 0, 0};
+      kst[i] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                       krsrc, (key * D + dch * 8) * 2, 0, 0));
     }
     if (VTHREADS == kFwdThreads || tid < VTHREADS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = j0 + vkq * 4 + i;
-        const bool ok = key >= geo.union_lo && key < geo.union_hi;
-        vst[i] = ok ? *(const u32x4_t*)(Vp + (size_t)key * D + vdc * 8)
-                    : u32x4_t{0, 0, 0, 0};
+        const int key = rel0 + vkq * 4 + i;
+        vst[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         vrsrc, (key * D + vdc * 8) * 2, 0, 0));
       }
     }
   };

@@ -1,0 +1,36 @@
+"""CPU checks of bench.py's work accounting against the oracle's mask."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from oracle import attn_oracle as ora  # noqa: E402
+
+
+@pytest.mark.parametrize("Sq,Sk,causal,window,ip,kl", [
+    (300, 300, True, 0, 0, 300), (128, 1000, True, 100, 872, 1000), (64, 64, False, 0, 0, 40),
+    (90, 200, True, 7, -30, 150), (50, 50, True, 0, 60, 50),
+])
+def test_allowed_pairs_matches_oracle_mask(Sq, Sk, causal, window, ip, kl):
+    assert bench.allowed_pairs(Sq, Sk, causal, window, ip, kl) == \
+        ora.allowed_pairs(Sq, Sk, causal, window, ip, kl)
+
+
+def test_workload_flops_closed_forms():
+    # causal square: S(S+1)/2 pairs per head; window: Sq*W; full: Sq*Sk.
+    assert bench.allowed_pairs(4096, 4096, True, 0, 0, 4096) * 64 * 512 == 274945015808
+    assert bench.allowed_pairs(2048, 16384, True, 4096, 14336, 16384) * 32 * 512 == 137438953472
+    assert bench.allowed_pairs(4096, 4096, False, 0, 0, 4096) * 32 * 512 == 274877906944
+
+
+def test_multi_gpu_request_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
