@@ -14,6 +14,9 @@ timed too, as extra lines of context.  ``cpu_baseline`` times the fp64 oracle
 on the host on a bounded sample (whole heads) of the prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+The GPU needs about a hundred prefill launches to reach its steady clock, so
+the default warm-up is 100 steps.
 """
 
 from __future__ import annotations
@@ -124,8 +127,8 @@ def cpu_baseline(w, seconds: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")

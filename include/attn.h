@@ -71,7 +71,7 @@ extern "C" {
 
 /* Prefill tile sizes used by attn_fwd (rows of Q per workgroup, keys per
  * K/V tile); attn_tile_plan reports the plan at these sizes. */
-#define ATTN_FWD_TILE_M 128
+#define ATTN_FWD_TILE_M 256
 #define ATTN_FWD_TILE_N 64
 
 /* Prefill forward, bfloat16 Q/K/V/O, float32 accumulation and LSE.

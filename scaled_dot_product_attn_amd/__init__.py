@@ -23,7 +23,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
-TILE_M, TILE_N = 128, 64  # prefill tile sizes (ATTN_FWD_TILE_M / _N)
+TILE_M, TILE_N = 256, 64  # prefill tile sizes (ATTN_FWD_TILE_M / _N)
 
 _lib = None
 
@@ -164,7 +164,7 @@ def attn_mask_dump(M, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
 
 def attn_tile_plan(P, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
                    stream=None) -> None:
-    """The prefill kernel's tile plan into P (int8 (ceil(Sq/128), ceil(Sk/64)))."""
+    """The prefill kernel's tile plan into P (int8 (ceil(Sq/256), ceil(Sk/64)))."""
     rc = lib().attn_tile_plan(_ptr(P), Sq, Sk, int(bool(causal)), int(window),
                               int(input_pos), Sk if k_len is None else int(k_len),
                               _stream(stream))

@@ -7,11 +7,23 @@
 // sliding_window_mask with -inf at blocked positions).
 //
 // Work decomposition
-//   One workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//   owns 32 rows.  The workgroup walks the key tiles of TILE_N = 64 keys that
-//   its rows can see (empty tiles are never visited), staging K and V^T
-//   through LDS with a register double buffer: tile t+1 is fetched from HBM
-//   while tile t is multiplied.
+//   One workgroup = 8 waves = 256 query rows of one (batch, head); each wave
+//   owns 32 rows.  The workgroup walks the 64-key tiles its rows can see
+//   (empty tiles are never visited).
+//
+// Ping-pong between two wave groups.  Waves 0-3 (group A) and 4-7 (group B)
+// sit one per SIMD each, so every SIMD holds one wave of each group.  Each
+// wave alternates two phases, separated by workgroup barriers:
+//   M-phase k: O += P(k-1) V(k-1) and S(k) = K(k) Q^T   (32 MFMAs)
+//   V-phase k: mask and online softmax of S(k) -> P(k), plus staging
+// and group B runs one phase behind group A, so while one wave of a SIMD
+// feeds the matrix core the other works on the vector ALU.
+//
+// Staging: K and V^T each have a two-tile LDS ring.  In V-phase k group A
+// stores K(k+1) and group B stores V(k+1) (transposed), from registers loaded
+// by buffer loads issued one V-phase earlier.  Reads of K(k) happen in the
+// M-phases k of both groups, reads of V(k) in the M-phases k+1, so no buffer
+// is rewritten while a group may still read it.
 //
 // Contractions on the matrix cores (v_mfma_f32_32x32x16_bf16), transposed so
 // that one lane owns one query row:
@@ -42,8 +54,9 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = 8;               // two groups of four
 constexpr int kFwdThreads = kFwdWaves * 64;
+constexpr int kGroupThreads = kFwdThreads / 2;
 constexpr int kFwdTileM = kFwdWaves * 32;  // query rows per workgroup
 constexpr int kFwdTileN = 64;              // keys per tile
 constexpr float kLazyRescale = 8.0f;       // log2 headroom before m is raised
@@ -62,8 +75,9 @@ struct FwdLds {
   // V^T tile: D rows of kFwdTileN bf16 keys (permuted order), padded likewise.
   static constexpr int kRowV = kFwdTileN * 2 + 16;
   static constexpr int kBytesV = D * kRowV;
-  static constexpr int kBuf = kBytesK + kBytesV;
-  static constexpr int kTotal = 2 * kBuf;
+  // two K buffers, then two V^T buffers
+  static constexpr int kOffV = 2 * kBytesK;
+  static constexpr int kTotal = 2 * kBytesK + 2 * kBytesV;
 };
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
@@ -72,8 +86,17 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ inline float wave_max_pair(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+// Reductions over the lane pair (l, l ^ 32): v_permlane32_swap hands each lane
+// both values (in some order), so combining its two results is symmetric.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Position of a key inside its 16-key group in the V^T rows: keys 4..7 and
@@ -93,14 +116,16 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   using L = FwdLds<D>;
   constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int DBLK = D / 32;     // 32-wide blocks of the head dimension
-  constexpr int KLOADS = kFwdTileN * D / 8 / kFwdThreads;  // 16B K loads/thread
-  constexpr int VTHREADS = (kFwdTileN / 4) * (D / 8);      // threads staging V
+  constexpr int KLOADS = kFwdTileN * D / 8 / kGroupThreads;  // K loads/thread
+  constexpr int VTHREADS = (kFwdTileN / 4) * (D / 8);        // threads staging V
 
   __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int grp = wave >> 2;              // 0: group A, 1: group B
+  const int gtid = tid & (kGroupThreads - 1);  // thread index within the group
   const int lrow = lane & 31;  // query row (within the wave) this lane owns
   const int half = lane >> 5;  // which half of each MFMA k-slice this lane feeds
 
@@ -163,63 +188,64 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   }
 
   // ---- staging: global -> registers -> LDS ----
-  u32x4_t kst[KLOADS];
-  u32x4_t vst[4];
-  const int vkq = tid & 15;  // key quad within the tile (V staging)
-  const int vdc = tid >> 4;  // 8-wide d chunk (V staging)
-
   // K/V are read through buffer resources whose range is exactly the keys
   // some row of this workgroup may attend, [union_lo, union_hi): the hardware
   // range check returns zeros for any other key, so keys that no row may see
   // (past k_lengths, past the causal frontier, before the window) are never
-  // read and the loads need no branches.
+  // read and the loads need no branches.  Group A stages K, group B stages V.
   const int nvalid = geo.union_hi - geo.union_lo;
   const size_t valid_base = kv_base + (size_t)geo.union_lo * D;
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(K + valid_base), (short)0, nvalid * D * 2, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(V + valid_base), (short)0, nvalid * D * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((grp == 0 ? K : V) + valid_base), (short)0, nvalid * D * 2,
+      kBufferRsrcWord3);
+
+  u32x4_t stg[4];
+  const int vkq = gtid & 15;  // key quad within the tile (V staging)
+  const int vdc = gtid >> 4;  // 8-wide d chunk (V staging)
+  const bool v_stager = VTHREADS == kGroupThreads || gtid < VTHREADS;
 
   auto fetch = [&](int kt) {
     const int rel0 = kt * kFwdTileN - geo.union_lo;  // tile start, in valid keys
+    if (grp == 0) {
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int c = i * kFwdThreads + tid;
-      const int key = rel0 + c / (D / 8);
-      const int dch = c % (D / 8);
-      kst[i] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                       krsrc, (key * D + dch * 8) * 2, 0, 0));
-    }
-    if (VTHREADS == kFwdThreads || tid < VTHREADS) {
+      for (int i = 0; i < KLOADS; ++i) {
+        const int c = i * kGroupThreads + gtid;
+        const int key = rel0 + c / (D / 8);
+        const int dch = c % (D / 8);
+        stg[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         rsrc, (key * D + dch * 8) * 2, 0, 0));
+      }
+    } else if (v_stager) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = rel0 + vkq * 4 + i;
-        vst[i] = __builtin_bit_cast(
+        stg[i] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                         vrsrc, (key * D + vdc * 8) * 2, 0, 0));
+                         rsrc, (key * D + vdc * 8) * 2, 0, 0));
       }
     }
   };
 
   auto stash = [&](int buf) {
-    char* kb = smem + buf * L::kBuf;
-    char* vb = kb + L::kBytesK;
+    if (grp == 0) {
+      char* kb = smem + buf * L::kBytesK;
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int c = i * kFwdThreads + tid;
-      const int key = c / (D / 8);
-      const int dch = c % (D / 8);
-      *(u32x4_t*)(kb + key * L::kRowK + dch * 16) = kst[i];
-    }
-    if (VTHREADS == kFwdThreads || tid < VTHREADS) {
+      for (int i = 0; i < KLOADS; ++i) {
+        const int c = i * kGroupThreads + gtid;
+        const int key = c / (D / 8);
+        const int dch = c % (D / 8);
+        *(u32x4_t*)(kb + key * L::kRowK + dch * 16) = stg[i];
+      }
+    } else if (v_stager) {
       // 4 keys x 8 d  ->  8 rows of V^T, 4 keys (8 bytes) each
-      const int grp = vkq >> 2;
-      const int pos = grp * 16 + vt_group_pos(vkq & 3);
+      char* vb = smem + L::kOffV + buf * L::kBytesV;
+      const int grp16 = vkq >> 2;
+      const int pos = grp16 * 16 + vt_group_pos(vkq & 3);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t r0 = vst[0][m], r1 = vst[1][m], r2 = vst[2][m],
-                       r3 = vst[3][m];
+        const uint32_t r0 = stg[0][m], r1 = stg[1][m], r2 = stg[2][m],
+                       r3 = stg[3][m];
         u32x2_t even = {__builtin_amdgcn_perm(r1, r0, 0x05040100u),
                         __builtin_amdgcn_perm(r3, r2, 0x05040100u)};
         u32x2_t odd = {__builtin_amdgcn_perm(r1, r0, 0x07060302u),
@@ -231,37 +257,48 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     }
   };
 
-  if (kt_first <= kt_last) {
-    fetch(kt_first);
-    stash(0);
-    __syncthreads();
-  }
+  f32x16_t s[2];           // S^T of the current tile (two 32-key blocks)
+  uint32_t pb[2][2][4];    // P^T of the previous tile, packed bf16
 
-  int buf = 0;
-  for (int kt = kt_first; kt <= kt_last; ++kt) {
-    if (kt < kt_last) fetch(kt + 1);
-
-    const char* kb = smem + buf * L::kBuf;
-    const char* vb = kb + L::kBytesK;
-    const int j0 = kt * kFwdTileN;
-    const int cls = tile_class(geo, j0, kFwdTileN);
-
-    // ---- S^T = K Q^T for two 32-key blocks ----
-    f32x16_t s[2];
+  // M-phase: O += P(kt-1) V(kt-1), then S(kt) = K(kt) Q^T
+  auto m_phase = [&](int kt, bool do_pv, bool do_s) {
+    if (do_pv) {
+      const char* vb = smem + L::kOffV + ((kt - 1) & 1) * L::kBytesV;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      s[kb2] = f32x16_t{};
-      const char* arow = kb + (kb2 * 32 + lrow) * L::kRowK + half * 16;
+      for (int db = 0; db < DBLK; ++db) {
+        const char* arow = vb + (db * 32 + lrow) * L::kRowV + half * 16;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        bf16x8_t a = *(const bf16x8_t*)(arow + ks * 32);
-        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb2],
-                                                         0, 0, 0);
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            bf16x8_t a = *(const bf16x8_t*)(arow + (kb2 * 2 + st) * 32);
+            u32x4_t bw = {pb[kb2][st][0], pb[kb2][st][1], pb[kb2][st][2],
+                          pb[kb2][st][3]};
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a, __builtin_bit_cast(bf16x8_t, bw), oacc[db], 0, 0, 0);
+          }
       }
     }
+    if (do_s) {
+      const char* kb = smem + (kt & 1) * L::kBytesK;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        s[kb2] = f32x16_t{};
+        const char* arow = kb + (kb2 * 32 + lrow) * L::kRowK + half * 16;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          bf16x8_t a = *(const bf16x8_t*)(arow + ks * 32);
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb2],
+                                                           0, 0, 0);
+        }
+      }
+    }
+  };
 
-    // ---- mask (partial tiles only) ----
-    if (cls == kTilePartial) {
+  // V-phase: softmax of S(kt) into P(kt); stage tile kt+1 and fetch kt+2
+  auto v_phase = [&](int kt) {
+    const int j0 = kt * kFwdTileN;
+    if (tile_class(geo, j0, kFwdTileN) == kTilePartial) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -270,30 +307,24 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
           if (j < rr.lo || j >= rr.hi) s[kb2][r] = -INFINITY;
         }
     }
-
-    // ---- online softmax ----
     float mx = s[0][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = wave_max_pair(mx);
-    const float mt = mx * scale_log2;
+    const float mt = pair_max(mx) * scale_log2;
     const bool need = mt > m_run + kLazyRescale;
     if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = need ? mt : m_run;
       // need == false leaves the lane unchanged (and avoids -inf - -inf)
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+      m_run = need ? mt : m_run;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
     }
     const float mref = m_run == -INFINITY ? 0.f : m_run;
-
-    uint32_t pb[2][2][4];  // [key block][k-step][packed pair]
     float psum = 0.f;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -307,32 +338,29 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         pb[kb2][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
       }
     l_run += psum;
+    if (kt + 1 <= kt_last) stash((kt + 1) & 1);
+    if (kt + 2 <= kt_last) fetch(kt + 2);
+  };
 
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const char* arow = vb + (db * 32 + lrow) * L::kRowV + half * 16;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          bf16x8_t a = *(const bf16x8_t*)(arow + (kb2 * 2 + st) * 32);
-          u32x4_t bw = {pb[kb2][st][0], pb[kb2][st][1], pb[kb2][st][2],
-                        pb[kb2][st][3]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              a, __builtin_bit_cast(bf16x8_t, bw), oacc[db], 0, 0, 0);
-        }
-    }
-
-    if (kt < kt_last) {
-      stash(buf ^ 1);
+  if (kt_first <= kt_last) {
+    // prologue: tile kt_first in LDS, tile kt_first+1 in flight
+    fetch(kt_first);
+    stash(kt_first & 1);
+    if (kt_first + 1 <= kt_last) fetch(kt_first + 1);
+    __syncthreads();
+    if (grp == 1) __syncthreads();  // group B runs one phase behind
+    for (int kt = kt_first; kt <= kt_last; ++kt) {
+      m_phase(kt, kt > kt_first, true);
       __syncthreads();
-      buf ^= 1;
+      v_phase(kt);
+      __syncthreads();
     }
+    m_phase(kt_last + 1, true, false);
+    if (grp == 0) __syncthreads();  // matches group B's extra barrier
   }
 
   // ---- epilogue ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (qi < Sq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __bf16* op = O + q_base + (size_t)qi * D;
