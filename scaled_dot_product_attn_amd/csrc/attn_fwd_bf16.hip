@@ -195,9 +195,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // read and the loads need no branches.  Group A stages K, group B stages V.
   const int nvalid = geo.union_hi - geo.union_lo;
   const size_t valid_base = kv_base + (size_t)geo.union_lo * D;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((grp == 0 ? K : V) + valid_base), (short)0, nvalid * D * 2,
-      kBufferRsrcWord3);
+  // one resource per tensor, both uniform: selecting between them per group
+  // would make the resource divergent
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(K + valid_base), (short)0, nvalid * D * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(V + valid_base), (short)0, nvalid * D * 2, kBufferRsrcWord3);
 
   u32x4_t stg[4];
   const int vkq = gtid & 15;  // key quad within the tile (V staging)
@@ -214,7 +217,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         const int dch = c % (D / 8);
         stg[i] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                         rsrc, (key * D + dch * 8) * 2, 0, 0));
+                         krsrc, (key * D + dch * 8) * 2, 0, 0));
       }
     } else if (v_stager) {
 #pragma unroll
@@ -222,7 +225,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         const int key = rel0 + vkq * 4 + i;
         stg[i] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                         rsrc, (key * D + vdc * 8) * 2, 0, 0));
+                         vrsrc, (key * D + vdc * 8) * 2, 0, 0));
       }
     }
   };
@@ -258,7 +261,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   };
 
   f32x16_t s[2];           // S^T of the current tile (two 32-key blocks)
-  uint32_t pb[2][2][4];    // P^T of the previous tile, packed bf16
+  u32x4_t pb[2][2];        // P^T of the previous tile, packed bf16 (MFMA B operands)
 
   // M-phase: O += P(kt-1) V(kt-1), then S(kt) = K(kt) Q^T
   auto m_phase = [&](int kt, bool do_pv, bool do_s) {
@@ -272,10 +275,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             bf16x8_t a = *(const bf16x8_t*)(arow + (kb2 * 2 + st) * 32);
-            u32x4_t bw = {pb[kb2][st][0], pb[kb2][st][1], pb[kb2][st][2],
-                          pb[kb2][st][3]};
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                a, __builtin_bit_cast(bf16x8_t, bw), oacc[db], 0, 0, 0);
+                a, __builtin_bit_cast(bf16x8_t, pb[kb2][st]), oacc[db], 0, 0, 0);
           }
       }
     }
@@ -299,12 +300,17 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   auto v_phase = [&](int kt) {
     const int j0 = kt * kFwdTileN;
     if (tile_class(geo, j0, kFwdTileN) == kTilePartial) {
+      // key j0 + half*4 + c is allowed iff c lies in [t_lo, t_lo + width);
+      // c is a compile-time constant per register, so one subtract, one
+      // unsigned compare and one select per score
+      const int t_lo = rr.lo - (j0 + half * 4);
+      const unsigned width = (unsigned)max(rr.hi - rr.lo, 0);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = j0 + kb2 * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          if (j < rr.lo || j >= rr.hi) s[kb2][r] = -INFINITY;
+          const int c = kb2 * 32 + (r >> 2) * 8 + (r & 3);
+          if ((unsigned)(c - t_lo) >= width) s[kb2][r] = -INFINITY;
         }
     }
     float mx = s[0][0];
