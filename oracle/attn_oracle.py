@@ -32,7 +32,11 @@ plainly, in float64 NumPy:
   LSE = M + ln L;
 * split-KV decode: one query per head and sequence, valid KV length per
   sequence, the cache processed as ``n_splits`` slices (Tylo.jl "Primitives",
-  ``decode_attention!``).
+  ``decode_attention!``);
+* the paged KV cache of a serving engine: a (num_blocks, block_size,
+  num_kv_heads, head_size) cache addressed through per-sequence block tables
+  and ``seq_lens`` (vllm_mlx.attention, ``get_kv_cache_shape`` and
+  ``MLXAttentionMetadata``).
 
 Readings taken where the pages are silent or disagree (each is listed in the
 repository's design notes):
@@ -46,7 +50,10 @@ repository's design notes):
 * a row with no allowed key has output 0 and LSE = -inf;
 * ``k_lengths`` / ``lengths`` values are clamped to [0, Sk];
 * the decode slices hold C = ceil(ceil(len / TILE_N) / n_splits) * TILE_N keys
-  each; the slice merge weighs each slice by exp(LSE_s - max LSE).
+  each; the slice merge weighs each slice by exp(LSE_s - max LSE);
+* block tables: entry i of a sequence's row names the physical block holding
+  its tokens [i * block_size, (i + 1) * block_size); a paged length is clamped
+  to [0, max_blocks * block_size].
 
 Layouts are row-major: Q/O (B, H, Sq, D), K/V (B, Hkv, Sk, D), LSE (B, H, Sq);
 decode Q/O (B, H, D), K/V (B, Hkv, Smax, D).  This is Tylo's column-major
@@ -311,6 +318,62 @@ def decode_split_ref(Q, K, V, lengths, n_splits: int, tile_n: int = 64,
             w = np.exp(lses - Mx)
             O[b, h] = sum(wi * oi for wi, (oi, _) in zip(w, parts)) / w.sum()
             LSE[b, h] = Mx + np.log(w.sum())
+    return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# paged KV cache (serving layout)
+# ---------------------------------------------------------------------------
+
+def gather_paged(cache, table_row, n: int, g: int) -> np.ndarray:
+    """Logical rows 0..n-1 of KV head g of one sequence from a paged cache.
+
+    The cache is (num_blocks, block_size, num_kv_heads, head_size)
+    (vllm_mlx.attention, ``MLXAttentionBackend.get_kv_cache_shape``); the
+    sequence's block table (``MLXAttentionMetadata.block_tables``) lists, for
+    its i-th run of block_size tokens, the physical block holding them, so
+    token t lives in block table_row[t // block_size] at slot t % block_size.
+    Entries past the sequence's last block are never read.
+    """
+    cache = np.asarray(cache)
+    bs = cache.shape[1]
+    t = np.arange(n)
+    blocks = np.asarray(table_row, dtype=np.int64)[t // bs]
+    return np.asarray(cache[blocks, t % bs, g], dtype=np.float64)
+
+
+def decode_paged_ref(Q, K_cache, V_cache, block_tables, lengths,
+                     scale: float | None = None, batches=None):
+    """Single-query decode over a paged KV cache, in float64.
+
+    Q (B, H, D); K_cache, V_cache (num_blocks, block_size, Hkv, D);
+    block_tables (B, max_blocks) int; lengths (B,) (``seq_lens``), clamped to
+    [0, max_blocks * block_size].  Sequence b attends to its first lengths[b]
+    tokens, gathered through its block table; the result is the plain decode
+    of those rows.  Returns (O (B, H, D), LSE (B, H)).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    B, H, D = Q.shape
+    _, bs, Hkv, _ = K_cache.shape
+    tables = np.asarray(block_tables)
+    cap = tables.shape[1] * bs
+    if H % Hkv != 0:
+        raise ValueError("Heads must be a multiple of Heads_KV")
+    G = H // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    O = np.full((B, H, V_cache.shape[3]), np.nan)
+    LSE = np.full((B, H), np.nan)
+    for b in (range(B) if batches is None else batches):
+        n = min(max(int(lengths[b]), 0), cap)
+        for g in range(Hkv):
+            kb = gather_paged(K_cache, tables[b], n, g)
+            vb = gather_paged(V_cache, tables[b], n, g)
+            for h in range(g * G, (g + 1) * G):
+                s = scores(Q[b, h][None, :], kb, scale)
+                P, M, L = softmax_stats(s)
+                O[b, h] = combine(P, vb)[0] if n else 0.0
+                LSE[b, h] = lse_from_stats(M, L)[0]
     return O, LSE
 
 

@@ -473,3 +473,88 @@ def test_planted_gqa_mapping_mistake(monkeypatch):
     monkeypatch.setattr(ora, "attn_ref", mutant)
     with pytest.raises(AssertionError):
         test_bruteforce_mpmath(BRUTE_CASES[1])
+
+
+# ---------------------------------------------------------------------------
+# paged KV cache
+# ---------------------------------------------------------------------------
+
+def _scatter_to_pages(K, V, lengths, bs, rng, spare_blocks=3):
+    """Write a contiguous (B, Hkv, S, D) cache into shuffled physical blocks.
+
+    Written independently of the oracle's gather: blocks are dealt to the
+    sequences from a random permutation, unused blocks and table slots hold
+    poison (NaN rows, table entry -1 / out of range).
+    """
+    B, Hkv, S, D = K.shape
+    nblk = [-(-int(n) // bs) for n in lengths]
+    maxb = max(max(nblk), 1) + 1
+    total = sum(nblk) + spare_blocks
+    perm = rng.permutation(total)
+    Kc = np.full((total, bs, Hkv, D), np.nan)
+    Vc = np.full((total, bs, Hkv, D), np.nan)
+    table = np.full((B, maxb), -1, dtype=np.int64)
+    table[:, -1] = 10 ** 9
+    nxt = 0
+    for b in range(B):
+        for i in range(nblk[b]):
+            phys = int(perm[nxt]); nxt += 1
+            table[b, i] = phys
+            for slot in range(bs):
+                t = i * bs + slot
+                if t < lengths[b]:
+                    for g in range(Hkv):
+                        Kc[phys, slot, g] = K[b, g, t]
+                        Vc[phys, slot, g] = V[b, g, t]
+    return Kc, Vc, table
+
+
+@pytest.mark.parametrize("bs", [1, 8, 16, 32])
+def test_paged_decode_equals_contiguous(bs):
+    # vllm_mlx.attention: (num_blocks, block_size, num_kv_heads, head_size)
+    # cache + block tables must give exactly the contiguous decode.
+    rng = np.random.default_rng(30 + bs)
+    B, H, Hkv, S, D = 4, 8, 2, 70, 16
+    Q = rng.standard_normal((B, H, D))
+    K, V = rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    lengths = np.array([70, 1, 33, 0])
+    Kc, Vc, table = _scatter_to_pages(K, V, lengths, bs, rng)
+    O, L = ora.decode_ref(Q, K, V, lengths)
+    Op, Lp = ora.decode_paged_ref(Q, Kc, Vc, table, lengths)
+    np.testing.assert_array_equal(Op, O)
+    np.testing.assert_array_equal(Lp, L)
+    assert np.all(np.isfinite(Op))
+
+
+def test_paged_length_clamped_to_table_capacity():
+    rng = np.random.default_rng(41)
+    B, H, Hkv, S, D, bs = 2, 2, 1, 32, 8, 8
+    Q = rng.standard_normal((B, H, D))
+    K, V = rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    Kc = K[0].transpose(1, 0, 2).reshape(S // bs, bs, Hkv, D)
+    Vc = V[0].transpose(1, 0, 2).reshape(S // bs, bs, Hkv, D)
+    table = np.array([[0, 1, 2, 3], [0, 1, 2, 3]])
+    Op, Lp = ora.decode_paged_ref(Q, Kc, Vc, table, np.array([10 ** 6, -5]))
+    O, L = ora.decode_ref(Q[:1], K[:1], V[:1], np.array([S]))
+    np.testing.assert_array_equal(Op[:1], O)
+    assert np.all(Op[1] == 0) and np.all(np.isneginf(Lp[1]))
+
+
+def test_planted_paged_gather_mistake(monkeypatch):
+    # block and slot swapped, or the wrong KV head, must be caught.
+    def swapped(cache, table_row, n, g):
+        cache = np.asarray(cache)
+        bs = cache.shape[1]
+        t = np.arange(n)
+        return np.asarray(cache[np.asarray(table_row)[t % bs], t // bs, g], dtype=np.float64)
+
+    def head0(cache, table_row, n, g):
+        return ORIG_GATHER(cache, table_row, n, 0)
+
+    for mutant in (swapped, head0):
+        monkeypatch.setattr(ora, "gather_paged", mutant)
+        with pytest.raises((AssertionError, IndexError)):
+            test_paged_decode_equals_contiguous(16)
+
+
+ORIG_GATHER = ora.gather_paged
