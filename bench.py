@@ -10,7 +10,9 @@ algorithmic work (4*D flops per allowed (query, key) pair) divided by the
 prefill kernel's mean duration from HIP events over the timed steps; the
 decode rate in GB/s (K/V bytes of the valid keys, once per KV head, plus Q and
 O) is reported beside it.  The window/offset and clustered-image workloads are
-timed too, as extra lines of context.  ``cpu_baseline`` times the fp64 oracle
+timed too, as extra lines of context, and so is the same decode batch stored
+in a paged serving cache (block size 16, shuffled physical blocks;
+attn_decode_paged).  ``cpu_baseline`` times the fp64 oracle
 on the host on a bounded sample (whole heads) of the prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -76,8 +78,12 @@ def prefill_flops(w) -> int:
 
 def decode_bytes(w) -> int:
     B, H, D = w.q.shape
-    Hkv = w.k.shape[1]
-    lens = w.lengths.cpu().clamp(0, w.k.shape[2]).long().sum().item()
+    if hasattr(w, "k_cache"):
+        Hkv = w.k_cache.shape[2]
+        cap = w.block_tables.shape[1] * w.k_cache.shape[1]
+    else:
+        Hkv, cap = w.k.shape[1], w.k.shape[2]
+    lens = w.lengths.cpu().clamp(0, cap).long().sum().item()
     return int(lens) * Hkv * D * 2 * 2 + B * H * D * 2 * 2
 
 
@@ -149,6 +155,7 @@ def main():
     dec = wl.make("decode_split", device=dev)
     extra = {} if args.no_extra else {n: wl.make(n, device=dev)
                                      for n in ("window_offset", "image_clustered")}
+    paged = None if args.no_extra else wl.make("decode_paged", device=dev)
     B, H, Sq, D = pre.q.shape
     O = torch.empty_like(pre.q)
     LSE = torch.empty(B, H, Sq, dtype=torch.float32, device=dev)
@@ -167,7 +174,13 @@ def main():
     def run_decode():
         attn.attn_decode_ws(Od, dec.q, dec.k, dec.v, dec.lengths, dec.n_splits, ws)
 
-    names = ["prefill", "decode"] + list(extra)
+    Op = torch.empty_like(dec.q)
+
+    def run_paged():
+        attn.attn_decode_paged(Op, paged.q, paged.k_cache, paged.v_cache, paged.block_tables,
+                               paged.lengths, paged.n_splits, workspace=ws)
+
+    names = ["prefill", "decode"] + list(extra) + (["decode_paged"] if paged is not None else [])
     ev = {n: [] for n in names}
 
     def step(record):
@@ -180,6 +193,8 @@ def main():
                 run_prefill(pre, O, LSE)
             elif n == "decode":
                 run_decode()
+            elif n == "decode_paged":
+                run_paged()
             else:
                 run_prefill(extra[n], *ext_out[n])
             if record:
@@ -245,6 +260,15 @@ def main():
             tf = f / (ms[n] * 1e-3) / 1e12
             out["extra"][n] = {"ms": round(ms[n], 4), "TFLOP/s": round(tf, 2),
                                "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": f}
+    if paged is not None:
+        pb = decode_bytes(paged)
+        gbs = pb / (ms["decode_paged"] * 1e-3) / 1e9
+        out["decode_paged"] = {
+            "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms["decode_paged"], 4),
+            "config": "same sequences as decode, cache (num_blocks, 16, 8, 128) with "
+                      "shuffled physical blocks",
+            "roofline": roof("hbm", gbs, PEAK_HBM_GBS, "GB/s", None),
+        }
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)

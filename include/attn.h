@@ -134,6 +134,38 @@ int attn_decode_ws(void* O, const void* Q, const void* K, const void* V,
                    int Smax, int D, void* workspace, size_t ws_bytes,
                    hipStream_t stream);
 
+/* Split-KV decode over a paged KV cache, bf16 Q/K/V/O.
+ *   O, Q          (B, H, D) bf16, as attn_decode
+ *   K_cache,
+ *   V_cache       in (num_blocks, block_size, Hkv, D) bf16: token slot
+ *                 `slot` of physical block `blk` holds the K (V) rows of all
+ *                 KV heads of one token
+ *   block_tables  device int32 (B, max_blocks): entry i of row b names the
+ *                 physical block holding tokens [i*block_size, (i+1)*block_size)
+ *                 of sequence b; entries past the sequence's last block are
+ *                 never read; entries outside [0, num_blocks) are clamped into
+ *                 range (no fault, meaningless result)
+ *   lengths       device int32 (B,): tokens of each sequence (seq_lens),
+ *                 clamped to [0, max_blocks * block_size]; zero gives O = 0
+ *   n_splits      >= 1, the same key slicing and merge as attn_decode
+ *   block_size    a power of two, 1..1024 (8, 16 and 32 are the serving sizes)
+ *   D             64 or 128
+ *   workspace     NULL: the library allocates its partial-result scratch
+ *                 stream-ordered (hipMallocAsync / hipFreeAsync on `stream`);
+ *                 else a caller buffer of ws_bytes >=
+ *                 attn_decode_workspace_bytes(B, H, n_splits, D), 256-byte
+ *                 aligned, not shared by concurrent calls.
+ * Defined by: vllm_mlx.attention, MLXAttentionBackend.get_kv_cache_shape
+ * (cache layout), supports_block_size (8/16/32), MLXAttentionMetadata
+ * (seq_lens, block_tables); Tylo.jl "Primitives", decode_attention! (the
+ * split-KV decode itself). */
+int attn_decode_paged(void* O, const void* Q, const void* K_cache,
+                      const void* V_cache, const int32_t* block_tables,
+                      const int32_t* lengths, int n_splits, int B, int H,
+                      int Hkv, int num_blocks, int block_size, int max_blocks,
+                      int D, void* workspace, size_t ws_bytes,
+                      hipStream_t stream);
+
 /* Debug export: evaluates the kernels' own mask predicate into M (device,
  * uint8 (Sq, Sk), 1 = attend, 0 = blocked) for one batch with valid key
  * length k_len (clamped to [0, Sk]).  Tylo.jl "Primitives", hmask: host and

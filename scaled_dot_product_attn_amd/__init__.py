@@ -35,6 +35,8 @@ _SIGS = {
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "attn_decode_ws": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
+                               ctypes.c_size_t, _P]),
     "attn_mask_dump": (_I, [_P, _I, _I, _I, _I, _I, _I, _P]),
     "attn_tile_plan": (_I, [_P, _I, _I, _I, _I, _I, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
@@ -151,6 +153,34 @@ def attn_decode_ws(O, Q, K, V, lengths, n_splits, workspace, stream=None) -> Non
                               int(n_splits), B, H, Hkv, Smax, D, ws, nbytes,
                               _stream(stream))
     _check(rc, "attn_decode_ws")
+
+
+def attn_decode_paged(O, Q, K_cache, V_cache, block_tables, lengths, n_splits=8,
+                      workspace=None, stream=None) -> None:
+    """Split-KV decode over a paged (num_blocks, block_size, Hkv, D) cache.
+
+    ``block_tables`` int32 (B, max_blocks), ``lengths`` int32 (B,); with
+    ``workspace=None`` the library allocates its scratch stream-ordered.
+    """
+    B, H, D = Q.shape
+    num_blocks, block_size, Hkv, Dk = K_cache.shape
+    if Dk != D or tuple(V_cache.shape) != tuple(K_cache.shape):
+        raise ValueError("K_cache / V_cache must be (num_blocks, block_size, Hkv, D)")
+    for t in (O, Q, K_cache, V_cache):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("decode takes bfloat16 tensors")
+    for t in (block_tables, lengths):
+        if t.dtype != torch.int32:
+            raise ValueError("block_tables and lengths must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be (B, max_blocks)")
+    ws = _ptr(workspace) if workspace is not None else None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().attn_decode_paged(_ptr(O), _ptr(Q), _ptr(K_cache), _ptr(V_cache),
+                                 _ptr(block_tables), _ptr(lengths), int(n_splits), B, H,
+                                 Hkv, num_blocks, block_size, block_tables.shape[1], D,
+                                 ws, nbytes, _stream(stream))
+    _check(rc, "attn_decode_paged")
 
 
 def attn_mask_dump(M, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,

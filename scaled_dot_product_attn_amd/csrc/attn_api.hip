@@ -26,6 +26,9 @@ hipError_t launch_decode(void*, const void*, const void*, const void*,
                          const int32_t*, int, int, int, int, int, int, void*,
                          hipStream_t);
 size_t decode_workspace_bytes(int B, int H, int n_splits, int D);
+hipError_t launch_decode_paged(void*, const void*, const void*, const void*,
+                               const int32_t*, const int32_t*, int, int, int,
+                               int, int, int, int, int, void*, hipStream_t);
 
 __global__ void mask_dump_kernel(uint8_t* __restrict__ M, int Sq, int Sk,
                                  int causal, int window, int input_pos,
@@ -90,6 +93,29 @@ static int check_decode(const void* O, const void* Q, const void* K,
   if ((long long)B * H * n_splits > INT_MAX / 2) return ATTN_EUNSUPPORTED;
   if ((long long)B * Hkv * H * n_splits > INT_MAX) return ATTN_EUNSUPPORTED;
   if (!O || !Q || !K || !V || !lengths) return ATTN_EINVAL;
+  return ATTN_OK;
+}
+
+// Checks of the paged decode; on success *bs_log2 = log2(block_size).
+static int check_decode_paged(const void* O, const void* Q, const void* Kc,
+                              const void* Vc, const int32_t* tables,
+                              const int32_t* lengths, int n_splits, int B,
+                              int H, int Hkv, int num_blocks, int block_size,
+                              int max_blocks, int D, int* bs_log2) {
+  if (B < 1 || H < 1 || Hkv < 1 || num_blocks < 1 || max_blocks < 1 ||
+      n_splits < 1 || block_size < 1)
+    return ATTN_EINVAL;
+  if (block_size & (block_size - 1)) return ATTN_EINVAL;  // power of two
+  if (H % Hkv != 0) return ATTN_EINVAL;
+  if (D != 64 && D != 128) return ATTN_EUNSUPPORTED;
+  if (block_size > 1024) return ATTN_EUNSUPPORTED;
+  if ((long long)max_blocks * block_size > INT_MAX - 256) return ATTN_EUNSUPPORTED;
+  if ((long long)B * H * n_splits > INT_MAX / 2) return ATTN_EUNSUPPORTED;
+  if ((long long)B * Hkv * H * n_splits > INT_MAX) return ATTN_EUNSUPPORTED;
+  if (!O || !Q || !Kc || !Vc || !tables || !lengths) return ATTN_EINVAL;
+  int lg = 0;
+  while ((1 << lg) < block_size) ++lg;
+  *bs_log2 = lg;
   return ATTN_OK;
 }
 
@@ -164,6 +190,41 @@ int attn_decode(void* O, const void* Q, const void* K, const void* V,
   rc = hip_status(launch_decode(O, Q, K, V, lengths, n_splits, B, H, Hkv, Smax,
                                 D, ws, stream));
   if (ws && hipFreeAsync(ws, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    rc = ATTN_EHIP;
+  }
+  return rc;
+}
+
+int attn_decode_paged(void* O, const void* Q, const void* K_cache,
+                      const void* V_cache, const int32_t* block_tables,
+                      const int32_t* lengths, int n_splits, int B, int H,
+                      int Hkv, int num_blocks, int block_size, int max_blocks,
+                      int D, void* workspace, size_t ws_bytes,
+                      hipStream_t stream) {
+  int bs_log2 = 0;
+  int rc = check_decode_paged(O, Q, K_cache, V_cache, block_tables, lengths,
+                              n_splits, B, H, Hkv, num_blocks, block_size,
+                              max_blocks, D, &bs_log2);
+  if (rc != ATTN_OK) return rc;
+  void* ws = workspace;
+  bool owned = false;
+  if (n_splits > 1) {
+    const size_t need = decode_workspace_bytes(B, H, n_splits, D);
+    if (ws) {
+      if (((uintptr_t)ws & 255) != 0 || ws_bytes < need) return ATTN_EINVAL;
+    } else {
+      if (hipMallocAsync(&ws, need, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return ATTN_EHIP;
+      }
+      owned = true;
+    }
+  }
+  rc = hip_status(launch_decode_paged(O, Q, K_cache, V_cache, block_tables,
+                                      lengths, n_splits, B, H, Hkv, num_blocks,
+                                      bs_log2, max_blocks, D, ws, stream));
+  if (owned && hipFreeAsync(ws, stream) != hipSuccess) {
     (void)hipGetLastError();
     rc = ATTN_EHIP;
   }

@@ -84,6 +84,89 @@ __device__ inline void split_range(int len, int n_splits, int s, int* k_begin,
   *k_end = (int)(hi < len ? hi : len);
 }
 
+// b = the sequence whose length ranks `rank`-th (longest first, ties by
+// index), so long slices start early; identity when B is too large to rank.
+__device__ inline int batch_of_rank(const int32_t* __restrict__ lengths, int B,
+                                    int rank, int tid, int& s_b) {
+  if (B > kDecSortMaxB) return rank;
+  if (tid < B) {
+    const int my = lengths[tid];
+    int r = 0;
+    for (int j = 0; j < B; ++j) {
+      const int lj = lengths[j];
+      r += (lj > my) || (lj == my && j < tid);
+    }
+    if (r == rank) s_b = tid;
+  }
+  __syncthreads();
+  return s_b;
+}
+
+// Merge the key slots of the workgroup (per-slot running max m, sum l and
+// unnormalised accumulators) and write the slice's result: the bf16 output
+// when there is a single slice, else the normalised partial output and its
+// base-2 LSE.
+template <int D, int GM>
+__device__ inline void slice_epilogue(
+    float (&m)[GM], float (&l)[GM], float (&acc)[GM][8], float (&s_m)[4][GM],
+    float (&s_acc)[4][GM][D], float (&s_l)[4][GM], int tid, int b, int H,
+    int h0, int nh, int s, int n_splits, float* __restrict__ Opart,
+    float* __restrict__ Lpart, __bf16* __restrict__ O) {
+  constexpr int LPK = D / 8;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = tid % LPK;
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh) {
+    float mw = m[hh];
+#pragma unroll
+    for (int x = LPK; x < 64; x <<= 1) mw = fmaxf(mw, __shfl_xor(mw, x));
+    if (lane == 0) s_m[wave][hh] = mw;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh) {
+    const float M = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]),
+                          fmaxf(s_m[2][hh], s_m[3][hh]));
+    const float f = m[hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hh] - M);
+    float lw = l[hh] * f;
+#pragma unroll
+    for (int x = LPK; x < 64; x <<= 1) lw += __shfl_xor(lw, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = acc[hh][e] * f;
+#pragma unroll
+      for (int x = LPK; x < 64; x <<= 1) a += __shfl_xor(a, x);
+      acc[hh][e] = a;
+    }
+    if (lane < LPK) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_acc[wave][hh][li * 8 + e] = acc[hh][e];
+      if (li == 0) s_l[wave][hh] = lw;
+    }
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < GM * D; idx += kDecThreads) {
+    const int hh = idx / D, d = idx % D;
+    if (hh >= nh) continue;
+    const float M = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]),
+                          fmaxf(s_m[2][hh], s_m[3][hh]));
+    const float lt = s_l[0][hh] + s_l[1][hh] + s_l[2][hh] + s_l[3][hh];
+    const float at = s_acc[0][hh][d] + s_acc[1][hh][d] + s_acc[2][hh][d] +
+                     s_acc[3][hh][d];
+    const float o = lt > 0.f ? at / lt : 0.f;
+    const size_t bh = (size_t)b * H + h0 + hh;
+    if (n_splits == 1) {
+      ((uint16_t*)O)[bh * D + d] = f32_to_bf16_rne(o);
+    } else {
+      Opart[(bh * n_splits + s) * D + d] = o;
+      if (d == 0) Lpart[bh * n_splits + s] = lt > 0.f ? M + __builtin_log2f(lt) : -INFINITY;
+    }
+  }
+}
+
+
 template <int D, int GM>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void attn_decode_split_kernel(
@@ -116,22 +199,7 @@ void attn_decode_split_kernel(
   const int g = t % Hkv;
   const int rank = t / Hkv;
 
-  int b = rank;
-  if (B <= kDecSortMaxB) {
-    // b = the sequence whose length ranks `rank`-th (longest first, ties by
-    // index), so long slices start early.
-    if (tid < B) {
-      const int my = lengths[tid];
-      int r = 0;
-      for (int j = 0; j < B; ++j) {
-        const int lj = lengths[j];
-        r += (lj > my) || (lj == my && j < tid);
-      }
-      if (r == rank) s_b = tid;
-    }
-    __syncthreads();
-    b = s_b;
-  }
+  const int b = batch_of_rank(lengths, B, rank, tid, s_b);
 
   const int len = min(max(lengths[b], 0), Smax);
   int k_begin, k_end;
@@ -244,55 +312,167 @@ void attn_decode_split_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- merge the key slots of the workgroup ----
-#pragma unroll
-  for (int hh = 0; hh < GM; ++hh) {
-    float mw = m[hh];
-#pragma unroll
-    for (int x = LPK; x < 64; x <<= 1) mw = fmaxf(mw, __shfl_xor(mw, x));
-    if (lane == 0) s_m[wave][hh] = mw;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int hh = 0; hh < GM; ++hh) {
-    const float M = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]),
-                          fmaxf(s_m[2][hh], s_m[3][hh]));
-    const float f = m[hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hh] - M);
-    float lw = l[hh] * f;
-#pragma unroll
-    for (int x = LPK; x < 64; x <<= 1) lw += __shfl_xor(lw, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float a = acc[hh][e] * f;
-#pragma unroll
-      for (int x = LPK; x < 64; x <<= 1) a += __shfl_xor(a, x);
-      acc[hh][e] = a;
-    }
-    if (lane < LPK) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave][hh][li * 8 + e] = acc[hh][e];
-      if (li == 0) s_l[wave][hh] = lw;
-    }
-  }
-  __syncthreads();
+  slice_epilogue<D, GM>(m, l, acc, s_m, s_acc, s_l, tid, b, H, h0, nh, s,
+                        n_splits, Opart, Lpart, O);
+}
 
-  for (int idx = tid; idx < GM * D; idx += kDecThreads) {
-    const int hh = idx / D, d = idx % D;
-    if (hh >= nh) continue;
-    const float M = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]),
-                          fmaxf(s_m[2][hh], s_m[3][hh]));
-    const float lt = s_l[0][hh] + s_l[1][hh] + s_l[2][hh] + s_l[3][hh];
-    const float at = s_acc[0][hh][d] + s_acc[1][hh][d] + s_acc[2][hh][d] +
-                     s_acc[3][hh][d];
-    const float o = lt > 0.f ? at / lt : 0.f;
-    const size_t bh = (size_t)b * H + h0 + hh;
-    if (n_splits == 1) {
-      ((uint16_t*)O)[bh * D + d] = f32_to_bf16_rne(o);
-    } else {
-      Opart[(bh * n_splits + s) * D + d] = o;
-      if (d == 0) Lpart[bh * n_splits + s] = lt > 0.f ? M + __builtin_log2f(lt) : -INFINITY;
-    }
+// Split-KV decode over a paged KV cache (vllm_mlx.attention: a
+// (num_blocks, block_size, num_kv_heads, head_size) cache, per-sequence block
+// tables and seq_lens).  Same work decomposition, key slicing, ring of loads
+// and merge as the contiguous kernel; only the addressing differs: token t of
+// sequence b sits in physical block tables[b][t / block_size] at slot
+// t % block_size, and one key row of one KV head is D contiguous bf16 inside
+// a token's (Hkv, D) row.  Block-table entries are fetched one round ahead of
+// the K/V loads that need them, so the gather adds no dependent latency to the
+// ring.  Keys past the slice read block 0 (always in bounds) and are masked:
+// their score is -inf and their V chunk is replaced by zeros, so neither
+// padding nor stale cache contents can reach the result.  Table entries are
+// clamped to [0, num_blocks) so a corrupt table cannot address outside the
+// cache.
+template <int D, int GM>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void attn_decode_paged_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
+    const __bf16* __restrict__ Vc, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ lengths, float* __restrict__ Opart,
+    float* __restrict__ Lpart, __bf16* __restrict__ O, int B, int H, int Hkv,
+    int num_blocks, int bs_log2, int max_blocks, int n_splits, int n_hchunks,
+    float scale_log2) {
+  constexpr int LPK = D / 8;
+  constexpr int KPP = kDecThreads / LPK;
+  constexpr int NS = kDecStages;
+
+  __shared__ int s_b;
+  __shared__ float s_m[4][GM];
+  __shared__ float s_acc[4][GM][D];
+  __shared__ float s_l[4][GM];
+
+  const int tid = threadIdx.x;
+  const int li = tid % LPK;
+  const int gi = tid / LPK;
+
+  const int lid = blockIdx.x;
+  const int s = lid % n_splits;
+  int t = lid / n_splits;
+  const int hc = t % n_hchunks;
+  t /= n_hchunks;
+  const int g = t % Hkv;
+  const int rank = t / Hkv;
+  const int b = batch_of_rank(lengths, B, rank, tid, s_b);
+
+  const int cap = max_blocks << bs_log2;
+  const int len = min(max(lengths[b], 0), cap);
+  int k_begin, k_end;
+  split_range(len, n_splits, s, &k_begin, &k_end);
+
+  const int G = H / Hkv;
+  const int h0 = g * G + hc * GM;
+  const int nh = min(GM, G - hc * GM);
+
+  uint32_t q[GM][4];
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh) {
+    const int hq = h0 + (hh < nh ? hh : 0);
+    const u32x4_t a = *(const u32x4_t*)(Q + ((size_t)b * H + hq) * D + li * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) q[hh][w] = a[w];
   }
+
+  float m[GM], l[GM], acc[GM][8];
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+  }
+
+  const int32_t* trow = tables + (size_t)b * max_blocks;
+  const size_t token_row = (size_t)Hkv * D;     // elements per cache token
+  const size_t head_off = (size_t)g * D + li * 8;
+  const int slot_mask = (1 << bs_log2) - 1;
+  const int nkeys = k_end - k_begin;
+  const int npass = (nkeys + KPP - 1) / KPP;
+  const int nround = (npass + NS - 1) / NS;
+  auto key_of = [&](int rd, int st) { return k_begin + (rd * NS + st) * KPP + gi; };
+  auto table_entry = [&](int key) { return trow[key < k_end ? key >> bs_log2 : 0]; };
+  auto element = [&](int key, int entry) {
+    const bool ok = key < k_end;
+    const int phys = ok ? min(max(entry, 0), num_blocks - 1) : 0;
+    const int slot = ok ? (key & slot_mask) : 0;
+    return (((size_t)phys << bs_log2) | (size_t)slot) * token_row + head_off;
+  };
+
+  // tcur: table entries of the keys loaded in this round (round rd + 1);
+  // tnext: those of round rd + 2, requested at the top of the round.
+  int tcur[NS], tnext[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) tcur[st] = table_entry(key_of(0, st));
+  u32x4_t kr[NS], vr[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) kr[st] = vr[st] = u32x4_t{0, 0, 0, 0};
+
+  for (int rd = -1; rd < nround; ++rd) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) tnext[st] = table_entry(key_of(rd + 2, st));
+    float tsc[NS][GM];
+    bool valid[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      valid[st] = rd >= 0 && (rd * NS + st) * KPP + gi < nkeys;
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) a = dot2_bf16(q[hh][w], kr[st][w], a);
+        a = group_sum<LPK>(a);
+        tsc[st][hh] = valid[st] ? a * scale_log2 : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      kr[st] = *(const u32x4_t*)(Kc + element(key_of(rd + 1, st), tcur[st]));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) {
+      float mx = tsc[0][hh];
+#pragma unroll
+      for (int st = 1; st < NS; ++st) mx = fmaxf(mx, tsc[st][hh]);
+      const bool need = mx > m[hh] + kDecLazy;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m[hh] - mx) : 1.f;
+      m[hh] = need ? mx : m[hh];
+      l[hh] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      float vf[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = valid[st] ? vr[st][w] : 0u;
+        vf[2 * w] = bf16_lo(x);
+        vf[2 * w + 1] = bf16_hi(x);
+      }
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh) {
+        const float mref = m[hh] == -INFINITY ? 0.f : m[hh];
+        const float pr = __builtin_amdgcn_exp2f(tsc[st][hh] - mref);
+        l[hh] += pr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(pr, vf[e], acc[hh][e]);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      vr[st] = *(const u32x4_t*)(Vc + element(key_of(rd + 1, st), tcur[st]));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) tcur[st] = tnext[st];
+  }
+
+  slice_epilogue<D, GM>(m, l, acc, s_m, s_acc, s_l, tid, b, H, h0, nh, s,
+                        n_splits, Opart, Lpart, O);
 }
 
 // One wave per (sequence, head): O = sum_s w_s O_s / sum_s w_s with
@@ -387,6 +567,68 @@ hipError_t launch_decode(void* O, const void* Q, const void* K, const void* V,
   if (D == 64)
     return launch_decode_d<64>(O, Q, K, V, lengths, n_splits, B, H, Hkv, Smax, ws, stream);
   return launch_decode_d<128>(O, Q, K, V, lengths, n_splits, B, H, Hkv, Smax, ws, stream);
+}
+
+template <int D, int GM>
+static hipError_t launch_paged_split(const void* Q, const void* Kc,
+                                     const void* Vc, const int32_t* tables,
+                                     const int32_t* lengths, float* Opart,
+                                     float* Lpart, void* O, int B, int H,
+                                     int Hkv, int num_blocks, int bs_log2,
+                                     int max_blocks, int n_splits,
+                                     hipStream_t stream) {
+  const int G = H / Hkv;
+  const int n_hchunks = (G + GM - 1) / GM;
+  const long long grid = (long long)B * Hkv * n_hchunks * n_splits;
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  hipLaunchKernelGGL((attn_decode_paged_kernel<D, GM>), dim3((unsigned)grid),
+                     dim3(kDecThreads), 0, stream, (const __bf16*)Q,
+                     (const __bf16*)Kc, (const __bf16*)Vc, tables, lengths,
+                     Opart, Lpart, (__bf16*)O, B, H, Hkv, num_blocks, bs_log2,
+                     max_blocks, n_splits, n_hchunks, scale_log2);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_paged_d(void* O, const void* Q, const void* Kc,
+                                 const void* Vc, const int32_t* tables,
+                                 const int32_t* lengths, int n_splits, int B,
+                                 int H, int Hkv, int num_blocks, int bs_log2,
+                                 int max_blocks, void* ws, hipStream_t stream) {
+  const size_t bhs = (size_t)B * H * n_splits;
+  float* Opart = (float*)ws;
+  float* Lpart =
+      (float*)((char*)ws + (bhs * D * sizeof(float) + 255) / 256 * 256);
+  const int G = H / Hkv;
+  hipError_t e;
+#define ATTN_PAGED(GM)                                                        \
+  launch_paged_split<D, GM>(Q, Kc, Vc, tables, lengths, Opart, Lpart, O, B,   \
+                            H, Hkv, num_blocks, bs_log2, max_blocks, n_splits, \
+                            stream)
+  if (G <= 1) e = ATTN_PAGED(1);
+  else if (G <= 2) e = ATTN_PAGED(2);
+  else if (G <= 4) e = ATTN_PAGED(4);
+  else e = ATTN_PAGED(8);
+#undef ATTN_PAGED
+  if (e != hipSuccess || n_splits == 1) return e;
+  const int BH = B * H;
+  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3((BH + 3) / 4), dim3(256),
+                     0, stream, (const float*)Opart, (const float*)Lpart,
+                     (__bf16*)O, BH, n_splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_paged(void* O, const void* Q, const void* Kc,
+                               const void* Vc, const int32_t* tables,
+                               const int32_t* lengths, int n_splits, int B,
+                               int H, int Hkv, int num_blocks, int bs_log2,
+                               int max_blocks, int D, void* ws,
+                               hipStream_t stream) {
+  if (D == 64)
+    return launch_paged_d<64>(O, Q, Kc, Vc, tables, lengths, n_splits, B, H,
+                              Hkv, num_blocks, bs_log2, max_blocks, ws, stream);
+  return launch_paged_d<128>(O, Q, Kc, Vc, tables, lengths, n_splits, B, H,
+                             Hkv, num_blocks, bs_log2, max_blocks, ws, stream);
 }
 
 }  // namespace attn

@@ -21,6 +21,10 @@ Workloads (the shapes of the pages' use cases; no dataset is involved):
 * ``decode_split``    B=64 sequences, H=32, Hkv=8, one query per head, D=128,
                       lengths uniform in [512, 32768], cache padded to 32768,
                       n_splits=8, TILE_N=64.
+* ``decode_paged``    the same sequences (same seed, same draws) stored in a
+                      paged serving cache: (num_blocks, block_size=16, Hkv=8,
+                      D=128) with the physical blocks of all sequences dealt
+                      from a seeded random permutation, plus spare blocks.
 """
 
 from __future__ import annotations
@@ -124,6 +128,56 @@ def decode_random(B=64, H=32, Hkv=8, D=128, smin=512, smax=32768, n_splits=8,
                   dict(B=B, H=H, Hkv=Hkv, Smax=smax, D=D, seed=seed))
 
 
+@dataclass
+class PagedDecode:
+    name: str
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_tables: torch.Tensor
+    lengths: torch.Tensor
+    n_splits: int = 8
+    meta: dict = field(default_factory=dict)
+
+
+def decode_paged(B=64, H=32, Hkv=8, D=128, smin=512, smax=32768, block_size=16,
+                 n_splits=8, seed=5, dtype=torch.bfloat16, device="cpu",
+                 pad_value=0.0, spare_blocks=64, name="decode_paged") -> PagedDecode:
+    """The draws of ``decode_random`` (same seed, same order) in a paged cache.
+
+    Cache (num_blocks, block_size, Hkv, D), num_blocks = sum of ceil(len /
+    block_size) + spare_blocks.  Physical blocks are dealt to the sequences'
+    logical blocks in order from a random permutation drawn on a second
+    generator, so K/V values equal ``decode_random``'s.  Unused token slots and
+    spare blocks hold ``pad_value``; unused table entries are -1.
+    """
+    gen = torch.Generator().manual_seed(seed)
+    perm_gen = torch.Generator().manual_seed(seed * 7919 + 1)
+    lengths = torch.randint(smin, smax + 1, (B,), generator=gen, dtype=torch.int64)
+    q = _randn(gen, (B, H, D), dtype)
+    nblk = [(int(n) + block_size - 1) // block_size for n in lengths]
+    num_blocks = sum(nblk) + spare_blocks
+    perm = torch.randperm(num_blocks, generator=perm_gen)
+    max_blocks = max((smax + block_size - 1) // block_size, 1)
+    tables = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    kc = torch.full((num_blocks, block_size, Hkv, D), pad_value, dtype=dtype, device=device)
+    vc = torch.full((num_blocks, block_size, Hkv, D), pad_value, dtype=dtype, device=device)
+    pos = 0
+    for b in range(B):
+        n, nb = int(lengths[b]), nblk[b]
+        phys = perm[pos:pos + nb]
+        pos += nb
+        tables[b, :nb] = phys.to(torch.int32)
+        for cache in (kc, vc):
+            x = torch.full((Hkv, nb * block_size, D), pad_value, dtype=dtype)
+            x[:, :n] = _randn(gen, (Hkv, n, D), dtype)
+            cache[phys.to(device)] = x.view(Hkv, nb, block_size, D).permute(1, 2, 0, 3).to(device)
+    return PagedDecode(name, q.to(device), kc, vc, tables.to(device),
+                       lengths.to(torch.int32).to(device), n_splits,
+                       dict(B=B, H=H, Hkv=Hkv, D=D, block_size=block_size,
+                            num_blocks=num_blocks, max_blocks=max_blocks, seed=seed))
+
+
 def make(name: str, device="cpu"):
     """The five named workloads at their full sizes."""
     if name == "tiny_f32":
@@ -140,7 +194,10 @@ def make(name: str, device="cpu"):
         return image_clustered(device=device)
     if name == "decode_split":
         return decode_random(device=device)
+    if name == "decode_paged":
+        return decode_paged(device=device)
     raise KeyError(name)
 
 
-NAMES = ("tiny_f32", "gqa_causal", "window_offset", "image_clustered", "decode_split")
+NAMES = ("tiny_f32", "gqa_causal", "window_offset", "image_clustered", "decode_split",
+         "decode_paged")

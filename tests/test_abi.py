@@ -37,7 +37,8 @@ def _declared():
 def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("attn_fwd", "attn_fwd_f32", "attn_decode", "attn_decode_ws",
-              "attn_decode_workspace_bytes", "attn_mask_dump", "attn_tile_plan",
+              "attn_decode_workspace_bytes", "attn_decode_paged", "attn_mask_dump",
+              "attn_tile_plan",
               "attn_status_string", "attn_version"):
         assert n in names
 
@@ -100,6 +101,27 @@ def test_decode_argument_errors(lib):
                               None) == attn.ATTN_EINVAL
     assert lib.attn_decode_workspace_bytes(0, 8, 8, 128) == 0
     assert lib.attn_decode_workspace_bytes(2, 8, 8, 96) == 0
+
+
+def test_decode_paged_argument_errors(lib):
+    def dec(O=1, Q=1, K=1, V=1, T=1, L=1, ns=8, B=2, H=8, Hkv=2, nb=16, bs=16, mb=4,
+            D=128, ws=256, nbytes=1 << 20):
+        return lib.attn_decode_paged(O, Q, K, V, T, L, ns, B, H, Hkv, nb, bs, mb, D, ws,
+                                     nbytes, None)
+    assert dec(ns=0) == attn.ATTN_EINVAL
+    assert dec(H=6, Hkv=4) == attn.ATTN_EINVAL
+    assert dec(nb=0) == attn.ATTN_EINVAL
+    assert dec(mb=0) == attn.ATTN_EINVAL
+    assert dec(bs=0) == attn.ATTN_EINVAL
+    assert dec(bs=12) == attn.ATTN_EINVAL          # not a power of two
+    assert dec(bs=2048) == attn.ATTN_EUNSUPPORTED
+    assert dec(mb=2 ** 30, bs=16) == attn.ATTN_EUNSUPPORTED
+    assert dec(T=None) == attn.ATTN_EINVAL
+    assert dec(L=None) == attn.ATTN_EINVAL
+    assert dec(D=96) == attn.ATTN_EUNSUPPORTED
+    need = lib.attn_decode_workspace_bytes(2, 8, 8, 128)
+    assert dec(nbytes=need - 1) == attn.ATTN_EINVAL
+    assert dec(ws=260, nbytes=need) == attn.ATTN_EINVAL
 
 
 def test_debug_export_argument_errors(lib):

@@ -343,3 +343,121 @@ def test_decode_full_size_workload_sampled():
                     lengths[picks], w.n_splits)
     err = _check_decode(sub, O[picks])
     _say(f"  decode_split: sampled max-abs error {err:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# paged-KV decode
+# ---------------------------------------------------------------------------
+
+def _to_dev_paged(w):
+    for f in ("q", "k_cache", "v_cache", "block_tables", "lengths"):
+        setattr(w, f, getattr(w, f).to(DEV))
+    return w
+
+
+def _check_paged(w, O, tol=TOL_BF16):
+    Or, _ = ora.decode_paged_ref(_np(w.q), _np(w.k_cache), _np(w.v_cache),
+                                 w.block_tables.cpu().numpy(), w.lengths.cpu().numpy())
+    err = np.max(np.abs(_np(O) - Or))
+    assert err <= tol, f"paged decode max-abs error {err}"
+    return err
+
+
+PAGED_CASES = [
+    # B, H, Hkv, D, smin, smax, block_size, n_splits
+    (4, 8, 2, 128, 1, 300, 16, 8),
+    (3, 4, 4, 128, 60, 70, 8, 3),
+    (5, 16, 2, 128, 100, 2000, 32, 1),
+    (2, 8, 1, 64, 1, 500, 8, 4),
+    (6, 32, 8, 128, 512, 4096, 16, 8),
+    (2, 4, 4, 64, 64, 64, 1, 64),
+    (3, 8, 2, 128, 1, 1000, 64, 8),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_decode_paged_parity(case):
+    B, H, Hkv, D, smin, smax, bs, ns = case
+    _say(f"paged decode {case}")
+    w = _to_dev_paged(wl.decode_paged(B, H, Hkv, D, smin, smax, bs, ns, seed=31,
+                                      spare_blocks=5))
+    O = torch.empty_like(w.q)
+    attn.attn_decode_paged(O, w.q, w.k_cache, w.v_cache, w.block_tables, w.lengths, ns)
+    torch.cuda.synchronize()
+    _check_paged(w, O)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_decode_paged_equals_contiguous_bitwise(bs):
+    # Same draws in both layouts: the two kernels do the same arithmetic in the
+    # same order, so the outputs must be identical.
+    B, H, Hkv, D, smin, smax, ns = 6, 16, 4, 128, 1, 3000, 8
+    c = wl.decode_random(B, H, Hkv, D, smin, smax, ns, seed=32)
+    p = _to_dev_paged(wl.decode_paged(B, H, Hkv, D, smin, smax, bs, ns, seed=32))
+    Oc = attn.decode(c.q.to(DEV), c.k.to(DEV), c.v.to(DEV), c.lengths.to(DEV), ns)
+    Op = torch.empty_like(p.q)
+    attn.attn_decode_paged(Op, p.q, p.k_cache, p.v_cache, p.block_tables, p.lengths, ns)
+    torch.cuda.synchronize()
+    assert torch.equal(Op, Oc)
+
+
+def test_decode_paged_poison_and_edge_lengths():
+    B, H, Hkv, D, bs = 6, 8, 2, 128, 16
+    # every sequence holds 250 tokens: the last of its 16 blocks has 6 NaN slots
+    w = wl.decode_paged(B, H, Hkv, D, 250, 250, bs, 8, seed=33, pad_value=float("nan"),
+                        spare_blocks=4)
+    # block 0 becomes a NaN spare that padded keys point at; shift every table entry
+    nan_block = torch.full((1,) + tuple(w.k_cache.shape[1:]), float("nan"), dtype=torch.bfloat16)
+    w.k_cache = torch.cat([nan_block, w.k_cache])
+    w.v_cache = torch.cat([nan_block, w.v_cache])
+    w.block_tables = torch.where(w.block_tables >= 0, w.block_tables + 1, w.block_tables)
+    _to_dev_paged(w)
+    written = w.lengths.clone()
+    for lens in ([0, 1, 15, 16, 17, 250], [250, 0, 0, 33, 200, 1]):
+        # keep each length within the tokens the workload wrote for it
+        w.lengths = torch.minimum(torch.tensor(lens, dtype=torch.int32, device=DEV), written)
+        for ns in (1, 2, 8, 64):
+            O = torch.empty_like(w.q)
+            attn.attn_decode_paged(O, w.q, w.k_cache, w.v_cache, w.block_tables, w.lengths, ns)
+            torch.cuda.synchronize()
+            assert torch.isfinite(O.float()).all()
+            for b, n in enumerate(w.lengths.tolist()):
+                if n == 0:
+                    assert torch.all(O[b] == 0)
+            _check_paged(w, O)
+
+
+def test_decode_paged_workspace_matches_allocating():
+    w = _to_dev_paged(wl.decode_paged(5, 16, 4, 128, 10, 3000, 16, 8, seed=34))
+    O1 = torch.empty_like(w.q)
+    attn.attn_decode_paged(O1, w.q, w.k_cache, w.v_cache, w.block_tables, w.lengths, 8)
+    nb = attn.attn_decode_workspace_bytes(5, 16, 8, 128)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    O2 = torch.empty_like(w.q)
+    attn.attn_decode_paged(O2, w.q, w.k_cache, w.v_cache, w.block_tables, w.lengths, 8,
+                           workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+    _check_paged(w, O1)
+
+
+def test_decode_paged_full_size_workload_sampled():
+    _say("workload decode_paged")
+    w = wl.make("decode_paged", device=DEV)
+    O = torch.empty_like(w.q)
+    attn.attn_decode_paged(O, w.q, w.k_cache, w.v_cache, w.block_tables, w.lengths,
+                           w.n_splits)
+    torch.cuda.synchronize()
+    assert torch.isfinite(O.float()).all()
+    lengths = w.lengths.cpu()
+    order = torch.argsort(lengths)
+    picks = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 0, 63})
+    bs = w.k_cache.shape[1]
+    for b in picks:
+        nb = (int(lengths[b]) + bs - 1) // bs
+        blocks = w.block_tables[b, :nb].long()
+        sub = wl.PagedDecode("sub", w.q[b:b + 1].cpu(), w.k_cache[blocks].cpu(),
+                             w.v_cache[blocks].cpu(),
+                             torch.arange(nb, dtype=torch.int32)[None], lengths[b:b + 1])
+        err = _check_paged(sub, O[b:b + 1])
+        _say(f"  decode_paged seq {b} (len {int(lengths[b])}): max-abs error {err:.3e}")
