@@ -329,7 +329,7 @@ void attn_decode_split_kernel(
 // padding nor stale cache contents can reach the result.  Table entries are
 // clamped to [0, num_blocks) so a corrupt table cannot address outside the
 // cache.
-template <int D, int GM>
+template <int D, int GM, bool WAVE_BLOCK>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void attn_decode_paged_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
@@ -388,33 +388,52 @@ void attn_decode_paged_kernel(
   }
 
   const int32_t* trow = tables + (size_t)b * max_blocks;
-  const size_t token_row = (size_t)Hkv * D;     // elements per cache token
-  const size_t head_off = (size_t)g * D + li * 8;
+  const int token_row = Hkv * D;                 // elements per cache token
+  const size_t block_elems = (size_t)token_row << bs_log2;
+  const int head_off = g * D + li * 8;
   const int slot_mask = (1 << bs_log2) - 1;
   const int nkeys = k_end - k_begin;
   const int npass = (nkeys + KPP - 1) / KPP;
   const int nround = (npass + NS - 1) / NS;
+  // The keys of one wave in one pass are KPW consecutive keys starting at a
+  // multiple of KPW (slices start at multiples of 64).  With WAVE_BLOCK
+  // (block_size >= KPW) they share one cache block, so the block-table entry
+  // is wave-uniform: a scalar load, and the block base a scalar address.
+  constexpr int KPW = 64 / LPK;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   auto key_of = [&](int rd, int st) { return k_begin + (rd * NS + st) * KPP + gi; };
-  auto table_entry = [&](int key) { return trow[key < k_end ? key >> bs_log2 : 0]; };
-  auto element = [&](int key, int entry) {
-    const bool ok = key < k_end;
-    const int phys = ok ? min(max(entry, 0), num_blocks - 1) : 0;
-    const int slot = ok ? (key & slot_mask) : 0;
-    return (((size_t)phys << bs_log2) | (size_t)slot) * token_row + head_off;
+  auto wave_key = [&](int rd, int st) {
+    return k_begin + (rd * NS + st) * KPP + wave * KPW;
+  };
+  auto table_entry = [&](int rd, int st) {
+    const int key = WAVE_BLOCK ? wave_key(rd, st) : key_of(rd, st);
+    return trow[key < k_end ? key >> bs_log2 : 0];
+  };
+  // Address of this lane's 16-byte chunk of key (rd, st) in `cache`, whose
+  // block-table entry is `entry`; keys past the slice read block 0.  With
+  // WAVE_BLOCK the block base is wave-uniform (a scalar 64-bit address) and
+  // the lane adds a 32-bit byte offset.
+  auto chunk = [&](const __bf16* cache, int rd, int st, int entry) {
+    const int key = key_of(rd, st);
+    const int lead = WAVE_BLOCK ? wave_key(rd, st) : key;
+    const int phys = lead < k_end ? min(max(entry, 0), num_blocks - 1) : 0;
+    const char* base = (const char*)(cache + (size_t)phys * block_elems);
+    const uint32_t off = (uint32_t)((key & slot_mask) * token_row + head_off) * 2u;
+    return *(const u32x4_t*)(base + off);
   };
 
   // tcur: table entries of the keys loaded in this round (round rd + 1);
   // tnext: those of round rd + 2, requested at the top of the round.
   int tcur[NS], tnext[NS];
 #pragma unroll
-  for (int st = 0; st < NS; ++st) tcur[st] = table_entry(key_of(0, st));
+  for (int st = 0; st < NS; ++st) tcur[st] = table_entry(0, st);
   u32x4_t kr[NS], vr[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st) kr[st] = vr[st] = u32x4_t{0, 0, 0, 0};
 
   for (int rd = -1; rd < nround; ++rd) {
 #pragma unroll
-    for (int st = 0; st < NS; ++st) tnext[st] = table_entry(key_of(rd + 2, st));
+    for (int st = 0; st < NS; ++st) tnext[st] = table_entry(rd + 2, st);
     float tsc[NS][GM];
     bool valid[NS];
 #pragma unroll
@@ -431,7 +450,7 @@ void attn_decode_paged_kernel(
     }
 #pragma unroll
     for (int st = 0; st < NS; ++st)
-      kr[st] = *(const u32x4_t*)(Kc + element(key_of(rd + 1, st), tcur[st]));
+      kr[st] = chunk(Kc, rd + 1, st, tcur[st]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh) {
@@ -465,7 +484,7 @@ void attn_decode_paged_kernel(
     }
 #pragma unroll
     for (int st = 0; st < NS; ++st)
-      vr[st] = *(const u32x4_t*)(Vc + element(key_of(rd + 1, st), tcur[st]));
+      vr[st] = chunk(Vc, rd + 1, st, tcur[st]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < NS; ++st) tcur[st] = tnext[st];
@@ -569,7 +588,7 @@ hipError_t launch_decode(void* O, const void* Q, const void* K, const void* V,
   return launch_decode_d<128>(O, Q, K, V, lengths, n_splits, B, H, Hkv, Smax, ws, stream);
 }
 
-template <int D, int GM>
+template <int D, int GM, bool WAVE_BLOCK>
 static hipError_t launch_paged_split(const void* Q, const void* Kc,
                                      const void* Vc, const int32_t* tables,
                                      const int32_t* lengths, float* Opart,
@@ -581,7 +600,7 @@ static hipError_t launch_paged_split(const void* Q, const void* Kc,
   const int n_hchunks = (G + GM - 1) / GM;
   const long long grid = (long long)B * Hkv * n_hchunks * n_splits;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-  hipLaunchKernelGGL((attn_decode_paged_kernel<D, GM>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_decode_paged_kernel<D, GM, WAVE_BLOCK>), dim3((unsigned)grid),
                      dim3(kDecThreads), 0, stream, (const __bf16*)Q,
                      (const __bf16*)Kc, (const __bf16*)Vc, tables, lengths,
                      Opart, Lpart, (__bf16*)O, B, H, Hkv, num_blocks, bs_log2,
@@ -601,14 +620,20 @@ static hipError_t launch_paged_d(void* O, const void* Q, const void* Kc,
       (float*)((char*)ws + (bhs * D * sizeof(float) + 255) / 256 * 256);
   const int G = H / Hkv;
   hipError_t e;
-#define ATTN_PAGED(GM)                                                        \
-  launch_paged_split<D, GM>(Q, Kc, Vc, tables, lengths, Opart, Lpart, O, B,   \
-                            H, Hkv, num_blocks, bs_log2, max_blocks, n_splits, \
-                            stream)
-  if (G <= 1) e = ATTN_PAGED(1);
-  else if (G <= 2) e = ATTN_PAGED(2);
-  else if (G <= 4) e = ATTN_PAGED(4);
-  else e = ATTN_PAGED(8);
+  // One wave covers 64 / (D / 8) consecutive keys per pass; when a cache
+  // block holds at least that many, the block lookup is wave-uniform.
+  // At most four query heads per workgroup (two with per-lane lookups): more
+  // would push the kernel past the 128 registers of four waves per SIMD;
+  // larger groups run as several head chunks that read the same K/V through L2.
+  const bool wave_block = (1 << bs_log2) >= 64 / (D / 8);
+#define ATTN_PAGED(GM, WB)                                                     \
+  launch_paged_split<D, GM, WB>(Q, Kc, Vc, tables, lengths, Opart, Lpart, O,  \
+                                B, H, Hkv, num_blocks, bs_log2, max_blocks,   \
+                                n_splits, stream)
+  if (G <= 1) e = wave_block ? ATTN_PAGED(1, true) : ATTN_PAGED(1, false);
+  else if (G <= 2 || !wave_block)
+    e = wave_block ? ATTN_PAGED(2, true) : ATTN_PAGED(2, false);
+  else e = ATTN_PAGED(4, true);
 #undef ATTN_PAGED
   if (e != hipSuccess || n_splits == 1) return e;
   const int BH = B * H;

@@ -372,6 +372,9 @@ PAGED_CASES = [
     (6, 32, 8, 128, 512, 4096, 16, 8),
     (2, 4, 4, 64, 64, 64, 1, 64),
     (3, 8, 2, 128, 1, 1000, 64, 8),
+    (2, 16, 2, 128, 1, 700, 16, 8),      # eight query heads per KV head
+    (2, 8, 2, 128, 1, 300, 2, 4),        # blocks smaller than a wave's keys
+    (2, 8, 2, 64, 1, 300, 4, 4),
 ]
 
 
