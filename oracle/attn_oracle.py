@@ -33,6 +33,9 @@ plainly, in float64 NumPy:
 * split-KV decode: one query per head and sequence, valid KV length per
   sequence, the cache processed as ``n_splits`` slices (Tylo.jl "Primitives",
   ``decode_attention!``);
+* the flex variants: ``SoftCapScore``, ``AliBiScore``, ``BiasScore``,
+  ``PrefixMask`` / ``prefix_lm``, ``DocumentMask`` and ``q_lengths``
+  (Tylo.jl "Primitives", ``flex_attention!`` and its mods);
 * the paged KV cache of a serving engine: a (num_blocks, block_size,
   num_kv_heads, head_size) cache addressed through per-sequence block tables
   and ``seq_lens`` (vllm_mlx.attention, ``get_kv_cache_shape`` and
@@ -51,6 +54,11 @@ repository's design notes):
 * ``k_lengths`` / ``lengths`` values are clamped to [0, Sk];
 * the decode slices hold C = ceil(ceil(len / TILE_N) / n_splits) * TILE_N keys
   each; the slice merge weighs each slice by exp(LSE_s - max LSE);
+* flex: score mods act on the scaled score, bias and ALiBi are added first
+  and soft-capping comes last; ALiBi adds slope * (q - kv) literally, with
+  absolute positions; the bias and doc_q are indexed by the local query row;
+  a prefix ORs keys j < prefix into the causal / window set; rows at or past
+  q_lengths[b] attend to nothing;
 * block tables: entry i of a sequence's row names the physical block holding
   its tokens [i * block_size, (i + 1) * block_size); a paged length is clamped
   to [0, max_blocks * block_size].
@@ -318,6 +326,117 @@ def decode_split_ref(Q, K, V, lengths, n_splits: int, tile_n: int = 64,
             w = np.exp(lses - Mx)
             O[b, h] = sum(wi * oi for wi, (oi, _) in zip(w, parts)) / w.sum()
             LSE[b, h] = Mx + np.log(w.sum())
+    return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# flex variants: score mods and mask mods
+# ---------------------------------------------------------------------------
+
+def flex_mask(Sq: int, Sk: int, causal: bool = False, window: int = 0,
+              input_pos: int = 0, k_len: int | None = None, q_len: int | None = None,
+              prefix: int = 0, doc_q=None, doc_kv=None) -> np.ndarray:
+    """Boolean (Sq, Sk) mask of the flex variants (Tylo.jl "Primitives").
+
+    * the causal / sliding-window set of ``allowed_mask`` (``CausalMask``,
+      ``SlidingWindowMask``; without causal it is ``FullMask``);
+    * OR keys j < prefix (``PrefixMask(len)``; ``prefix_lm(len)`` is
+      ``CausalMask() | PrefixMask(len)``);
+    * AND j < k_len, AND i < q_len (``k_lengths`` / ``q_lengths``: per-batch
+      valid lengths; query rows at or past q_len attend to nothing);
+    * AND doc_q[i] == doc_kv[j] (``DocumentMask(doc_q, doc_kv)``: a pair
+      attends iff its document ids match; doc_q is indexed by the local query
+      row, whose absolute position is input_pos + i).
+    """
+    base = allowed_mask(Sq, Sk, causal, window, input_pos, None)
+    j = np.arange(Sk)[None, :]
+    i = np.arange(Sq)[:, None]
+    if prefix > 0:
+        base = base | (j < prefix)
+    kl = Sk if k_len is None else min(max(int(k_len), 0), Sk)
+    ok = base & (j < kl)
+    if q_len is not None:
+        ok = ok & (i < min(max(int(q_len), 0), Sq))
+    if doc_q is not None:
+        ok = ok & (np.asarray(doc_q)[:Sq, None] == np.asarray(doc_kv)[None, :Sk])
+    return np.broadcast_to(ok, (Sq, Sk)).copy()
+
+
+def score_mods(s: np.ndarray, rows: np.ndarray, input_pos: int, bias=None,
+               alibi_slope: float | None = None, softcap: float = 0.0) -> np.ndarray:
+    """Score mods applied to scaled scores s (len(rows), Sk), in this order:
+
+    * ``BiasScore``: s + bias[i, j] (indexed by the local query row i);
+    * ``AliBiScore``: s + slope * (q - kv), q = input_pos + i the absolute query
+      position and kv the key position;
+    * ``SoftCapScore(cap)``: cap * tanh(s / cap), last.
+    The additive mods commute; soft-capping their sum is the composition
+    ``SoftCapScore ∘ ...`` (``ComposeScore`` applies its first mod first).
+    """
+    out = s.copy()
+    Sk = s.shape[1]
+    if bias is not None:
+        out = out + np.asarray(bias, dtype=np.float64)[rows][:, :Sk]
+    if alibi_slope is not None:
+        q = (input_pos + np.asarray(rows, dtype=np.int64))[:, None]
+        kv = np.arange(Sk, dtype=np.int64)[None, :]
+        out = out + float(alibi_slope) * (q - kv)
+    if softcap and softcap > 0:
+        out = softcap * np.tanh(out / softcap)
+    return out
+
+
+def flex_ref(Q, K, V, causal: bool = False, window: int = 0, input_pos: int = 0,
+             k_lengths=None, q_lengths=None, prefix: int = 0, softcap: float = 0.0,
+             alibi_slopes=None, bias=None, doc_q=None, doc_kv=None,
+             scale: float | None = None, heads=None, rows=None, row_chunk: int = 1024):
+    """FlexAttention forward in float64 (Tylo.jl "Primitives", ``flex_attention!``).
+
+    Scores s = scale * q.k (``qk_scale``, default 1/sqrt(D)); then the score
+    mods of ``score_mods``; then the mask of ``flex_mask`` (-inf where
+    blocked); softmax, O = P V, LSE = M + ln L.  ``bias`` is (Bb, Hb, Sq, Sk)
+    with Bb in {1, B} and Hb in {1, H}, broadcast when 1 (``BiasScore``);
+    ``alibi_slopes`` (H,); ``doc_q`` (B, Sq) and ``doc_kv`` (B, Sk) ints;
+    ``k_lengths`` / ``q_lengths`` (B,).  Returns (O, LSE) like ``attn_ref``.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, Sq, D = Q.shape
+    _, Hkv, Sk, _ = K.shape
+    if Hkv <= 0 or H % Hkv != 0:
+        raise ValueError("Heads must be a multiple of Heads_KV")
+    _check_mask_args(causal, window)
+    G = H // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    O = np.full((B, H, Sq, V.shape[3]), np.nan)
+    LSE = np.full((B, H, Sq), np.nan)
+    row_idx = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    masks = {}
+    for b, h in pairs:
+        if b not in masks:
+            masks[b] = flex_mask(
+                Sq, Sk, causal, window, input_pos,
+                None if k_lengths is None else int(k_lengths[b]),
+                None if q_lengths is None else int(q_lengths[b]), prefix,
+                None if doc_q is None else np.asarray(doc_q)[b],
+                None if doc_kv is None else np.asarray(doc_kv)[b])
+        g = h // G
+        bh = None
+        if bias is not None:
+            bias_a = np.asarray(bias)
+            bh = bias_a[b if bias_a.shape[0] > 1 else 0, h if bias_a.shape[1] > 1 else 0]
+        slope = None if alibi_slopes is None else float(alibi_slopes[h])
+        for c0 in range(0, len(row_idx), row_chunk):
+            r = row_idx[c0:c0 + row_chunk]
+            s = score_mods(scores(Q[b, h, r], K[b, g], scale), r, input_pos, bh, slope,
+                           softcap)
+            s = apply_mask(s, masks[b][r])
+            P, M, L = softmax_stats(s)
+            O[b, h, r] = combine(P, V[b, g])
+            LSE[b, h, r] = lse_from_stats(M, L)
     return O, LSE
 
 

@@ -558,3 +558,236 @@ def test_planted_paged_gather_mistake(monkeypatch):
 
 
 ORIG_GATHER = ora.gather_paged
+
+
+# ---------------------------------------------------------------------------
+# flex variants (score mods and mask mods)
+# ---------------------------------------------------------------------------
+
+def _flex_case(seed, B=2, H=4, Hkv=2, Sq=12, Sk=15, D=8):
+    rng = np.random.default_rng(seed)
+    return (rng, rng.standard_normal((B, H, Sq, D)), rng.standard_normal((B, Hkv, Sk, D)),
+            rng.standard_normal((B, Hkv, Sk, D)))
+
+
+@pytest.mark.parametrize("causal,window,ip,kl", [(False, 0, 0, None), (True, 0, 0, None),
+                                                 (True, 4, 3, [15, 9]), (True, 0, -2, [6, 15])])
+def test_flex_without_mods_is_plain_attention(causal, window, ip, kl):
+    _, Q, K, V = _flex_case(50)
+    O, L = ora.flex_ref(Q, K, V, causal, window, ip, kl)
+    Or, Lr = ora.attn_ref(Q, K, V, causal, window, ip, kl)
+    np.testing.assert_array_equal(O, Or)
+    np.testing.assert_array_equal(L, Lr)
+
+
+def _torch_sdpa_additive(Q, K, V, add):
+    """torch's own SDPA in float64 with a float additive mask (B or 1, H, Sq, Sk)."""
+    H, Hkv = Q.shape[1], K.shape[1]
+    rep = H // Hkv
+    q, k, v = (torch.from_numpy(x) for x in (Q, K, V))
+    k = k.repeat_interleave(rep, dim=1)
+    v = v.repeat_interleave(rep, dim=1)
+    return torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=torch.from_numpy(add)).numpy()
+
+
+@pytest.mark.parametrize("bias_shape", [(1, 1), (2, 1), (1, 4), (2, 4)])
+def test_flex_bias_alibi_document_prefix_vs_torch_sdpa(bias_shape):
+    rng, Q, K, V = _flex_case(51)
+    B, H, Sq, D = Q.shape
+    Sk = K.shape[2]
+    ip, prefix = 3, 5
+    bias = rng.standard_normal(bias_shape + (Sq, Sk))
+    slopes = -np.array([0.5, 0.25, 0.125, 0.0625])
+    doc_q = np.array([[0] * 6 + [1] * 6, [0] * 12])
+    doc_kv = np.array([[0] * 9 + [1] * 6, [0] * 10 + [2] * 5])
+    kl, ql = [15, 11], [12, 9]
+    O, L = ora.flex_ref(Q, K, V, True, 0, ip, kl, ql, prefix, 0.0, slopes, bias, doc_q, doc_kv)
+    # the additive mask, written out pair by pair
+    add = np.zeros((B, H, Sq, Sk))
+    for b in range(B):
+        for h in range(H):
+            for i in range(Sq):
+                for j in range(Sk):
+                    p = ip + i
+                    ok = (j <= p or j < prefix) and j < kl[b] and i < ql[b] \
+                        and doc_q[b][i] == doc_kv[b][j]
+                    add[b, h, i, j] = (bias[b % bias_shape[0], h % bias_shape[1], i, j]
+                                       + slopes[h] * (p - j)) if ok else -np.inf
+    Ot = _torch_sdpa_additive(Q, K, V, add)
+    has = np.isfinite(add).any(axis=3)
+    np.testing.assert_allclose(O[has], Ot[has], atol=1e-12)
+    assert np.all(O[~has] == 0) and np.all(np.isneginf(L[~has]))
+    sc = np.einsum("bhid,bhjd->bhij", Q, np.repeat(K, 2, axis=1)) / math.sqrt(D)
+    tot = np.where(np.isfinite(add), np.exp(sc + np.where(np.isfinite(add), add, 0.0)), 0.0)
+    lse_t = np.log(tot.sum(axis=3)[has])
+    np.testing.assert_allclose(L[has], lse_t, atol=1e-12)
+
+
+def test_alibi_closed_form_geometric_weights():
+    # Q = 0 makes every score slope*(p - j); with V = identity, O row p is the
+    # probability vector x^(p-j) / sum_{t<=p} x^t, x = e^slope (causal).
+    S = D = 16
+    slope = -0.3
+    Q = np.zeros((1, 1, S, D))
+    K = np.random.default_rng(52).standard_normal((1, 1, S, D))
+    V = np.eye(S)[None, None]
+    O, L = ora.flex_ref(Q, K, V, True, alibi_slopes=[slope])
+    x = math.exp(slope)
+    for p in range(S):
+        want = np.array([x ** (p - j) if j <= p else 0.0 for j in range(S)])
+        want /= (1 - x ** (p + 1)) / (1 - x)
+        np.testing.assert_allclose(O[0, 0, p], want, atol=1e-14)
+        assert abs(L[0, 0, p] - math.log((1 - x ** (p + 1)) / (1 - x))) < 1e-13
+
+
+def test_softcap_bruteforce_mpmath():
+    # brute force at 40 digits: scaled score, plus bias and ALiBi, then the cap
+    rng, Q, K, V = _flex_case(53, B=1, H=2, Hkv=1, Sq=4, Sk=6, D=3)
+    Q *= 3.0   # large scores so the cap bites
+    cap, ip = 1.5, 2
+    bias = rng.standard_normal((1, 2, 4, 6))
+    slopes = [-0.7, 0.4]
+    O, L = ora.flex_ref(Q, K, V, True, 0, ip, softcap=cap, alibi_slopes=slopes, bias=bias)
+    mpmath.mp.dps = 40
+    for h in range(2):
+        for i in range(4):
+            p = ip + i
+            w = []
+            for j in range(p + 1):
+                s = mpmath.mpf(0)
+                for d in range(3):
+                    s += mpmath.mpf(Q[0, h, i, d]) * mpmath.mpf(K[0, 0, j, d])
+                s = s / mpmath.sqrt(3) + mpmath.mpf(bias[0, h, i, j]) + slopes[h] * (p - j)
+                w.append(mpmath.exp(cap * mpmath.tanh(s / cap)))
+            tot = mpmath.fsum(w)
+            for d in range(3):
+                o = mpmath.fsum(w[j] * mpmath.mpf(V[0, 0, j, d]) for j in range(p + 1)) / tot
+                assert abs(float(o) - O[0, h, i, d]) < 1e-13
+            assert abs(float(mpmath.log(tot)) - L[0, h, i]) < 1e-13
+
+
+def test_softcap_limits():
+    _, Q, K, V = _flex_case(54)
+    O, _ = ora.flex_ref(Q, K, V, True, softcap=1e7)
+    Or, _ = ora.attn_ref(Q, K, V, True)
+    np.testing.assert_allclose(O, Or, atol=1e-9)
+    # a tiny cap squeezes every score to ~0: uniform weights over allowed keys
+    O, L = ora.flex_ref(Q, K, V, True, softcap=1e-9)
+    G = Q.shape[1] // K.shape[1]
+    for i in range(Q.shape[2]):
+        for h in range(Q.shape[1]):
+            np.testing.assert_allclose(O[:, h, i], V[:, h // G, :i + 1].mean(axis=1), atol=1e-9)
+            np.testing.assert_allclose(L[:, h, i], math.log(i + 1), atol=1e-9)
+
+
+def test_prefix_lm_decomposes():
+    # prefix_lm(len) = Causal | Prefix(len): rows inside the prefix see the whole
+    # prefix (bidirectional), later rows are plain causal rows.
+    _, Q, K, V = _flex_case(55, Sq=14, Sk=14)
+    n = 6
+    O, L = ora.flex_ref(Q, K, V, True, prefix=n)
+    Oa, La = ora.attn_ref(Q, K, V, False, 0, 0, [n, n])
+    Oc, Lc = ora.attn_ref(Q, K, V, True)
+    np.testing.assert_array_equal(O[:, :, :n], Oa[:, :, :n])
+    np.testing.assert_array_equal(O[:, :, n:], Oc[:, :, n:])
+    np.testing.assert_array_equal(L[:, :, n:], Lc[:, :, n:])
+
+
+def test_document_mask_block_diagonal_equals_separate_sequences():
+    _, Q, K, V = _flex_case(56, B=1, Sq=13, Sk=13)
+    bounds = [0, 4, 9, 13]
+    doc = np.repeat(np.arange(3), np.diff(bounds))[None]
+    O, L = ora.flex_ref(Q, K, V, True, doc_q=doc, doc_kv=doc)
+    for a, b in zip(bounds, bounds[1:]):
+        Od, Ld = ora.attn_ref(Q[:, :, a:b], K[:, :, a:b], V[:, :, a:b], True)
+        np.testing.assert_allclose(O[:, :, a:b], Od, atol=1e-14)
+        np.testing.assert_allclose(L[:, :, a:b], Ld, atol=1e-14)
+
+
+def test_q_lengths_rows_attend_to_nothing():
+    _, Q, K, V = _flex_case(57)
+    O, L = ora.flex_ref(Q, K, V, True, q_lengths=[5, 12])
+    Or, Lr = ora.attn_ref(Q, K, V, True)
+    np.testing.assert_array_equal(O[0, :, :5], Or[0, :, :5])
+    assert np.all(O[0, :, 5:] == 0) and np.all(np.isneginf(L[0, :, 5:]))
+    np.testing.assert_array_equal(O[1], Or[1])
+
+
+def _flex_pins_pass():
+    checks = [
+        lambda: test_flex_bias_alibi_document_prefix_vs_torch_sdpa((2, 4)),
+        test_alibi_closed_form_geometric_weights,
+        test_softcap_bruteforce_mpmath,
+        test_prefix_lm_decomposes,
+        test_document_mask_block_diagonal_equals_separate_sequences,
+        test_q_lengths_rows_attend_to_nothing,
+    ]
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError, TypeError):
+            return False
+    return True
+
+
+ORIG_SCORE_MODS = ora.score_mods
+ORIG_FLEX_MASK = ora.flex_mask
+
+
+def _mut_alibi_sign(s, rows, input_pos, bias=None, alibi_slope=None, softcap=0.0):
+    return ORIG_SCORE_MODS(s, rows, input_pos, bias,
+                           None if alibi_slope is None else -alibi_slope, softcap)
+
+
+def _mut_alibi_local_positions(s, rows, input_pos, bias=None, alibi_slope=None, softcap=0.0):
+    return ORIG_SCORE_MODS(s, rows, 0, bias, alibi_slope, softcap)
+
+
+def _mut_softcap_first(s, rows, input_pos, bias=None, alibi_slope=None, softcap=0.0):
+    out = softcap * np.tanh(s / softcap) if softcap else s
+    return ORIG_SCORE_MODS(out, rows, input_pos, bias, alibi_slope, 0.0)
+
+
+def _mut_bias_transposed(s, rows, input_pos, bias=None, alibi_slope=None, softcap=0.0):
+    if bias is not None:
+        bias = np.asarray(bias)
+        n = min(bias.shape)
+        bias = bias.copy()
+        bias[:n, :n] = bias[:n, :n].T
+    return ORIG_SCORE_MODS(s, rows, input_pos, bias, alibi_slope, softcap)
+
+
+def _mut_prefix_and(Sq, Sk, causal=False, window=0, input_pos=0, k_len=None, q_len=None,
+                    prefix=0, doc_q=None, doc_kv=None):
+    ok = ORIG_FLEX_MASK(Sq, Sk, causal, window, input_pos, k_len, q_len, 0, doc_q, doc_kv)
+    if prefix > 0:
+        ok &= np.arange(Sk)[None, :] < prefix
+    return ok
+
+
+def _mut_qlen_ignored(Sq, Sk, causal=False, window=0, input_pos=0, k_len=None, q_len=None,
+                      prefix=0, doc_q=None, doc_kv=None):
+    return ORIG_FLEX_MASK(Sq, Sk, causal, window, input_pos, k_len, None, prefix, doc_q, doc_kv)
+
+
+def _mut_doc_shifted(Sq, Sk, causal=False, window=0, input_pos=0, k_len=None, q_len=None,
+                     prefix=0, doc_q=None, doc_kv=None):
+    if doc_q is not None:
+        doc_q = np.roll(np.asarray(doc_q), 1)
+    return ORIG_FLEX_MASK(Sq, Sk, causal, window, input_pos, k_len, q_len, prefix, doc_q, doc_kv)
+
+
+@pytest.mark.parametrize("target,mutant", [
+    ("score_mods", _mut_alibi_sign),
+    ("score_mods", _mut_alibi_local_positions),
+    ("score_mods", _mut_softcap_first),
+    ("score_mods", _mut_bias_transposed),
+    ("flex_mask", _mut_prefix_and),
+    ("flex_mask", _mut_qlen_ignored),
+    ("flex_mask", _mut_doc_shifted),
+])
+def test_planted_flex_mistakes(monkeypatch, target, mutant):
+    assert _flex_pins_pass()
+    monkeypatch.setattr(ora, target, mutant)
+    assert not _flex_pins_pass(), f"no pin caught the planted mistake in {target}"
