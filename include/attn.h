@@ -102,6 +102,54 @@ int attn_fwd_f32(void* O, const void* Q, const void* K, const void* V,
                  int causal, int window, int input_pos,
                  const int32_t* k_lengths, hipStream_t stream);
 
+/* Flex variants of the bf16 prefill (Tylo.jl "Primitives", flex_attention!
+ * and its mods).  Every pointer is a caller-owned device pointer or NULL (mod
+ * off); a zeroed struct is plain attention.
+ *   q_lengths     int32 (B,): query rows i >= q_lengths[b] (clamped to
+ *                 [0, Sq]) attend to nothing: O = 0, LSE = -inf (q_lengths)
+ *   alibi_slopes  float32 (H,): adds slopes[h] * (q - kv) to the score, q the
+ *                 absolute query position input_pos + i, kv the key position
+ *                 (AliBiScore)
+ *   bias          float32 (bias_B, bias_H, Sq, Sk) row-major, added to the
+ *                 score; bias_B in {1, B} and bias_H in {1, H}, a size of 1
+ *                 broadcasting; indexed by the local query row (BiasScore).
+ *                 Requires (Sq * Sk + Sk) * 4 + 256 <= INT_MAX.
+ *   doc_q, doc_kv int32 (B, Sq) and (B, Sk): a pair attends only if
+ *                 doc_q[b][i] == doc_kv[b][j] (DocumentMask(doc_q, doc_kv));
+ *                 both or neither
+ *   prefix        >= 0: keys j < prefix are visible to every query in addition
+ *                 to the causal set (PrefixMask; causal + prefix is
+ *                 prefix_lm); > 0 with a window is ATTN_EUNSUPPORTED
+ *   softcap       0: off; > 0: score -> softcap * tanh(score / softcap),
+ *                 applied after bias and ALiBi (SoftCapScore)
+ *   qk_scale      0: 1/sqrt(D); > 0: the scale applied to q.k (qk_scale)
+ * The score is qk_scale * q.k, plus bias, plus ALiBi, then soft-capped; blocked
+ * pairs (causal / window / k_lengths / q_lengths / documents, OR the prefix)
+ * contribute nothing. */
+typedef struct attn_flex {
+  const int32_t* q_lengths;
+  const float* alibi_slopes;
+  const float* bias;
+  const int32_t* doc_q;
+  const int32_t* doc_kv;
+  int bias_B, bias_H;
+  int prefix;
+  float softcap;
+  float qk_scale;
+} attn_flex_t;
+
+/* attn_fwd with the flex mods of *flex (NULL = none), bf16 only.  Same
+ * arguments, layouts and errors as attn_fwd, plus ATTN_EINVAL for a bad
+ * flex field (softcap or qk_scale < 0, prefix < 0, bias_B / bias_H not 1 or
+ * B / H, doc_q without doc_kv or the reverse).  Defined by: Tylo.jl
+ * "Primitives", flex_attention! (score_mod, mask_mod, qk_scale, q_lengths),
+ * SoftCapScore, AliBiScore, BiasScore, PrefixMask, prefix_lm, DocumentMask. */
+int attn_fwd_flex(void* O, const void* Q, const void* K, const void* V,
+                  float* LSE, int B, int H, int Hkv, int Sq, int Sk, int D,
+                  int causal, int window, int input_pos,
+                  const int32_t* k_lengths, const attn_flex_t* flex,
+                  hipStream_t stream);
+
 /* Split-KV (Flash-Decoding) single-query decode, bf16 Q/K/V/O.
  *   O        out (B, H, D) bf16
  *   Q        in  (B, H, D) bf16

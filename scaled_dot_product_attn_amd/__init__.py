@@ -29,9 +29,19 @@ _lib = None
 
 _I = ctypes.c_int
 _P = ctypes.c_void_p
+
+
+class AttnFlex(ctypes.Structure):
+    """attn_flex_t of include/attn.h (device pointers, NULL = mod off)."""
+    _fields_ = [("q_lengths", _P), ("alibi_slopes", _P), ("bias", _P), ("doc_q", _P),
+                ("doc_kv", _P), ("bias_B", _I), ("bias_H", _I), ("prefix", _I),
+                ("softcap", ctypes.c_float), ("qk_scale", ctypes.c_float)]
+
 _SIGS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "attn_fwd_flex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P,
+                           ctypes.POINTER(AttnFlex), _P]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "attn_decode_ws": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
@@ -119,6 +129,39 @@ def attn_fwd_f32(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
     """float32 prefill forward into O (and LSE if given); see include/attn.h."""
     _fwd("attn_fwd_f32", torch.float32, O, Q, K, V, LSE, causal, window, input_pos,
          k_lengths, stream)
+
+
+def attn_fwd_flex(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
+                  k_lengths=None, q_lengths=None, prefix=0, softcap=0.0, alibi_slopes=None,
+                  bias=None, doc_q=None, doc_kv=None, qk_scale=0.0, stream=None) -> None:
+    """bf16 prefill with the flex mods (see attn_flex_t in include/attn.h).
+
+    ``bias`` float32 (bias_B, bias_H, Sq, Sk) with bias_B in {1, B}, bias_H in
+    {1, H}; ``alibi_slopes`` float32 (H,); ``q_lengths`` int32 (B,);
+    ``doc_q`` / ``doc_kv`` int32 (B, Sq) / (B, Sk).
+    """
+    B, H, Sq, D = Q.shape
+    _, Hkv, Sk, _ = K.shape
+    for t in (O, Q, K, V):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("attn_fwd_flex takes bfloat16 tensors")
+    for t, dt, name in ((LSE, torch.float32, "LSE"), (k_lengths, torch.int32, "k_lengths"),
+                        (q_lengths, torch.int32, "q_lengths"),
+                        (alibi_slopes, torch.float32, "alibi_slopes"),
+                        (bias, torch.float32, "bias"), (doc_q, torch.int32, "doc_q"),
+                        (doc_kv, torch.int32, "doc_kv")):
+        if t is not None and t.dtype != dt:
+            raise ValueError(f"{name} must be {dt}")
+    if bias is not None and (bias.dim() != 4 or tuple(bias.shape[2:]) != (Sq, Sk)):
+        raise ValueError("bias must be (bias_B, bias_H, Sq, Sk)")
+    f = AttnFlex(_ptr(q_lengths), _ptr(alibi_slopes), _ptr(bias), _ptr(doc_q), _ptr(doc_kv),
+                 bias.shape[0] if bias is not None else 0,
+                 bias.shape[1] if bias is not None else 0,
+                 int(prefix), float(softcap), float(qk_scale))
+    rc = lib().attn_fwd_flex(_ptr(O), _ptr(Q), _ptr(K), _ptr(V), _ptr(LSE), B, H, Hkv, Sq,
+                             Sk, D, int(bool(causal)), int(window), int(input_pos),
+                             _ptr(k_lengths), ctypes.byref(f), _stream(stream))
+    _check(rc, "attn_fwd_flex")
 
 
 def attn_decode_workspace_bytes(B: int, H: int, n_splits: int, D: int) -> int:

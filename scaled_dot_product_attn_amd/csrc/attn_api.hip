@@ -19,6 +19,10 @@ hipError_t launch_fwd_bf16(void*, const void*, const void*, const void*,
                            float*, int, int, int, int, int, int, int, int,
                            const int32_t*, hipStream_t);
 template <int D>
+hipError_t launch_fwd_flex(void*, const void*, const void*, const void*,
+                           float*, int, int, int, int, int, int, int, int,
+                           const int32_t*, const attn_flex_t*, hipStream_t);
+template <int D>
 hipError_t launch_fwd_f32(void*, const void*, const void*, const void*,
                           float*, int, int, int, int, int, int, int, int,
                           const int32_t*, hipStream_t);
@@ -137,6 +141,32 @@ int attn_fwd(void* O, const void* Q, const void* K, const void* V, float* LSE,
               : launch_fwd_bf16<128>(O, Q, K, V, LSE, B, H, Hkv, Sq, Sk,
                                      causal, window, input_pos, k_lengths,
                                      stream);
+  return hip_status(e);
+}
+
+int attn_fwd_flex(void* O, const void* Q, const void* K, const void* V,
+                  float* LSE, int B, int H, int Hkv, int Sq, int Sk, int D,
+                  int causal, int window, int input_pos,
+                  const int32_t* k_lengths, const attn_flex_t* flex,
+                  hipStream_t stream) {
+  int rc = check_fwd(O, Q, K, V, B, H, Hkv, Sq, Sk, D, causal, window);
+  if (rc != ATTN_OK) return rc;
+  attn_flex_t none = {};
+  const attn_flex_t* f = flex ? flex : &none;
+  if (f->softcap < 0.f || f->qk_scale < 0.f || f->prefix < 0) return ATTN_EINVAL;
+  if ((f->doc_q == nullptr) != (f->doc_kv == nullptr)) return ATTN_EINVAL;
+  if (f->bias) {
+    if ((f->bias_B != 1 && f->bias_B != B) || (f->bias_H != 1 && f->bias_H != H))
+      return ATTN_EINVAL;
+    if (((long long)Sq * Sk + Sk) * 4 + 256 > INT_MAX) return ATTN_EUNSUPPORTED;
+  }
+  if (f->prefix > 0 && window > 0) return ATTN_EUNSUPPORTED;
+  if (Sq == 0) return ATTN_OK;
+  hipError_t e =
+      D == 64 ? launch_fwd_flex<64>(O, Q, K, V, LSE, B, H, Hkv, Sq, Sk, causal,
+                                    window, input_pos, k_lengths, f, stream)
+              : launch_fwd_flex<128>(O, Q, K, V, LSE, B, H, Hkv, Sq, Sk, causal,
+                                     window, input_pos, k_lengths, f, stream);
   return hip_status(e);
 }
 

@@ -8,7 +8,10 @@
 // For one row that is the half-open interval [lo, hi) with
 //   lo = clamp(p - window + 1, 0, kl)   (0 without a window)
 //   hi = clamp(p + 1, 0, kl)            (kl without causal masking)
-// and both ends are non-decreasing in i.
+// and both ends are non-decreasing in i.  The flex prefix (Tylo.jl
+// "Primitives", PrefixMask / prefix_lm = CausalMask | PrefixMask) ORs keys
+// j < prefix into a causal row without a window, which keeps the row one
+// interval: hi = clamp(max(p + 1, prefix), 0, kl).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,10 +31,12 @@ __host__ __device__ inline int clamp_i64(long long x, int lo, int hi) {
 }
 
 __host__ __device__ inline RowRange row_range(int i, int kl, int causal,
-                                              int window, int input_pos) {
+                                              int window, int input_pos,
+                                              int prefix = 0) {
   long long p = (long long)input_pos + i;
   RowRange r;
-  r.hi = causal ? clamp_i64(p + 1, 0, kl) : kl;
+  const long long reach = p + 1 > prefix ? p + 1 : (long long)prefix;
+  r.hi = causal ? clamp_i64(reach, 0, kl) : kl;
   r.lo = window > 0 ? clamp_i64(p - window + 1, 0, kl) : 0;
   return r;
 }
@@ -52,21 +57,25 @@ struct KvGeometry {
 };
 
 // Closed form from the monotone row ends.  A row is non-empty iff kl > 0,
-// p >= 0 when causal (earlier rows have hi = 0) and p <= kl + window - 2 when
-// windowed (later rows have lo = kl).  So the non-empty rows are [a, b] with
-//   a = max(i0, -input_pos) (causal) and b = min(i1 - 1, kl + window - 2 -
-//   input_pos) (window),
-// and the union of their intervals runs from lo(a) to hi(b).
+// p >= 0 when causal without a prefix (earlier rows have hi = 0) and
+// p <= kl + window - 2 when windowed (later rows have lo = kl).  So the
+// non-empty rows are [a, b] with
+//   a = max(i0, -input_pos) (causal, no prefix) and b = min(i1 - 1, kl +
+//   window - 2 - input_pos) (window),
+// and the union of their intervals runs from lo(a) to hi(b).  (A prefix is
+// only taken without a window.)
 __host__ __device__ inline KvGeometry kv_geometry(int i0, int i1, int kl,
                                                   int causal, int window,
-                                                  int input_pos) {
+                                                  int input_pos,
+                                                  int prefix = 0) {
   KvGeometry g;
-  RowRange first = row_range(i0, kl, causal, window, input_pos);
-  RowRange last = row_range(i1 - 1, kl, causal, window, input_pos);
+  RowRange first = row_range(i0, kl, causal, window, input_pos, prefix);
+  RowRange last = row_range(i1 - 1, kl, causal, window, input_pos, prefix);
   g.all_lo = last.lo;
   g.all_hi = first.hi;
   long long a = i0, b = (long long)i1 - 1;
-  if (causal && -(long long)input_pos > a) a = -(long long)input_pos;
+  if (causal && prefix <= 0 && -(long long)input_pos > a)
+    a = -(long long)input_pos;
   if (window > 0) {
     long long lb = (long long)kl + window - 2 - input_pos;
     if (lb < b) b = lb;
@@ -77,8 +86,8 @@ __host__ __device__ inline KvGeometry kv_geometry(int i0, int i1, int kl,
     return g;
   }
   g.any = 1;
-  g.union_lo = row_range((int)a, kl, causal, window, input_pos).lo;
-  g.union_hi = row_range((int)b, kl, causal, window, input_pos).hi;
+  g.union_lo = row_range((int)a, kl, causal, window, input_pos, prefix).lo;
+  g.union_hi = row_range((int)b, kl, causal, window, input_pos, prefix).hi;
   return g;
 }
 

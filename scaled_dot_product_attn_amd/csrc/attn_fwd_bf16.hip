@@ -35,6 +35,15 @@
 //   The key order inside V^T's LDS rows is permuted to match the order in
 //   which the S^T accumulator registers hold the keys.
 //
+// Flex variants (FLEX = true; Tylo.jl "Primitives", flex_attention! and its
+// mods): the same kernel with the score rewritten before the softmax, in this
+// order: qk_scale * s, plus an additive bias tile (BiasScore), plus
+// slope_h * (q - kv) (AliBiScore), then cap * tanh(. / cap) (SoftCapScore);
+// and the mask extended by a prefix (prefix_lm = CausalMask | PrefixMask),
+// per-batch query lengths (q_lengths) and document ids (DocumentMask).  The
+// bias tile of a lane's row is loaded at the start of the M-phase that computes
+// the tile's scores, document ids of the keys are staged in LDS with K.
+//
 // Online softmax in base 2: t = s * log2(e) / sqrt(D), p = exp2(t - m).  The
 // running max m is only raised when a tile's max exceeds it by more than
 // 2^8 (p <= 256 otherwise), so the O rescale is skipped on almost all tiles;
@@ -66,6 +75,19 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 static_assert(kFwdTileM == ATTN_FWD_TILE_M && kFwdTileN == ATTN_FWD_TILE_N,
               "the exported tile plan must use the kernel's tile sizes");
 
+// Kernel-side copy of attn_flex_t (see include/attn.h); strides in elements.
+struct FlexArgs {
+  const int32_t* q_lengths;
+  const float* alibi;
+  const float* bias;
+  const int32_t* doc_q;
+  const int32_t* doc_kv;
+  long long bias_bstride, bias_hstride;
+  int prefix;
+  float softcap;
+  float qk_scale;
+};
+
 template <int D>
 struct FwdLds {
   // K tile: kFwdTileN rows of D bf16, each row padded by 16 bytes so that the
@@ -78,6 +100,10 @@ struct FwdLds {
   // two K buffers, then two V^T buffers
   static constexpr int kOffV = 2 * kBytesK;
   static constexpr int kTotal = 2 * kBytesK + 2 * kBytesV;
+  // flex: two buffers of the tile's kFwdTileN document ids
+  static constexpr int kOffDoc = kTotal;
+  static constexpr int kBytesDoc = kFwdTileN * 4;
+  static constexpr int kTotalFlex = kTotal + 2 * kBytesDoc;
 };
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
@@ -105,21 +131,21 @@ __device__ inline int vt_group_pos(int quad_in_group) {
   return ((quad_in_group & 1) << 3) | ((quad_in_group >> 1) << 2);
 }
 
-template <int D>
+template <int D, bool FLEX>
 __global__ __launch_bounds__(kFwdThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     __bf16* __restrict__ O, const __bf16* __restrict__ Q,
     const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     float* __restrict__ LSE, int B, int H, int Hkv, int Sq, int Sk, int causal,
     int window, int input_pos, const int32_t* __restrict__ k_lengths,
-    float scale_log2) {
+    float scale_log2, FlexArgs fx) {
   using L = FwdLds<D>;
   constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int DBLK = D / 32;     // 32-wide blocks of the head dimension
   constexpr int KLOADS = kFwdTileN * D / 8 / kGroupThreads;  // K loads/thread
   constexpr int VTHREADS = (kFwdTileN / 4) * (D / 8);        // threads staging V
 
-  __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
+  __shared__ __attribute__((aligned(16))) char smem[FLEX ? L::kTotalFlex : L::kTotal];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -155,14 +181,27 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const int i0 = qt * kFwdTileM;
   const int i1 = min(i0 + kFwdTileM, Sq);
   const int kl = k_lengths ? min(max(k_lengths[b], 0), Sk) : Sk;
-  const KvGeometry geo = kv_geometry(i0, i1, kl, causal, window, input_pos);
+  // flex: rows at or past q_lengths[b] attend to nothing; the geometry covers
+  // the live rows, and a workgroup with dead rows (or a document mask) masks
+  // every tile element by element
+  int prefix = 0, ql = Sq;
+  bool force_partial = false;
+  if constexpr (FLEX) {
+    prefix = fx.prefix;
+    if (fx.q_lengths) ql = min(max(fx.q_lengths[b], 0), Sq);
+    force_partial = fx.doc_q != nullptr || ql < i1;
+  }
+  const int i1g = FLEX ? max(min(i1, ql), i0) : i1;
+  KvGeometry geo = {0, 0, 0, 0, 0};
+  if (i1g > i0) geo = kv_geometry(i0, i1g, kl, causal, window, input_pos, prefix);
 
   const size_t q_base = ((size_t)(b * H + h) * Sq) * D;
   const size_t kv_base = ((size_t)(b * Hkv + g) * Sk) * D;
 
   // ---- my query row ----
   const int qi = i0 + wave * 32 + lrow;  // global query row of this lane
-  const RowRange rr = row_range(qi, kl, causal, window, input_pos);
+  RowRange rr = row_range(qi, kl, causal, window, input_pos, prefix);
+  if (FLEX && qi >= ql) rr.lo = rr.hi = 0;
 
   bf16x8_t qreg[KSTEPS];
   {
@@ -202,6 +241,31 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(V + valid_base), (short)0, nvalid * D * 2, kBufferRsrcWord3);
 
+  // ---- flex per-lane state ----
+  const bool has_bias = FLEX && fx.bias != nullptr;
+  const bool has_alibi = FLEX && fx.alibi != nullptr;
+  const bool has_doc = FLEX && fx.doc_q != nullptr;
+  const bool has_cap = FLEX && fx.softcap > 0.f;
+  float alibi_slope = 0.f;
+  int doc_row = 0;
+  int bias_row = 0;
+  if constexpr (FLEX) {
+    if (has_alibi) alibi_slope = fx.alibi[h];
+    if (has_doc) doc_row = qi < Sq ? fx.doc_q[(size_t)b * Sq + qi] : 0;
+    // rows past Sq read zeros
+    if (has_bias) bias_row = qi < Sq ? qi * Sk : Sq * Sk;
+  }
+  // document ids of the workgroup's key union; the (batch, head) bias plane
+  const __amdgpu_buffer_rsrc_t doc_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      has_doc ? (void*)(fx.doc_kv + (size_t)b * Sk + geo.union_lo) : nullptr,
+      (short)0, has_doc ? nvalid * 4 : 0, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t bias_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      has_bias ? (void*)(fx.bias + b * fx.bias_bstride + h * fx.bias_hstride)
+               : nullptr,
+      (short)0, has_bias ? Sq * Sk * 4 : 0, kBufferRsrcWord3);
+  f32x16_t bias_t[2];  // bias of this lane's row for the tile being scored
+  u32x4_t stg_doc = {0, 0, 0, 0};
+
   u32x4_t stg[4];
   const int vkq = gtid & 15;  // key quad within the tile (V staging)
   const int vdc = gtid >> 4;  // 8-wide d chunk (V staging)
@@ -219,6 +283,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                          krsrc, (key * D + dch * 8) * 2, 0, 0));
       }
+      if (FLEX && has_doc && gtid < kFwdTileN / 4)
+        stg_doc = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         doc_rsrc, (rel0 + gtid * 4) * 4, 0, 0));
     } else if (v_stager) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -240,6 +308,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         const int dch = c % (D / 8);
         *(u32x4_t*)(kb + key * L::kRowK + dch * 16) = stg[i];
       }
+      if (FLEX && has_doc && gtid < kFwdTileN / 4)
+        *(u32x4_t*)(smem + L::kOffDoc + buf * L::kBytesDoc + gtid * 16) = stg_doc;
     } else if (v_stager) {
       // 4 keys x 8 d  ->  8 rows of V^T, 4 keys (8 bytes) each
       char* vb = smem + L::kOffV + buf * L::kBytesV;
@@ -280,6 +350,20 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
           }
       }
     }
+    if (FLEX && do_s && has_bias) {
+      // lane's keys of the tile: j0 + kb2*32 + q4*8 + half*4 + e, held in
+      // register q4*4 + e of block kb2 (the S^T accumulator order)
+      const int jb = kt * kFwdTileN + half * 4;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = jb + kb2 * 32 + (r >> 2) * 8 + (r & 3);
+          bias_t[kb2][r] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(
+                         bias_rsrc, (bias_row + j) * 4, 0, 0));
+        }
+    }
     if (do_s) {
       const char* kb = smem + (kt & 1) * L::kBytesK;
 #pragma unroll
@@ -297,9 +381,72 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   };
 
   // V-phase: softmax of S(kt) into P(kt); stage tile kt+1 and fetch kt+2
+  // flex: scores into base-2 units of the modified score, in place
+  constexpr float kLog2e = 1.4426950408889634f;
+  auto flex_scores = [&](int j0) {
+    const float cap = fx.softcap;
+    const float cap_k = 2.f * kLog2e / cap;  // exp(2x/cap) = exp2(x * cap_k)
+    const int p = input_pos + qi;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb2][r] *= fx.qk_scale;
+    if (has_bias) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb2][r] += bias_t[kb2][r];
+    }
+    if (has_alibi) {
+      // slope * (p - j) with j = j0 + half*4 + c, c constant per register
+      const float a0 = alibi_slope * (float)(p - j0 - half * 4);
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float c = (float)(kb2 * 32 + (r >> 2) * 8 + (r & 3));
+          s[kb2][r] += __builtin_fmaf(-alibi_slope, c, a0);
+        }
+    }
+    if (has_cap) {
+      // cap * tanh(x / cap) = cap - 2 cap / (exp(2x / cap) + 1)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(s[kb2][r] * cap_k);
+          s[kb2][r] = cap - 2.f * cap * __builtin_amdgcn_rcpf(e + 1.f);
+        }
+    }
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb2][r] *= kLog2e;
+  };
+  // flex: a key whose document differs from the row's is blocked
+  auto doc_mask = [&](int kt) {
+    const char* db = smem + L::kOffDoc + (kt & 1) * L::kBytesDoc + half * 16;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x4_t ids = *(const u32x4_t*)(db + (kb2 * 32 + q4 * 8) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((int)ids[e] != doc_row) s[kb2][q4 * 4 + e] = -INFINITY;
+      }
+  };
+  // base-2 factor of the exponent: the plain path scales here, flex scores
+  // are already in base-2 units
+  const float sl2 = FLEX ? 1.f : scale_log2;
+
   auto v_phase = [&](int kt) {
     const int j0 = kt * kFwdTileN;
-    if (tile_class(geo, j0, kFwdTileN) == kTilePartial) {
+    if constexpr (FLEX) {
+      flex_scores(j0);
+      if (has_doc) doc_mask(kt);
+    }
+    if (tile_class(geo, j0, kFwdTileN) == kTilePartial || (FLEX && force_partial)) {
       // key j0 + half*4 + c is allowed iff c lies in [t_lo, t_lo + width);
       // c is a compile-time constant per register, so one subtract, one
       // unsigned compare and one select per score
@@ -318,7 +465,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    const float mt = pair_max(mx) * scale_log2;
+    const float mt = pair_max(mx) * sl2;
     const bool need = mt > m_run + kLazyRescale;
     if (__builtin_amdgcn_ballot_w64(need)) {
       // need == false leaves the lane unchanged (and avoids -inf - -inf)
@@ -337,9 +484,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 =
-            __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], scale_log2, -mref));
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], sl2, -mref));
         const float p1 = __builtin_amdgcn_exp2f(
-            __builtin_fmaf(s[kb2][r + 1], scale_log2, -mref));
+            __builtin_fmaf(s[kb2][r + 1], sl2, -mref));
         psum += p0 + p1;
         pb[kb2][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
       }
@@ -399,21 +546,54 @@ hipError_t launch_fwd_bf16(void* O, const void* Q, const void* K,
   const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
   const long long total = (long long)nqt * H * B;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)total),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), dim3((unsigned)total),
                      dim3(kFwdThreads), 0, stream, (__bf16*)O,
                      (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                      B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                     scale_log2);
+                     scale_log2, FlexArgs{});
   return hipGetLastError();
 }
 
-template hipError_t launch_fwd_bf16<64>(void*, const void*, const void*,
-                                        const void*, float*, int, int, int,
-                                        int, int, int, int, int,
-                                        const int32_t*, hipStream_t);
-template hipError_t launch_fwd_bf16<128>(void*, const void*, const void*,
-                                         const void*, float*, int, int, int,
-                                         int, int, int, int, int,
-                                         const int32_t*, hipStream_t);
+template <int D>
+hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
+                           const void* V, float* LSE, int B, int H, int Hkv,
+                           int Sq, int Sk, int causal, int window,
+                           int input_pos, const int32_t* k_lengths,
+                           const attn_flex_t* f, hipStream_t stream) {
+  const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
+  const long long total = (long long)nqt * H * B;
+  FlexArgs fx{};
+  fx.q_lengths = f->q_lengths;
+  fx.alibi = f->alibi_slopes;
+  fx.bias = f->bias;
+  fx.doc_q = f->doc_q;
+  fx.doc_kv = f->doc_kv;
+  const long long plane = (long long)Sq * Sk;
+  fx.bias_hstride = f->bias && f->bias_H > 1 ? plane : 0;
+  fx.bias_bstride = f->bias && f->bias_B > 1 ? plane * f->bias_H : 0;
+  fx.prefix = f->prefix;
+  fx.softcap = f->softcap;
+  fx.qk_scale = f->qk_scale > 0.f ? f->qk_scale : 1.f / sqrtf((float)D);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), dim3((unsigned)total),
+                     dim3(kFwdThreads), 0, stream, (__bf16*)O,
+                     (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
+                     B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
+                     0.f, fx);
+  return hipGetLastError();
+}
+
+#define ATTN_INST(D)                                                          \
+  template hipError_t launch_fwd_bf16<D>(void*, const void*, const void*,     \
+                                         const void*, float*, int, int, int,  \
+                                         int, int, int, int, int,             \
+                                         const int32_t*, hipStream_t);        \
+  template hipError_t launch_fwd_flex<D>(void*, const void*, const void*,     \
+                                         const void*, float*, int, int, int,  \
+                                         int, int, int, int, int,             \
+                                         const int32_t*, const attn_flex_t*,  \
+                                         hipStream_t);
+ATTN_INST(64)
+ATTN_INST(128)
+#undef ATTN_INST
 
 }  // namespace attn

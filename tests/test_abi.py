@@ -37,7 +37,8 @@ def _declared():
 def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("attn_fwd", "attn_fwd_f32", "attn_decode", "attn_decode_ws",
-              "attn_decode_workspace_bytes", "attn_decode_paged", "attn_mask_dump",
+              "attn_decode_workspace_bytes", "attn_decode_paged", "attn_fwd_flex",
+              "attn_mask_dump",
               "attn_tile_plan",
               "attn_status_string", "attn_version"):
         assert n in names
@@ -82,6 +83,26 @@ def test_fwd_argument_errors(lib, fn):
     assert _fwd(lib, fn, Sq=2**31 - 10) == attn.ATTN_EUNSUPPORTED
     # nothing to do: returns before touching the device
     assert _fwd(lib, fn, Sq=0, O=None, Q=None) == attn.ATTN_OK
+
+
+def test_fwd_flex_argument_errors(lib):
+    def flex(f=None, causal=1, window=0, B=1, H=4, Sq=8, Sk=8, D=128):
+        return lib.attn_fwd_flex(1, 1, 1, 1, None, B, H, 2, Sq, Sk, D, causal, window, 0,
+                                 None, None if f is None else ctypes.byref(f), None)
+    assert flex(H=3) == attn.ATTN_EINVAL
+    assert flex(D=96) == attn.ATTN_EUNSUPPORTED
+    assert flex(causal=0, window=3) == attn.ATTN_EINVAL
+    assert flex(attn.AttnFlex(softcap=-1.0)) == attn.ATTN_EINVAL
+    assert flex(attn.AttnFlex(qk_scale=-0.5)) == attn.ATTN_EINVAL
+    assert flex(attn.AttnFlex(prefix=-1)) == attn.ATTN_EINVAL
+    assert flex(attn.AttnFlex(prefix=4), window=2) == attn.ATTN_EUNSUPPORTED
+    assert flex(attn.AttnFlex(bias=8, bias_B=3, bias_H=1), B=2) == attn.ATTN_EINVAL
+    assert flex(attn.AttnFlex(bias=8, bias_B=1, bias_H=2)) == attn.ATTN_EINVAL
+    assert flex(attn.AttnFlex(bias=8, bias_B=1, bias_H=1), Sq=40000, Sk=40000) == \
+        attn.ATTN_EUNSUPPORTED
+    assert flex(attn.AttnFlex(doc_q=8)) == attn.ATTN_EINVAL
+    assert flex(attn.AttnFlex(doc_kv=8)) == attn.ATTN_EINVAL
+    assert flex(Sq=0) == attn.ATTN_OK
 
 
 def test_decode_argument_errors(lib):

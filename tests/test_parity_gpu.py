@@ -464,3 +464,133 @@ def test_decode_paged_full_size_workload_sampled():
                              torch.arange(nb, dtype=torch.int32)[None], lengths[b:b + 1])
         err = _check_paged(sub, O[b:b + 1])
         _say(f"  decode_paged seq {b} (len {int(lengths[b])}): max-abs error {err:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# flex variants
+# ---------------------------------------------------------------------------
+
+def _flex_inputs(B, H, Hkv, Sq, Sk, D, seed, qscale=1.0):
+    w = wl.prefill_random(B, H, Hkv, Sq, Sk, D, torch.bfloat16, seed=seed)
+    if qscale != 1.0:
+        w.q = (w.q.float() * qscale).bfloat16()
+    return w
+
+
+def _run_flex(w, causal=True, window=0, input_pos=0, k_lengths=None, **mods):
+    dev = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in mods.items()}
+    q, k, v = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV)
+    O = torch.empty_like(q)
+    L = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    kl = None if k_lengths is None else torch.tensor(k_lengths, dtype=torch.int32, device=DEV)
+    attn.attn_fwd_flex(O, q, k, v, L, causal, window, input_pos, kl, **dev)
+    torch.cuda.synchronize()
+    return O, L
+
+
+def _check_flex(w, O, L, causal=True, window=0, input_pos=0, k_lengths=None, heads=None,
+                rows=None, **mods):
+    np_mods = {k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in mods.items()}
+    if "qk_scale" in np_mods:  # the oracle's name for qk_scale
+        np_mods["scale"] = np_mods.pop("qk_scale")
+    Or, Lr = ora.flex_ref(_np(w.q), _np(w.k), _np(w.v), causal, window, input_pos,
+                          k_lengths, heads=heads, rows=rows, **np_mods)
+    On, Ln = _np(O), _np(L)
+    sel = ~np.isnan(Lr)
+    err = np.max(np.abs(On[sel] - Or[sel]))
+    assert err <= TOL_BF16, f"flex O max-abs error {err}"
+    np.testing.assert_array_equal(np.isneginf(Ln[sel]), np.isneginf(Lr[sel]))
+    fin = sel & np.isfinite(Lr)
+    if fin.any():
+        lerr = np.max(np.abs(Ln[fin] - Lr[fin]))
+        assert lerr <= TOL_LSE, f"flex LSE error {lerr}"
+    return err
+
+
+def _docs(B, S, n_docs, seed):
+    g = torch.Generator().manual_seed(seed)
+    out = torch.empty(B, S, dtype=torch.int32)
+    for b in range(B):
+        cuts = torch.sort(torch.randperm(S - 1, generator=g)[:n_docs - 1] + 1).values.tolist()
+        edges = [0] + cuts + [S]
+        for d, (a, c) in enumerate(zip(edges, edges[1:])):
+            out[b, a:c] = d
+    return out
+
+
+FLEX_CASES = {
+    "softcap": dict(shape=(2, 8, 2, 257, 257, 128), qscale=4.0, mods=dict(softcap=20.0)),
+    "softcap_d64": dict(shape=(1, 4, 4, 300, 300, 64), qscale=4.0, mods=dict(softcap=5.0)),
+    "alibi_offset": dict(shape=(1, 8, 2, 200, 456, 128), causal=True, input_pos=256,
+                         mods=dict(alibi=True)),
+    "bias_full": dict(shape=(2, 4, 2, 257, 300, 128), causal=False, mods=dict(bias=(2, 4))),
+    "bias_broadcast": dict(shape=(2, 4, 2, 257, 257, 128), mods=dict(bias=(1, 1))),
+    "bias_heads": dict(shape=(2, 4, 1, 130, 190, 64), causal=False, mods=dict(bias=(1, 4))),
+    "document": dict(shape=(2, 8, 2, 600, 600, 128), mods=dict(docs=5)),
+    "document_noncausal": dict(shape=(1, 4, 2, 300, 300, 128), causal=False, mods=dict(docs=3)),
+    "prefix_lm": dict(shape=(2, 4, 2, 300, 300, 128), mods=dict(prefix=100)),
+    "prefix_long": dict(shape=(1, 4, 1, 520, 520, 128), mods=dict(prefix=400)),
+    "q_lengths": dict(shape=(2, 4, 2, 600, 600, 128), mods=dict(q_lengths=[517, 37])),
+    "qk_scale": dict(shape=(1, 4, 2, 200, 200, 128), mods=dict(qk_scale=0.05)),
+    "everything": dict(shape=(2, 8, 2, 300, 330, 128), input_pos=30, k_lengths=[330, 250],
+                       qscale=2.0,
+                       mods=dict(softcap=15.0, alibi=True, bias=(2, 1), docs=4, prefix=40,
+                                 q_lengths=[290, 300])),
+}
+
+
+def _build_mods(case, w, seed):
+    B, H, Hkv, Sq, Sk, D = case["shape"]
+    g = torch.Generator().manual_seed(seed)
+    mods = {}
+    for k, v in case["mods"].items():
+        if k == "alibi":
+            mods["alibi_slopes"] = -torch.rand(H, generator=g, dtype=torch.float32) * 0.1
+        elif k == "bias":
+            mods["bias"] = torch.randn(v + (Sq, Sk), generator=g, dtype=torch.float32)
+        elif k == "docs":
+            docs = _docs(B, max(Sq, Sk), v, seed)
+            mods["doc_q"] = docs[:, :Sq].contiguous()
+            mods["doc_kv"] = docs[:, :Sk].contiguous()
+        elif k == "q_lengths":
+            mods["q_lengths"] = torch.tensor(v, dtype=torch.int32)
+        else:
+            mods[k] = v
+    return mods
+
+
+@pytest.mark.parametrize("name", list(FLEX_CASES))
+def test_flex_parity(name):
+    case = FLEX_CASES[name]
+    _say(f"flex {name} {case['shape']}")
+    w = _flex_inputs(*case["shape"], seed=60, qscale=case.get("qscale", 1.0))
+    mods = _build_mods(case, w, 61)
+    kw = dict(causal=case.get("causal", True), input_pos=case.get("input_pos", 0),
+              k_lengths=case.get("k_lengths"))
+    O, L = _run_flex(w, **kw, **mods)
+    assert torch.isfinite(O.float()).all()
+    _check_flex(w, O, L, **kw, **mods)
+
+
+def test_flex_without_mods_matches_plain():
+    w = _flex_inputs(2, 8, 2, 300, 300, 128, seed=62)
+    O, L = _run_flex(w, causal=True)
+    Op, Lp = _run_prefill(wl.Prefill("p", w.q, w.k, w.v, True))
+    assert (O.float() - Op.float()).abs().max().item() <= 2 * TOL_BF16 / 4
+    assert (L - Lp).abs().max().item() <= 1e-4
+    _check_flex(w, O, L, causal=True)
+
+
+def test_flex_full_size_sampled():
+    # the causal GQA shape with soft-capping and ALiBi, sampled rows
+    _say("flex gqa_causal-size softcap + alibi")
+    w = wl.make("gqa_causal")
+    g = torch.Generator().manual_seed(63)
+    slopes = -torch.rand(32, generator=g) * 0.01
+    O, L = _run_flex(w, causal=True, softcap=30.0, alibi_slopes=slopes)
+    assert torch.isfinite(O.float()).all()
+    rows = _sample_rows(4096, np.random.default_rng(64))
+    heads = [(0, 0), (0, 13), (1, 31)]
+    err = _check_flex(w, O, L, causal=True, heads=heads, rows=rows, softcap=30.0,
+                      alibi_slopes=slopes)
+    _say(f"  sampled max-abs error {err:.3e}")
