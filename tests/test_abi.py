@@ -174,32 +174,54 @@ def _random_cases(n, seed):
         ip = int(rng.integers(-100, 500))
         kl = int(rng.integers(-5, Sk + 6))
         tm, tn = [(128, 64), (64, 32), (16, 16), (7, 5)][int(rng.integers(0, 4))]
-        cases.append((Sq, Sk, causal, window, ip, kl, tm, tn))
+        # a prefix (prefix_lm) only with causal masking and no window
+        prefix = int(rng.choice([0, 0, 1, 7, 100, 300])) if causal and window == 0 else 0
+        cases.append((Sq, Sk, causal, window, ip, kl, tm, tn, prefix))
     return cases
+
+
+def _plan_from_mask(ok, Sq, Sk, tm, tn):
+    """Empty / partial / full per tile, by brute force over the element mask."""
+    nqt, nkt = -(-Sq // tm), -(-Sk // tn)
+    pad = np.zeros((Sq, nkt * tn), dtype=bool)
+    pad[:, :Sk] = ok
+    plan = np.empty((nqt, nkt), dtype=np.int8)
+    for qt in range(nqt):
+        for kt in range(nkt):
+            blk = pad[qt * tm:(qt + 1) * tm, kt * tn:(kt + 1) * tn]
+            plan[qt, kt] = ora.TILE_EMPTY if not blk.any() else (
+                ora.TILE_FULL if blk.all() else ora.TILE_PARTIAL)
+    return plan
 
 
 def test_host_geometry_matches_oracle(plan_check):
     cases = _random_cases(400, 1) + [
-        (4096, 4096, 1, 0, 0, 4096, 128, 64), (2048, 16384, 1, 4096, 14336, 16384, 128, 64),
-        (256, 256, 1, 0, 0, 256, 128, 64), (256, 256, 1, 64, 0, 256, 128, 64),
-        (100, 100, 0, 0, 0, 100, 64, 64), (10, 0, 0, 0, 0, 0, 128, 64),
+        (4096, 4096, 1, 0, 0, 4096, 128, 64, 0), (2048, 16384, 1, 4096, 14336, 16384, 128, 64, 0),
+        (256, 256, 1, 0, 0, 256, 128, 64, 0), (256, 256, 1, 64, 0, 256, 128, 64, 0),
+        (100, 100, 0, 0, 0, 100, 64, 64, 0), (10, 0, 0, 0, 0, 0, 128, 64, 0),
+        (300, 300, 1, 0, 0, 300, 256, 64, 100), (300, 300, 1, 0, -50, 250, 256, 64, 400),
     ]
     inp = "\n".join(" ".join(map(str, c)) for c in cases) + "\n"
     out = subprocess.run([plan_check], input=inp, capture_output=True, text=True,
                          check=True).stdout.split("\n")
     pos = 0
-    for (Sq, Sk, causal, window, ip, kl, tm, tn) in cases:
+    for (Sq, Sk, causal, window, ip, kl, tm, tn, prefix) in cases:
         _, nqt, nkt = out[pos].split()
         pos += 1
         plan = np.array([[int(ch) for ch in out[pos + r]] for r in range(int(nqt))],
                         dtype=np.int8).reshape(int(nqt), int(nkt))
         pos += int(nqt)
-        want = ora.tile_plan_ref(Sq, Sk, bool(causal), window, ip, kl, tm, tn)
-        np.testing.assert_array_equal(plan, want, err_msg=str((Sq, Sk, causal, window, ip, kl, tm, tn)))
+        case = (Sq, Sk, causal, window, ip, kl, tm, tn, prefix)
+        mask = ora.flex_mask(Sq, Sk, bool(causal), window, ip, kl, prefix=prefix)
+        if prefix == 0:
+            want = ora.tile_plan_ref(Sq, Sk, bool(causal), window, ip, kl, tm, tn)
+        else:
+            want = _plan_from_mask(mask, Sq, Sk, tm, tn)
+        np.testing.assert_array_equal(plan, want, err_msg=str(case))
         assert out[pos] == f"rows {Sq}"
         pos += 1
         rows = np.array([list(map(int, out[pos + i].split())) for i in range(Sq)])
         pos += Sq
         j = np.arange(Sk)[None, :]
         got = (j >= rows[:, :1]) & (j < rows[:, 1:])
-        np.testing.assert_array_equal(got, ora.allowed_mask(Sq, Sk, bool(causal), window, ip, kl))
+        np.testing.assert_array_equal(got, mask, err_msg=str(case))
