@@ -12,7 +12,8 @@ decode rate in GB/s (K/V bytes of the valid keys, once per KV head, plus Q and
 O) is reported beside it.  The window/offset and clustered-image workloads are
 timed too, as extra lines of context, and so is the same decode batch stored
 in a paged serving cache (block size 16, shuffled physical blocks;
-attn_decode_paged).  ``cpu_baseline`` times the fp64 oracle
+attn_decode_paged), and the causal GQA prefill with soft-capping and ALiBi
+(attn_fwd_flex).  ``cpu_baseline`` times the fp64 oracle
 on the host on a bounded sample (whole heads) of the prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -156,6 +157,9 @@ def main():
     extra = {} if args.no_extra else {n: wl.make(n, device=dev)
                                      for n in ("window_offset", "image_clustered")}
     paged = None if args.no_extra else wl.make("decode_paged", device=dev)
+    # flex: the causal GQA prefill with soft-capping (cap 30) and ALiBi slopes
+    gflex = torch.Generator().manual_seed(7)
+    flex_slopes = (-torch.rand(pre.q.shape[1], generator=gflex) * 0.01).to(dev)
     B, H, Sq, D = pre.q.shape
     O = torch.empty_like(pre.q)
     LSE = torch.empty(B, H, Sq, dtype=torch.float32, device=dev)
@@ -180,7 +184,15 @@ def main():
         attn.attn_decode_paged(Op, paged.q, paged.k_cache, paged.v_cache, paged.block_tables,
                                paged.lengths, paged.n_splits, workspace=ws)
 
+    Of, Lf = torch.empty_like(pre.q), torch.empty_like(LSE)
+
+    def run_flex():
+        attn.attn_fwd_flex(Of, pre.q, pre.k, pre.v, Lf, True, softcap=30.0,
+                           alibi_slopes=flex_slopes)
+
     names = ["prefill", "decode"] + list(extra) + (["decode_paged"] if paged is not None else [])
+    if not args.no_extra:
+        names.append("flex_softcap_alibi")
     ev = {n: [] for n in names}
 
     def step(record):
@@ -195,6 +207,8 @@ def main():
                 run_decode()
             elif n == "decode_paged":
                 run_paged()
+            elif n == "flex_softcap_alibi":
+                run_flex()
             else:
                 run_prefill(extra[n], *ext_out[n])
             if record:
@@ -260,6 +274,12 @@ def main():
             tf = f / (ms[n] * 1e-3) / 1e12
             out["extra"][n] = {"ms": round(ms[n], 4), "TFLOP/s": round(tf, 2),
                                "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": f}
+    if "flex_softcap_alibi" in ms:
+        tf = fl / (ms["flex_softcap_alibi"] * 1e-3) / 1e12
+        out["flex_softcap_alibi"] = {
+            "ms": round(ms["flex_softcap_alibi"], 4), "TFLOP/s": round(tf, 2),
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": fl,
+            "config": "gqa_causal prefill with soft-cap 30 and ALiBi slopes (attn_fwd_flex)"}
     if paged is not None:
         pb = decode_bytes(paged)
         gbs = pb / (ms["decode_paged"] * 1e-3) / 1e9

@@ -131,7 +131,7 @@ __device__ inline int vt_group_pos(int quad_in_group) {
   return ((quad_in_group & 1) << 3) | ((quad_in_group >> 1) << 2);
 }
 
-template <int D, bool FLEX>
+template <int D, bool FLEX, bool BIAS>
 __global__ __launch_bounds__(kFwdThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     __bf16* __restrict__ O, const __bf16* __restrict__ Q,
@@ -242,7 +242,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       (void*)(V + valid_base), (short)0, nvalid * D * 2, kBufferRsrcWord3);
 
   // ---- flex per-lane state ----
-  const bool has_bias = FLEX && fx.bias != nullptr;
+  const bool has_bias = FLEX && BIAS;
   const bool has_alibi = FLEX && fx.alibi != nullptr;
   const bool has_doc = FLEX && fx.doc_q != nullptr;
   const bool has_cap = FLEX && fx.softcap > 0.f;
@@ -381,47 +381,52 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   };
 
   // V-phase: softmax of S(kt) into P(kt); stage tile kt+1 and fetch kt+2
-  // flex: scores into base-2 units of the modified score, in place
+  // flex: scores into base-2 units of the modified score, in place.  With y =
+  // qk_scale * s + bias + alibi (natural units), the base-2 score is
+  //   y * log2(e)                                  without a cap, and
+  //   log2(e) * cap * tanh(y / cap) = A - B / (exp2(y * 2 log2(e) / cap) + 1)
+  // with A = log2(e) * cap, B = 2 A; the factor in front of y (u) is folded
+  // into the per-element FMAs.  Without bias, ALiBi and cap the factor goes
+  // into the exponent instead (no pass over the scores).
   constexpr float kLog2e = 1.4426950408889634f;
+  const bool transform = has_bias || has_alibi || has_cap;
+  const float u = has_cap ? 2.f * kLog2e / fx.softcap : kLog2e;
+  const float k_s = fx.qk_scale * u;
+  const float cap_a = kLog2e * fx.softcap, cap_b = 2.f * cap_a;
   auto flex_scores = [&](int j0) {
-    const float cap = fx.softcap;
-    const float cap_k = 2.f * kLog2e / cap;  // exp(2x/cap) = exp2(x * cap_k)
-    const int p = input_pos + qi;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb2][r] *= fx.qk_scale;
-    if (has_bias) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb2][r] += bias_t[kb2][r];
-    }
     if (has_alibi) {
-      // slope * (p - j) with j = j0 + half*4 + c, c constant per register
-      const float a0 = alibi_slope * (float)(p - j0 - half * 4);
+      // u * slope * (p - j) with j = j0 + half*4 + c, c constant per register
+      const float su = alibi_slope * u;
+      const float a0 = su * (float)(input_pos + qi - j0 - half * 4);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float c = (float)(kb2 * 32 + (r >> 2) * 8 + (r & 3));
-          s[kb2][r] += __builtin_fmaf(-alibi_slope, c, a0);
+          s[kb2][r] = __builtin_fmaf(s[kb2][r], k_s, __builtin_fmaf(-su, c, a0));
         }
+    } else {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb2][r] *= k_s;
+    }
+    if (has_bias) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb2][r] = __builtin_fmaf(bias_t[kb2][r], u, s[kb2][r]);
     }
     if (has_cap) {
-      // cap * tanh(x / cap) = cap - 2 cap / (exp(2x / cap) + 1)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[kb2][r] * cap_k);
-          s[kb2][r] = cap - 2.f * cap * __builtin_amdgcn_rcpf(e + 1.f);
+          const float e = __builtin_amdgcn_exp2f(s[kb2][r]);
+          s[kb2][r] = __builtin_fmaf(-cap_b, __builtin_amdgcn_rcpf(e + 1.f), cap_a);
         }
     }
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb2][r] *= kLog2e;
   };
   // flex: a key whose document differs from the row's is blocked
   auto doc_mask = [&](int kt) {
@@ -436,14 +441,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
           if ((int)ids[e] != doc_row) s[kb2][q4 * 4 + e] = -INFINITY;
       }
   };
-  // base-2 factor of the exponent: the plain path scales here, flex scores
-  // are already in base-2 units
-  const float sl2 = FLEX ? 1.f : scale_log2;
+  // base-2 factor of the exponent: the plain path scales here, transformed
+  // flex scores are already in base-2 units
+  const float sl2 = FLEX ? (transform ? 1.f : fx.qk_scale * kLog2e) : scale_log2;
 
   auto v_phase = [&](int kt) {
     const int j0 = kt * kFwdTileN;
     if constexpr (FLEX) {
-      flex_scores(j0);
+      if (transform) flex_scores(j0);
       if (has_doc) doc_mask(kt);
     }
     if (tile_class(geo, j0, kFwdTileN) == kTilePartial || (FLEX && force_partial)) {
@@ -546,7 +551,7 @@ hipError_t launch_fwd_bf16(void* O, const void* Q, const void* K,
   const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
   const long long total = (long long)nqt * H * B;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), dim3((unsigned)total),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false>), dim3((unsigned)total),
                      dim3(kFwdThreads), 0, stream, (__bf16*)O,
                      (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                      B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
@@ -574,11 +579,19 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
   fx.prefix = f->prefix;
   fx.softcap = f->softcap;
   fx.qk_scale = f->qk_scale > 0.f ? f->qk_scale : 1.f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), dim3((unsigned)total),
-                     dim3(kFwdThreads), 0, stream, (__bf16*)O,
-                     (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
-                     B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                     0.f, fx);
+  // the bias tile costs 32 registers per lane: a kernel of its own
+  if (fx.bias)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true>), dim3((unsigned)total),
+                       dim3(kFwdThreads), 0, stream, (__bf16*)O,
+                       (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
+                       B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
+                       0.f, fx);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false>), dim3((unsigned)total),
+                       dim3(kFwdThreads), 0, stream, (__bf16*)O,
+                       (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
+                       B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
+                       0.f, fx);
   return hipGetLastError();
 }
 
