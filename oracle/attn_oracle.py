@@ -33,6 +33,8 @@ plainly, in float64 NumPy:
 * split-KV decode: one query per head and sequence, valid KV length per
   sequence, the cache processed as ``n_splits`` slices (Tylo.jl "Primitives",
   ``decode_attention!``);
+* the backward: input gradients from the output gradient (Tylo.jl
+  "Primitives", ``∇attention!``);
 * the flex variants: ``SoftCapScore``, ``AliBiScore``, ``BiasScore``,
   ``PrefixMask`` / ``prefix_lm``, ``DocumentMask`` and ``q_lengths``
   (Tylo.jl "Primitives", ``flex_attention!`` and its mods);
@@ -327,6 +329,63 @@ def decode_split_ref(Q, K, V, lengths, n_splits: int, tile_n: int = 64,
             O[b, h] = sum(wi * oi for wi, (oi, _) in zip(w, parts)) / w.sum()
             LSE[b, h] = Mx + np.log(w.sum())
     return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def softmax_backward(P: np.ndarray, dP: np.ndarray) -> np.ndarray:
+    """Row-wise softmax vector-Jacobian product: dS = P * (dP - sum_j dP P)."""
+    return P * (dP - (dP * P).sum(axis=1, keepdims=True))
+
+
+def attn_bwd_ref(Q, K, V, dO, causal: bool = False, window: int = 0, input_pos: int = 0,
+                 k_lengths=None, scale: float | None = None, heads=None):
+    """Gradients of the masked attention forward, in float64.
+
+    Tylo.jl "Primitives", ``∇attention!``: from the output gradient dO (Ō) and
+    the primals, the input gradients dQ, dK, dV.  Written out from the chain
+    rule of O = P V with P = softmax(S), S = scale * Q K^T + mask:
+
+      dV   = P^T dO
+      dP   = dO V^T
+      dS   = P * (dP - rowsum(dP * P))       (softmax Jacobian, row by row)
+      dQ   = scale * dS K,   dK = scale * dS^T Q
+
+    With GQA, a KV head's dK / dV sum the contributions of every query head
+    that reads it.  Rows without an allowed key contribute nothing.  Returns
+    (dQ (B, H, Sq, D), dK, dV (B, Hkv, Sk, D)); ``heads`` restricts dQ to the
+    listed (b, h) pairs (dK / dV are then partial sums and not meaningful).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, H, Sq, D = Q.shape
+    _, Hkv, Sk, _ = K.shape
+    if Hkv <= 0 or H % Hkv != 0:
+        raise ValueError("Heads must be a multiple of Heads_KV")
+    _check_mask_args(causal, window)
+    G = H // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dQ = np.full(Q.shape, np.nan)
+    dK = np.zeros(K.shape)
+    dV = np.zeros(V.shape)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    for b, h in pairs:
+        kl = None if k_lengths is None else int(k_lengths[b])
+        ok = allowed_mask(Sq, Sk, causal, window, input_pos, kl)
+        g = h // G
+        s = apply_mask(scores(Q[b, h], K[b, g], scale), ok)
+        P, _, _ = softmax_stats(s)
+        dV[b, g] += P.T @ dO[b, h]
+        dP = dO[b, h] @ V[b, g].T
+        dS = softmax_backward(P, dP)
+        dQ[b, h] = scale * (dS @ K[b, g])
+        dK[b, g] += scale * (dS.T @ Q[b, h])
+    return dQ, dK, dV
 
 
 # ---------------------------------------------------------------------------

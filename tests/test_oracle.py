@@ -791,3 +791,97 @@ def test_planted_flex_mistakes(monkeypatch, target, mutant):
     assert _flex_pins_pass()
     monkeypatch.setattr(ora, target, mutant)
     assert not _flex_pins_pass(), f"no pin caught the planted mistake in {target}"
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def _loss(Q, K, V, dO, **kw):
+    O, _ = ora.attn_ref(Q, K, V, **kw)
+    return float(np.sum(np.where(np.isnan(O), 0.0, O) * dO))
+
+
+@pytest.mark.parametrize("kw", [dict(causal=False), dict(causal=True),
+                                dict(causal=True, window=3, input_pos=2, k_lengths=[7, 5])],
+                         ids=["full", "causal", "window_offset_klen"])
+def test_bwd_matches_central_differences(kw):
+    # d/dx of sum(dO * O(Q, K, V)) by central differences of the forward oracle
+    rng = np.random.default_rng(70)
+    B, H, Hkv, Sq, Sk, D = 2, 4, 2, 5, 7, 3
+    Q = rng.standard_normal((B, H, Sq, D))
+    K = rng.standard_normal((B, Hkv, Sk, D))
+    V = rng.standard_normal((B, Hkv, Sk, D))
+    dO = rng.standard_normal((B, H, Sq, D))
+    dQ, dK, dV = ora.attn_bwd_ref(Q, K, V, dO, **kw)
+    eps = 1e-6
+    for X, G in ((Q, dQ), (K, dK), (V, dV)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            x0 = X[idx]
+            X[idx] = x0 + eps
+            lp = _loss(Q, K, V, dO, **kw)
+            X[idx] = x0 - eps
+            lm = _loss(Q, K, V, dO, **kw)
+            X[idx] = x0
+            num[idx] = (lp - lm) / (2 * eps)
+        G = np.where(np.isnan(G), 0.0, G)
+        np.testing.assert_allclose(G, num, atol=1e-7)
+
+
+def test_bwd_matches_torch_autograd():
+    rng = np.random.default_rng(71)
+    B, H, Hkv, S, D = 2, 8, 2, 33, 16
+    Q = rng.standard_normal((B, H, S, D))
+    K = rng.standard_normal((B, Hkv, S, D))
+    V = rng.standard_normal((B, Hkv, S, D))
+    dO = rng.standard_normal((B, H, S, D))
+    dQ, dK, dV = ora.attn_bwd_ref(Q, K, V, dO, causal=True)
+    q, k, v = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q, k.repeat_interleave(H // Hkv, dim=1), v.repeat_interleave(H // Hkv, dim=1),
+        is_causal=True)
+    o.backward(torch.from_numpy(dO))
+    np.testing.assert_allclose(dQ, q.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dK, k.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dV, v.grad.numpy(), atol=1e-12)
+
+
+def test_bwd_special_cases():
+    rng = np.random.default_rng(72)
+    B, H, S, D = 1, 2, 6, 4
+    Q = rng.standard_normal((B, H, S, D))
+    K = rng.standard_normal((B, H, S, D))
+    V = rng.standard_normal((B, H, S, D))
+    dO = rng.standard_normal((B, H, S, D))
+    # constant V: O does not depend on Q or K at all
+    Vc = np.ones_like(V) * 0.7
+    dQ, dK, dV = ora.attn_bwd_ref(Q, K, Vc, dO, causal=True)
+    np.testing.assert_allclose(dQ, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dK, 0.0, atol=1e-14)
+    # dV columns sum to the dO columns (each row of P sums to one)
+    np.testing.assert_allclose(dV.sum(axis=2), dO.sum(axis=2), atol=1e-12)
+    # a row whose only key is itself (window 1): O = V_i exactly, so dV_i = dO_i
+    # and no gradient reaches Q or K
+    dQ, dK, dV = ora.attn_bwd_ref(Q, K, V, dO, causal=True, window=1)
+    np.testing.assert_allclose(dV, dO, atol=1e-14)
+    np.testing.assert_allclose(dQ, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dK, 0.0, atol=1e-14)
+
+
+def test_planted_bwd_mistakes(monkeypatch):
+    def no_rowsum(P, dP):
+        return P * dP
+
+    def transposed(P, dP):
+        return (P * (dP - (dP * P).sum(axis=1, keepdims=True))).T.T * 1.0001
+
+    for mutant in (no_rowsum, transposed):
+        monkeypatch.setattr(ora, "softmax_backward", mutant)
+        with pytest.raises(AssertionError):
+            test_bwd_matches_central_differences(dict(causal=True))
+    monkeypatch.undo()
+    real = ora.scores
+    monkeypatch.setattr(ora, "scores", lambda q, k, scale: real(q, k, 1.0))
+    with pytest.raises(AssertionError):
+        test_bwd_matches_torch_autograd()
