@@ -150,6 +150,36 @@ int attn_fwd_flex(void* O, const void* Q, const void* K, const void* V,
                   const int32_t* k_lengths, const attn_flex_t* flex,
                   hipStream_t stream);
 
+/* Bytes of scratch attn_bwd needs (two float32 values per query row),
+ * host-only; 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int D);
+
+/* Backward of attn_fwd (bf16): input gradients from the output gradient.
+ *   dQ        out (B, H, Sq, D) bf16
+ *   dK, dV    out (B, Hkv, Sk, D) bf16 (overwritten; keys no query may see
+ *             get 0)
+ *   dO        in  (B, H, Sq, D) bf16, the output gradient
+ *   Q, K, V   in  the forward's inputs
+ *   O, LSE    in  the forward's output and its float32 row LSE (attn_fwd with
+ *             LSE != NULL); rows with LSE = -inf contribute nothing
+ *   B .. k_lengths: as attn_fwd and equal to the forward's
+ *   workspace NULL: allocated stream-ordered on `stream`; else a caller buffer
+ *             of ws_bytes >= attn_bwd_workspace_bytes(B, H, Sq, D), 256-byte
+ *             aligned, not shared by concurrent calls
+ * With S = Q K^T / sqrt(D) + mask and P = exp(S - LSE):
+ *   dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)), dQ = dS K / sqrt(D),
+ *   dK = dS^T Q / sqrt(D); a KV head's dK / dV sum over its query heads.
+ * Float32 accumulation; P and dS are rounded to bf16 as matrix-core operands.
+ * Errors as attn_fwd, plus ATTN_EINVAL for a NULL gradient, dO or LSE, or too
+ * small / misaligned a workspace.  Defined by: Tylo.jl "Primitives",
+ * ∇attention! (gradients from Ō, the primals, O and the checkpoints M/L;
+ * scratch workspace; causal / input_pos matching the forward). */
+int attn_bwd(void* dQ, void* dK, void* dV, const void* dO, const void* Q,
+             const void* K, const void* V, const void* O, const float* LSE,
+             int B, int H, int Hkv, int Sq, int Sk, int D, int causal,
+             int window, int input_pos, const int32_t* k_lengths,
+             void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Split-KV (Flash-Decoding) single-query decode, bf16 Q/K/V/O.
  *   O        out (B, H, D) bf16
  *   Q        in  (B, H, D) bf16

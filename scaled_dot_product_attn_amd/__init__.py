@@ -45,6 +45,9 @@ _SIGS = {
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "attn_decode_ws": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                      _P, _P, ctypes.c_size_t, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
                                ctypes.c_size_t, _P]),
     "attn_mask_dump": (_I, [_P, _I, _I, _I, _I, _I, _I, _P]),
@@ -162,6 +165,31 @@ def attn_fwd_flex(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
                              Sk, D, int(bool(causal)), int(window), int(input_pos),
                              _ptr(k_lengths), ctypes.byref(f), _stream(stream))
     _check(rc, "attn_fwd_flex")
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, Sq: int, D: int) -> int:
+    return lib().attn_bwd_workspace_bytes(B, H, Sq, D)
+
+
+def attn_bwd(dQ, dK, dV, dO, Q, K, V, O, LSE, causal=False, window=0, input_pos=0,
+             k_lengths=None, workspace=None, stream=None) -> None:
+    """Backward of attn_fwd into dQ, dK, dV (bf16); see include/attn.h."""
+    B, H, Sq, D = Q.shape
+    _, Hkv, Sk, _ = K.shape
+    for t in (dQ, dK, dV, dO, Q, K, V, O):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("attn_bwd takes bfloat16 tensors")
+    if LSE.dtype != torch.float32:
+        raise ValueError("LSE must be float32")
+    if k_lengths is not None and k_lengths.dtype != torch.int32:
+        raise ValueError("k_lengths must be int32")
+    ws = _ptr(workspace) if workspace is not None else None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().attn_bwd(_ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dO), _ptr(Q), _ptr(K), _ptr(V),
+                        _ptr(O), _ptr(LSE), B, H, Hkv, Sq, Sk, D, int(bool(causal)),
+                        int(window), int(input_pos), _ptr(k_lengths), ws, nbytes,
+                        _stream(stream))
+    _check(rc, "attn_bwd")
 
 
 def attn_decode_workspace_bytes(B: int, H: int, n_splits: int, D: int) -> int:

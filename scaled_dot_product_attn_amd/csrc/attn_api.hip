@@ -30,6 +30,11 @@ hipError_t launch_decode(void*, const void*, const void*, const void*,
                          const int32_t*, int, int, int, int, int, int, void*,
                          hipStream_t);
 size_t decode_workspace_bytes(int B, int H, int n_splits, int D);
+hipError_t launch_bwd(void*, void*, void*, const void*, const void*,
+                      const void*, const void*, const void*, const float*, int,
+                      int, int, int, int, int, int, int, int, const int32_t*,
+                      void*, hipStream_t);
+size_t bwd_workspace_bytes(int B, int H, int Sq);
 hipError_t launch_decode_paged(void*, const void*, const void*, const void*,
                                const int32_t*, const int32_t*, int, int, int,
                                int, int, int, int, int, void*, hipStream_t);
@@ -220,6 +225,48 @@ int attn_decode(void* O, const void* Q, const void* K, const void* V,
   rc = hip_status(launch_decode(O, Q, K, V, lengths, n_splits, B, H, Hkv, Smax,
                                 D, ws, stream));
   if (ws && hipFreeAsync(ws, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    rc = ATTN_EHIP;
+  }
+  return rc;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int D) {
+  if (B < 1 || H < 1 || Sq < 1 || (D != 64 && D != 128)) return 0;
+  return bwd_workspace_bytes(B, H, Sq);
+}
+
+int attn_bwd(void* dQ, void* dK, void* dV, const void* dO, const void* Q,
+             const void* K, const void* V, const void* O, const float* LSE,
+             int B, int H, int Hkv, int Sq, int Sk, int D, int causal,
+             int window, int input_pos, const int32_t* k_lengths,
+             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_fwd(O, Q, K, V, B, H, Hkv, Sq, Sk, D, causal, window);
+  if (rc != ATTN_OK) return rc;
+  if (Sq == 0 && Sk == 0) return ATTN_OK;
+  if (Sk > 0 && (!dK || !dV || !K || !V)) return ATTN_EINVAL;
+  if (Sq > 0 && (!dQ || !dO || !LSE)) return ATTN_EINVAL;
+  if ((long long)B * H * Sq > INT_MAX / 2) return ATTN_EUNSUPPORTED;
+  if (Sq == 0)  // no query: the key gradients are zero, no scratch needed
+    return hip_status(launch_bwd(dQ, dK, dV, dO, Q, K, V, O, LSE, B, H, Hkv,
+                                 Sq, Sk, D, causal, window, input_pos,
+                                 k_lengths, nullptr, stream));
+  void* ws = workspace;
+  bool owned = false;
+  const size_t need = bwd_workspace_bytes(B, H, Sq);
+  if (ws) {
+    if (((uintptr_t)ws & 255) != 0 || ws_bytes < need) return ATTN_EINVAL;
+  } else {
+    if (hipMallocAsync(&ws, need, stream) != hipSuccess) {
+      (void)hipGetLastError();
+      return ATTN_EHIP;
+    }
+    owned = true;
+  }
+  rc = hip_status(launch_bwd(dQ, dK, dV, dO, Q, K, V, O, LSE, B, H, Hkv, Sq, Sk,
+                             D, causal, window, input_pos, k_lengths, ws,
+                             stream));
+  if (owned && hipFreeAsync(ws, stream) != hipSuccess) {
     (void)hipGetLastError();
     rc = ATTN_EHIP;
   }

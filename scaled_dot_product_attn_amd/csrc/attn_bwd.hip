@@ -1,0 +1,604 @@
+// Backward of the bf16 attention forward on gfx950 (MI355X).
+//
+// Tylo.jl "Primitives", ∇attention!: from the output gradient dO, the primals
+// Q, K, V, the forward output O and its saved softmax statistics (here the row
+// LSE), the input gradients.  With S = scale * Q K^T + mask, P = exp(S - LSE):
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),  delta_i = sum_d dO O,
+//   dQ = scale * dS K,  dK = scale * dS^T Q
+// (delta_i equals sum_j P_ij dP_ij because O = P V).  With GQA a KV head's
+// dK / dV sum over the query heads of its group.
+//
+// Three kernels:
+//   attn_bwd_delta_kernel  delta and the base-2 LSE per query row (HBM-bound);
+//   attn_bwd_dkdv_kernel   one workgroup per (128-key tile, KV head, batch),
+//                          one wave per 32 keys; it walks every query head of
+//                          the group and every 64-row query tile that can see
+//                          its keys, keeping dK^T and dV^T in registers;
+//   attn_bwd_dq_kernel     one workgroup per (128-row query tile, head,
+//                          batch), one wave per 32 rows, walking the 64-key
+//                          tiles its rows can see (the forward's structure).
+// dQ is computed by its own kernel rather than by atomics from the dK/dV
+// kernel: it costs two more contractions per pair but no read-modify-write
+// traffic and gives deterministic results.
+//
+// Contractions on v_mfma_f32_32x32x16_bf16 with the forward's conventions:
+// A operands are rows read from LDS, B operands are per-lane registers, and a
+// product whose result feeds the next contraction as a B operand is formed
+// transposed so that the accumulator already has the B layout; the LDS copies
+// read as A operands of those second contractions (dO^T, Q^T, K^T) keep their
+// inner index in the permuted order the accumulator registers hold it in.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_common.h"
+
+namespace attn {
+
+namespace bwd {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;      // four waves
+constexpr int kKeysPerWave = 32;
+constexpr int kKvTile = 128;       // keys per dK/dV workgroup
+constexpr int kQTile = 64;         // query rows per step of the dK/dV kernel
+constexpr int kDqRows = 128;       // query rows per dQ workgroup
+constexpr int kDqKeys = 64;        // keys per step of the dQ kernel
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, out-of-range reads = 0
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Position of element e of quad q4 of a 16-group in the permuted order of the
+// accumulator registers: quads 1 and 2 trade places.
+__device__ inline int perm16(int q4) {
+  return ((q4 & 1) << 3) | ((q4 >> 1) << 2);
+}
+
+// Row-major tile of R rows x D bf16 (rows padded by 16 bytes) and its
+// transpose D rows x R bf16 in permuted order (rows padded by 16 bytes).
+template <int D, int R>
+struct TileLds {
+  static constexpr int kRow = D * 2 + 16;
+  static constexpr int kBytes = R * kRow;
+  static constexpr int kRowT = R * 2 + 16;
+  static constexpr int kBytesT = D * kRowT;
+};
+
+// Each staging thread holds 4 consecutive rows x 8 d (one 16-byte chunk per
+// row) of an R x D tile; writes them row-major and, if T, transposed.
+template <int D, int R, bool T>
+__device__ inline void stash_rows(char* rowmajor, char* transposed,
+                                  const u32x4_t (&x)[4], int quad, int dch) {
+  using L = TileLds<D, R>;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *(u32x4_t*)(rowmajor + (quad * 4 + i) * L::kRow + dch * 16) = x[i];
+  if constexpr (T) {
+    const int pos = (quad >> 2) * 16 + perm16(quad & 3);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t r0 = x[0][m], r1 = x[1][m], r2 = x[2][m], r3 = x[3][m];
+      u32x2_t even = {__builtin_amdgcn_perm(r1, r0, 0x05040100u),
+                      __builtin_amdgcn_perm(r3, r2, 0x05040100u)};
+      u32x2_t odd = {__builtin_amdgcn_perm(r1, r0, 0x07060302u),
+                     __builtin_amdgcn_perm(r3, r2, 0x07060302u)};
+      const int d = dch * 8 + 2 * m;
+      *(u32x2_t*)(transposed + d * L::kRowT + pos * 2) = even;
+      *(u32x2_t*)(transposed + (d + 1) * L::kRowT + pos * 2) = odd;
+    }
+  }
+}
+
+}  // namespace bwd
+
+using namespace bwd;
+
+// ---------------------------------------------------------------------------
+// delta_i = sum_d dO_id O_id and L2_i = LSE_i * log2(e) (+inf for a row with
+// no allowed key, so that exp2(s - L2) = 0 there)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(
+    const __bf16* __restrict__ dO, const __bf16* __restrict__ O,
+    const float* __restrict__ LSE, float* __restrict__ delta,
+    float* __restrict__ L2, long long rows) {
+  constexpr int TPR = D / 8;  // threads per row, 8 d each
+  const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4_t a = *(const u32x4_t*)(dO + row * D + c * 8);
+    const u32x4_t o = *(const u32x4_t*)(O + row * D + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc += __uint_as_float(a[w] << 16) * __uint_as_float(o[w] << 16);
+      acc += __uint_as_float(a[w] & 0xffff0000u) * __uint_as_float(o[w] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int x = 1; x < TPR; x <<= 1) acc += __shfl_xor(acc, x);
+  if (row < rows && c == 0) {
+    delta[row] = acc;
+    const float l = LSE[row];
+    L2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (128-key tile, KV head, batch)
+// ---------------------------------------------------------------------------
+template <int D>
+struct DkdvLds {
+  using T = TileLds<D, kQTile>;
+  // per stage: Q, Q^T, dO, dO^T, L2 and delta of one 64-row query tile
+  static constexpr int kOffQ = 0;
+  static constexpr int kOffQT = kOffQ + T::kBytes;
+  static constexpr int kOffO = kOffQT + T::kBytesT;
+  static constexpr int kOffOT = kOffO + T::kBytes;
+  static constexpr int kOffL = kOffOT + T::kBytesT;
+  static constexpr int kOffDel = kOffL + kQTile * 4;
+  static constexpr int kStage = kOffDel + kQTile * 4;
+  static constexpr int kTotal = 2 * kStage;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV,
+    const __bf16* __restrict__ dO, const __bf16* __restrict__ Q,
+    const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const float* __restrict__ delta, const float* __restrict__ L2,
+    int B, int H, int Hkv, int Sq, int Sk, int causal, int window,
+    int input_pos, const int32_t* __restrict__ k_lengths, float scale) {
+  using L = DkdvLds<D>;
+  using T = TileLds<D, kQTile>;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lcol = lane & 31;  // key column this lane owns
+  const int half = lane >> 5;
+
+  const int kt = blockIdx.x;  // low keys (the most rows under causal masking) first
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = H / Hkv;
+  const int j0 = kt * kKvTile;
+  const int j1 = min(j0 + kKvTile, Sk);
+  const int kl = k_lengths ? min(max(k_lengths[b], 0), Sk) : Sk;
+  const int kj = j0 + wave * kKeysPerWave + lcol;  // this lane's key
+
+  // K and V rows of my key as B operands (zero past Sk)
+  bf16x8_t kreg[KSTEPS], vreg[KSTEPS];
+  {
+    const size_t base = ((size_t)(b * Hkv + g) * Sk + (kj < Sk ? kj : 0)) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4_t k4 = kj < Sk ? *(const u32x4_t*)(K + base + ks * 16) : u32x4_t{0, 0, 0, 0};
+      u32x4_t v4 = kj < Sk ? *(const u32x4_t*)(V + base + ks * 16) : u32x4_t{0, 0, 0, 0};
+      kreg[ks] = __builtin_bit_cast(bf16x8_t, k4);
+      vreg[ks] = __builtin_bit_cast(bf16x8_t, v4);
+    }
+  }
+
+  f32x16_t dkT[DBLK], dvT[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) dkT[db] = dvT[db] = f32x16_t{};
+
+  // query rows that may see keys [j0, min(j1, kl)): causal needs p >= j0, a
+  // window needs p - window + 1 <= j_last
+  int i_lo = 0, i_hi = Sq;
+  const int jl = min(j1, kl);
+  if (jl <= j0) i_hi = 0;
+  if (causal) i_lo = max(i_lo, j0 - input_pos);
+  if (window > 0) i_hi = min(i_hi, (int)min((long long)jl - 1 + window - input_pos, (long long)Sq));
+  i_lo = max(i_lo, 0);
+  const int qt_lo = i_lo / kQTile;
+  const int qt_hi = i_hi > i_lo ? (i_hi + kQTile - 1) / kQTile : qt_lo;
+  const int nq = qt_hi - qt_lo;
+  const int n_items = nq * G;
+
+  // staging: for D = 128 every thread stages 4 rows x 8 d of Q and of dO; for
+  // D = 64 threads 0-127 stage Q and 128-255 stage dO
+  constexpr int STG_PER = (kQTile / 4) * (D / 8);  // threads per tensor
+  constexpr bool BOTH = STG_PER == kThreads;
+  u32x4_t sq[4], so[4];
+  float sl = 0.f, sd = 0.f;
+  const int st_t = BOTH ? tid : (tid % STG_PER);
+  const int quad = st_t % (kQTile / 4);
+  const int dch = st_t / (kQTile / 4);
+  auto item_rows = [&](int it, int& h, int& i0) {
+    const int hh = it / nq;
+    h = g * G + hh;
+    i0 = (qt_lo + (it - hh * nq)) * kQTile;
+  };
+  auto fetch = [&](int it) {
+    int h, i0;
+    item_rows(it, h, i0);
+    const size_t rb = (size_t)(b * H + h) * Sq;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + quad * 4 + r;
+      const size_t off = (rb + (i < Sq ? i : 0)) * D + dch * 8;
+      if (BOTH || tid < STG_PER)
+        sq[r] = i < Sq ? *(const u32x4_t*)(Q + off) : u32x4_t{0, 0, 0, 0};
+      if (BOTH || tid >= STG_PER)
+        so[r] = i < Sq ? *(const u32x4_t*)(dO + off) : u32x4_t{0, 0, 0, 0};
+    }
+    if (tid < kQTile) {
+      const int i = i0 + tid;
+      sl = i < Sq ? L2[rb + i] : INFINITY;
+      sd = i < Sq ? delta[rb + i] : 0.f;
+    }
+  };
+  auto stash = [&](int buf) {
+    char* st = smem + buf * L::kStage;
+    if (BOTH || tid < STG_PER)
+      stash_rows<D, kQTile, true>(st + L::kOffQ, st + L::kOffQT, sq, quad, dch);
+    if (BOTH || tid >= STG_PER)
+      stash_rows<D, kQTile, true>(st + L::kOffO, st + L::kOffOT, so, quad, dch);
+    if (tid < kQTile) {
+      ((float*)(st + L::kOffL))[tid] = sl;
+      ((float*)(st + L::kOffDel))[tid] = sd;
+    }
+  };
+
+  const float sl2 = scale * kLog2e;
+  if (n_items > 0) {
+    fetch(0);
+    stash(0);
+    __syncthreads();
+  }
+  for (int it = 0; it < n_items; ++it) {
+    if (it + 1 < n_items) fetch(it + 1);
+    const char* st = smem + (it & 1) * L::kStage;
+    int h, i0;
+    item_rows(it, h, i0);
+    // mask per element unless every (row, key) pair of the tile is allowed
+    const int i1 = min(i0 + kQTile, Sq);
+    const KvGeometry geo = kv_geometry(i0, i1, kl, causal, window, input_pos);
+    const bool partial = i1 - i0 < kQTile ||
+                         tile_class(geo, j0, kKvTile) != kTileFull;
+
+    // S and dP (64 queries x 32 keys), two 32-query blocks
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = dp[qb] = f32x16_t{};
+      const char* qrow = st + L::kOffQ + (qb * 32 + lcol) * T::kRow + half * 16;
+      const char* orow = st + L::kOffO + (qb * 32 + lcol) * T::kRow + half * 16;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8_t a = *(const bf16x8_t*)(qrow + ks * 32);
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[ks], s[qb], 0, 0, 0);
+        const bf16x8_t o = *(const bf16x8_t*)(orow + ks * 32);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, vreg[ks], dp[qb], 0, 0, 0);
+      }
+    }
+    // P = exp2(s * scale * log2e - L2), dS = P (dP - delta); lane's queries are
+    // i0 + qb*32 + 8*(r/4) + 4*half + r%4
+    u32x4_t pk[4], dsk[4];  // packed bf16, one 16-query k-step each
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int qo = qb * 32 + r4 * 8 + half * 4;
+        const f32x4_t l4 = *(const f32x4_t*)(st + L::kOffL + qo * 4);
+        const f32x4_t d4 = *(const f32x4_t*)(st + L::kOffDel + qo * 4);
+        float pv[4], dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = r4 * 4 + e;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], sl2, -l4[e]));
+          if (partial) {
+            const int i = i0 + qo + e;
+            const long long d = (long long)input_pos + i - kj;  // p - j
+            const bool ok = kj < kl && i < Sq && (!causal || d >= 0) &&
+                            (window <= 0 || d < window);
+            p = ok ? p : 0.f;
+          }
+          pv[e] = p;
+          dv[e] = p * (dp[qb][r] - d4[e]);
+        }
+        const int kq = qb * 2 + (r4 >> 1);
+        const int w = (r4 & 1) * 2;
+        pk[kq][w] = pack_bf16x2(pv[0], pv[1]);
+        pk[kq][w + 1] = pack_bf16x2(pv[2], pv[3]);
+        dsk[kq][w] = pack_bf16x2(dv[0], dv[1]);
+        dsk[kq][w + 1] = pack_bf16x2(dv[2], dv[3]);
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (d x keys), k over the 64 queries
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const char* ot = st + L::kOffOT + (db * 32 + lcol) * T::kRowT + half * 16;
+      const char* qt = st + L::kOffQT + (db * 32 + lcol) * T::kRowT + half * 16;
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        const bf16x8_t ao = *(const bf16x8_t*)(ot + kq * 32);
+        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ao, __builtin_bit_cast(bf16x8_t, pk[kq]), dvT[db], 0, 0, 0);
+        const bf16x8_t aq = *(const bf16x8_t*)(qt + kq * 32);
+        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            aq, __builtin_bit_cast(bf16x8_t, dsk[kq]), dkT[db], 0, 0, 0);
+      }
+    }
+    if (it + 1 < n_items) stash((it + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- store: lane owns key kj, holds d = db*32 + 8*(r/4) + 4*half + r%4 ----
+  if (kj < Sk) {
+    const size_t base = ((size_t)(b * Hkv + g) * Sk + kj) * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + r4 * 8 + half * 4;
+        u32x2_t wk = {pack_bf16x2(dkT[db][r4 * 4] * scale, dkT[db][r4 * 4 + 1] * scale),
+                      pack_bf16x2(dkT[db][r4 * 4 + 2] * scale, dkT[db][r4 * 4 + 3] * scale)};
+        u32x2_t wv = {pack_bf16x2(dvT[db][r4 * 4], dvT[db][r4 * 4 + 1]),
+                      pack_bf16x2(dvT[db][r4 * 4 + 2], dvT[db][r4 * 4 + 3])};
+        *(u32x2_t*)(dK + base + d) = wk;
+        *(u32x2_t*)(dV + base + d) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (128-row query tile, head, batch)
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqLds {
+  using T = TileLds<D, kDqKeys>;
+  // per stage: K, K^T and V of one 64-key tile
+  static constexpr int kOffK = 0;
+  static constexpr int kOffKT = kOffK + T::kBytes;
+  static constexpr int kOffV = kOffKT + T::kBytesT;
+  static constexpr int kStage = kOffV + T::kBytes;
+  static constexpr int kTotal = 2 * kStage;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dq_kernel(
+    __bf16* __restrict__ dQ, const __bf16* __restrict__ dO,
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+    const __bf16* __restrict__ V, const float* __restrict__ delta,
+    const float* __restrict__ L2, int B, int H, int Hkv, int Sq, int Sk,
+    int causal, int window, int input_pos, const int32_t* __restrict__ k_lengths,
+    float scale) {
+  using L = DqLds<D>;
+  using T = TileLds<D, kDqKeys>;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lrow = lane & 31;
+  const int half = lane >> 5;
+
+  const int nqt = (Sq + kDqRows - 1) / kDqRows;
+  const int qtr = blockIdx.x;
+  const int qt = causal ? nqt - 1 - qtr : qtr;  // heaviest first
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int g = h / (H / Hkv);
+  const int i0 = qt * kDqRows;
+  const int i1 = min(i0 + kDqRows, Sq);
+  const int kl = k_lengths ? min(max(k_lengths[b], 0), Sk) : Sk;
+  const KvGeometry geo = kv_geometry(i0, i1, kl, causal, window, input_pos);
+
+  const int qi = i0 + wave * 32 + lrow;
+  const RowRange rr = row_range(qi, kl, causal, window, input_pos);
+  const size_t rowbase = (size_t)(b * H + h) * Sq;
+  bf16x8_t qreg[KSTEPS], oreg[KSTEPS];
+  {
+    const bool ok = qi < Sq;
+    const size_t off = (rowbase + (ok ? qi : 0)) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4_t q4 = ok ? *(const u32x4_t*)(Q + off + ks * 16) : u32x4_t{0, 0, 0, 0};
+      u32x4_t o4 = ok ? *(const u32x4_t*)(dO + off + ks * 16) : u32x4_t{0, 0, 0, 0};
+      qreg[ks] = __builtin_bit_cast(bf16x8_t, q4);
+      oreg[ks] = __builtin_bit_cast(bf16x8_t, o4);
+    }
+  }
+  const float l2 = qi < Sq ? L2[rowbase + qi] : INFINITY;
+  const float del = qi < Sq ? delta[rowbase + qi] : 0.f;
+
+  f32x16_t dqT[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) dqT[db] = f32x16_t{};
+
+  int kt_first = 0, kt_last = -1;
+  if (geo.any) {
+    kt_first = geo.union_lo / kDqKeys;
+    kt_last = (geo.union_hi - 1) / kDqKeys;
+  }
+  const int nvalid = geo.union_hi - geo.union_lo;
+  const size_t valid_base = ((size_t)(b * Hkv + g) * Sk + geo.union_lo) * D;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(K + valid_base), (short)0, nvalid * D * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(V + valid_base), (short)0, nvalid * D * 2, kRsrcWord3);
+
+  // staging: threads hold 4 keys x 8 d of K (both layouts) and of V
+  constexpr int STG_PER = (kDqKeys / 4) * (D / 8);
+  constexpr bool BOTH = STG_PER == kThreads;
+  const int st_t = BOTH ? tid : (tid % STG_PER);
+  const int quad = st_t % (kDqKeys / 4);
+  const int dch = st_t / (kDqKeys / 4);
+  u32x4_t sk[4], sv[4];
+  auto fetch = [&](int kt) {
+    const int rel0 = kt * kDqKeys - geo.union_lo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int off = ((rel0 + quad * 4 + r) * D + dch * 8) * 2;
+      if (BOTH || tid < STG_PER)
+        sk[r] = __builtin_bit_cast(u32x4_t,
+                                   __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+      if (BOTH || tid >= STG_PER)
+        sv[r] = __builtin_bit_cast(u32x4_t,
+                                   __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+    }
+  };
+  auto stash = [&](int buf) {
+    char* st = smem + buf * L::kStage;
+    if (BOTH || tid < STG_PER)
+      stash_rows<D, kDqKeys, true>(st + L::kOffK, st + L::kOffKT, sk, quad, dch);
+    if (BOTH || tid >= STG_PER)
+      stash_rows<D, kDqKeys, false>(st + L::kOffV, nullptr, sv, quad, dch);
+  };
+
+  const float sl2 = scale * kLog2e;
+  if (kt_first <= kt_last) {
+    fetch(kt_first);
+    stash(0);
+    __syncthreads();
+  }
+  for (int kt = kt_first; kt <= kt_last; ++kt) {
+    const int it = kt - kt_first;
+    if (kt + 1 <= kt_last) fetch(kt + 1);
+    const char* st = smem + (it & 1) * L::kStage;
+    const int j0 = kt * kDqKeys;
+    // S^T and dP^T (64 keys x 32 queries), two 32-key blocks
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = dp[kb] = f32x16_t{};
+      const char* krow = st + L::kOffK + (kb * 32 + lrow) * T::kRow + half * 16;
+      const char* vrow = st + L::kOffV + (kb * 32 + lrow) * T::kRow + half * 16;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8_t a = *(const bf16x8_t*)(krow + ks * 32);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
+        const bf16x8_t v = *(const bf16x8_t*)(vrow + ks * 32);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, oreg[ks], dp[kb], 0, 0, 0);
+      }
+    }
+    // lane's keys: j0 + kb*32 + 8*(r/4) + 4*half + r%4
+    const bool partial = tile_class(geo, j0, kDqKeys) == kTilePartial;
+    const int t_lo = rr.lo - (j0 + half * 4);
+    const unsigned width = (unsigned)max(rr.hi - rr.lo, 0);
+    u32x4_t dsk[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float dv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + e], sl2, -l2));
+          if (partial) {
+            const int c = kb * 32 + ((r + e) >> 2) * 8 + ((r + e) & 3);
+            p = (unsigned)(c - t_lo) < width ? p : 0.f;
+          }
+          dv[e] = p * (dp[kb][r + e] - del);
+        }
+        dsk[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dv[0], dv[1]);
+      }
+    // dQ^T (d x queries) += K^T (d x keys) dS^T (keys x queries)
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const char* arow = st + L::kOffKT + (db * 32 + lrow) * T::kRowT + half * 16;
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        const bf16x8_t a = *(const bf16x8_t*)(arow + kq * 32);
+        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, __builtin_bit_cast(bf16x8_t, dsk[kq]), dqT[db], 0, 0, 0);
+      }
+    }
+    if (kt + 1 <= kt_last) stash((it + 1) & 1);
+    __syncthreads();
+  }
+
+  if (qi < Sq) {
+    __bf16* op = dQ + (rowbase + qi) * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + r4 * 8 + half * 4;
+        u32x2_t w = {pack_bf16x2(dqT[db][r4 * 4] * scale, dqT[db][r4 * 4 + 1] * scale),
+                     pack_bf16x2(dqT[db][r4 * 4 + 2] * scale, dqT[db][r4 * 4 + 3] * scale)};
+        *(u32x2_t*)(op + d) = w;
+      }
+  }
+}
+
+size_t bwd_workspace_bytes(int B, int H, int Sq) {
+  const size_t rows = (size_t)B * H * Sq;
+  return 2 * ((rows * sizeof(float) + 255) / 256 * 256);
+}
+
+template <int D>
+static hipError_t launch_bwd_d(void* dQ, void* dK, void* dV, const void* dO,
+                               const void* Q, const void* K, const void* V,
+                               const void* O, const float* LSE, int B, int H,
+                               int Hkv, int Sq, int Sk, int causal, int window,
+                               int input_pos, const int32_t* k_lengths,
+                               void* ws, hipStream_t stream) {
+  const long long rows = (long long)B * H * Sq;
+  float* delta = (float*)ws;
+  float* L2 = (float*)((char*)ws + ((size_t)rows * sizeof(float) + 255) / 256 * 256);
+  const float scale = 1.f / sqrtf((float)D);
+  constexpr int RPB = 256 / (D / 8);
+  hipError_t e = hipSuccess;
+  if (rows > 0) {
+    hipLaunchKernelGGL(attn_bwd_delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)),
+                       dim3(256), 0, stream, (const __bf16*)dO, (const __bf16*)O, LSE,
+                       delta, L2, rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (Sk > 0) {
+    const int nkt = (Sk + kKvTile - 1) / kKvTile;
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(nkt, Hkv, B), dim3(kThreads), 0,
+                       stream, (__bf16*)dK, (__bf16*)dV, (const __bf16*)dO,
+                       (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V,
+                       (const float*)delta, (const float*)L2, B, H, Hkv, Sq, Sk,
+                       causal, window, input_pos, k_lengths, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (rows == 0) return hipSuccess;
+  const int nqt = (Sq + kDqRows - 1) / kDqRows;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(nqt, H, B), dim3(kThreads), 0,
+                     stream, (__bf16*)dQ, (const __bf16*)dO, (const __bf16*)Q,
+                     (const __bf16*)K, (const __bf16*)V, (const float*)delta,
+                     (const float*)L2, B, H, Hkv, Sq, Sk, causal, window,
+                     input_pos, k_lengths, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(void* dQ, void* dK, void* dV, const void* dO,
+                      const void* Q, const void* K, const void* V,
+                      const void* O, const float* LSE, int B, int H, int Hkv,
+                      int Sq, int Sk, int D, int causal, int window,
+                      int input_pos, const int32_t* k_lengths, void* ws,
+                      hipStream_t stream) {
+  if (D == 64)
+    return launch_bwd_d<64>(dQ, dK, dV, dO, Q, K, V, O, LSE, B, H, Hkv, Sq, Sk,
+                            causal, window, input_pos, k_lengths, ws, stream);
+  return launch_bwd_d<128>(dQ, dK, dV, dO, Q, K, V, O, LSE, B, H, Hkv, Sq, Sk,
+                           causal, window, input_pos, k_lengths, ws, stream);
+}
+
+}  // namespace attn

@@ -38,6 +38,7 @@ def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("attn_fwd", "attn_fwd_f32", "attn_decode", "attn_decode_ws",
               "attn_decode_workspace_bytes", "attn_decode_paged", "attn_fwd_flex",
+              "attn_bwd", "attn_bwd_workspace_bytes",
               "attn_mask_dump",
               "attn_tile_plan",
               "attn_status_string", "attn_version"):
@@ -103,6 +104,24 @@ def test_fwd_flex_argument_errors(lib):
     assert flex(attn.AttnFlex(doc_q=8)) == attn.ATTN_EINVAL
     assert flex(attn.AttnFlex(doc_kv=8)) == attn.ATTN_EINVAL
     assert flex(Sq=0) == attn.ATTN_OK
+
+
+def test_bwd_argument_errors(lib):
+    def bwd(dQ=1, dK=1, dV=1, dO=1, L=1, H=4, Hkv=2, Sq=8, Sk=8, D=128, causal=1, window=0,
+            ws=256, nbytes=1 << 20):
+        return lib.attn_bwd(dQ, dK, dV, dO, 1, 1, 1, 1, L, 1, H, Hkv, Sq, Sk, D, causal,
+                            window, 0, None, ws, nbytes, None)
+    assert bwd(H=3) == attn.ATTN_EINVAL
+    assert bwd(D=96) == attn.ATTN_EUNSUPPORTED
+    assert bwd(causal=0, window=2) == attn.ATTN_EINVAL
+    for k in ("dQ", "dK", "dV", "dO", "L"):
+        assert bwd(**{k: None}) == attn.ATTN_EINVAL, k
+    need = lib.attn_bwd_workspace_bytes(1, 4, 8, 128)
+    assert need == 2 * 256
+    assert bwd(nbytes=need - 1) == attn.ATTN_EINVAL
+    assert bwd(ws=260, nbytes=need) == attn.ATTN_EINVAL
+    assert lib.attn_bwd_workspace_bytes(0, 4, 8, 128) == 0
+    assert bwd(Sq=0, Sk=0) == attn.ATTN_OK
 
 
 def test_decode_argument_errors(lib):

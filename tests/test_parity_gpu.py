@@ -594,3 +594,83 @@ def test_flex_full_size_sampled():
     err = _check_flex(w, O, L, causal=True, heads=heads, rows=rows, softcap=30.0,
                       alibi_slopes=slopes)
     _say(f"  sampled max-abs error {err:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def _bwd_run(w, seed=80):
+    g = torch.Generator().manual_seed(seed)
+    dO = torch.randn(w.q.shape, generator=g).bfloat16()
+    q, k, v, do = (t.to(DEV) for t in (w.q, w.k, w.v, dO))
+    kl = None if w.k_lengths is None else w.k_lengths.to(DEV)
+    O = torch.empty_like(q)
+    L = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    attn.attn_fwd(O, q, k, v, L, w.causal, w.window, w.input_pos, kl)
+    dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    attn.attn_bwd(dQ, dK, dV, do, q, k, v, O, L, w.causal, w.window, w.input_pos, kl)
+    torch.cuda.synchronize()
+    return dO, dQ, dK, dV
+
+
+def _bwd_check(w, dO, dQ, dK, dV, heads=None):
+    kl = None if w.k_lengths is None else w.k_lengths.cpu().numpy()
+    rQ, rK, rV = ora.attn_bwd_ref(_np(w.q), _np(w.k), _np(w.v), _np(dO), w.causal, w.window,
+                                  w.input_pos, kl, heads=heads)
+    errs = {}
+    for name, got, ref in (("dQ", dQ, rQ), ("dK", dK, rK), ("dV", dV, rV)):
+        g = _np(got)
+        sel = ~np.isnan(ref)
+        if name != "dQ" and heads is not None:
+            sel = np.zeros_like(sel)
+            for b, gg in {(b, h // (w.q.shape[1] // w.k.shape[1])) for b, h in heads}:
+                sel[b, gg] = True
+        err = np.max(np.abs(g[sel] - ref[sel]))
+        scale = max(1.0, float(np.max(np.abs(ref[sel]))))
+        errs[name] = (err, scale)
+        # bf16 operands (P, dS) and bf16 outputs: ~2^-8 relative per rounding
+        assert err <= TOL_BF16 * scale, f"{name} max-abs error {err} (scale {scale})"
+    return errs
+
+
+BWD_CASES = [
+    # B, H, Hkv, Sq, Sk, D, causal, window, input_pos, k_lengths
+    (1, 4, 2, 128, 128, 128, True, 0, 0, None),
+    (2, 4, 1, 257, 257, 128, True, 0, 0, None),
+    (1, 2, 2, 300, 300, 128, False, 0, 0, None),
+    (1, 8, 2, 200, 456, 128, True, 128, 256, [456]),
+    (2, 4, 2, 130, 190, 64, True, 0, 60, [190, 100]),
+    (1, 4, 4, 96, 96, 64, False, 0, 0, None),
+    (1, 2, 1, 64, 256, 128, True, 16, 300, [200]),
+    (1, 4, 2, 33, 700, 128, False, 0, 0, [650]),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"-c{int(c[6])}w{c[7]}p{c[8]}")
+def test_bwd_parity(case):
+    B, H, Hkv, Sq, Sk, D, causal, window, ip, kl = case
+    _say(f"bwd {case}")
+    w = wl.prefill_random(B, H, Hkv, Sq, Sk, D, torch.bfloat16, seed=81, causal=causal,
+                          window=window, input_pos=ip, k_lengths=kl)
+    dO, dQ, dK, dV = _bwd_run(w)
+    for t in (dQ, dK, dV):
+        assert torch.isfinite(t.float()).all()
+    errs = _bwd_check(w, dO, dQ, dK, dV)
+    _say("  " + ", ".join(f"{k} {e:.2e}/{s:.1f}" for k, (e, s) in errs.items()))
+
+
+def test_bwd_keys_nobody_sees_get_zero():
+    w = wl.prefill_random(1, 4, 2, 100, 300, 128, torch.bfloat16, seed=82, causal=True,
+                          k_lengths=[200])
+    _, dQ, dK, dV = _bwd_run(w)
+    # keys >= 200 are past k_lengths, keys >= 100 are past every causal row
+    assert torch.all(dK[:, :, 100:] == 0) and torch.all(dV[:, :, 100:] == 0)
+
+
+def test_bwd_full_size_one_kv_group():
+    _say("bwd gqa_causal, KV head 0 of batch 0")
+    w = wl.make("gqa_causal")
+    dO, dQ, dK, dV = _bwd_run(w)
+    errs = _bwd_check(w, dO, dQ, dK, dV, heads=[(0, h) for h in range(4)])
+    _say("  " + ", ".join(f"{k} {e:.2e}/{s:.1f}" for k, (e, s) in errs.items()))
