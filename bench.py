@@ -13,7 +13,7 @@ O) is reported beside it.  The window/offset and clustered-image workloads are
 timed too, as extra lines of context, and so is the same decode batch stored
 in a paged serving cache (block size 16, shuffled physical blocks;
 attn_decode_paged), and the causal GQA prefill with soft-capping and ALiBi
-(attn_fwd_flex).  ``cpu_baseline`` times the fp64 oracle
+(attn_fwd_flex), and its backward (attn_bwd).  ``cpu_baseline`` times the fp64 oracle
 on the host on a bounded sample (whole heads) of the prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -185,6 +185,18 @@ def main():
                                paged.lengths, paged.n_splits, workspace=ws)
 
     Of, Lf = torch.empty_like(pre.q), torch.empty_like(LSE)
+    # backward of the causal GQA prefill (dO seeded, O / LSE from attn_fwd)
+    if not args.no_extra:
+        gb = torch.Generator().manual_seed(8)
+        dO = torch.randn(pre.q.shape, generator=gb).bfloat16().to(dev)
+        Ob, Lb = torch.empty_like(pre.q), torch.empty_like(LSE)
+        attn.attn_fwd(Ob, pre.q, pre.k, pre.v, Lb, True)
+        dQ, dK, dV = torch.empty_like(pre.q), torch.empty_like(pre.k), torch.empty_like(pre.v)
+        bws = torch.empty(attn.attn_bwd_workspace_bytes(B, H, Sq, D), dtype=torch.uint8,
+                          device=dev)
+
+    def run_bwd():
+        attn.attn_bwd(dQ, dK, dV, dO, pre.q, pre.k, pre.v, Ob, Lb, True, workspace=bws)
 
     def run_flex():
         attn.attn_fwd_flex(Of, pre.q, pre.k, pre.v, Lf, True, softcap=30.0,
@@ -192,7 +204,7 @@ def main():
 
     names = ["prefill", "decode"] + list(extra) + (["decode_paged"] if paged is not None else [])
     if not args.no_extra:
-        names.append("flex_softcap_alibi")
+        names += ["flex_softcap_alibi", "backward"]
     ev = {n: [] for n in names}
 
     def step(record):
@@ -209,6 +221,8 @@ def main():
                 run_paged()
             elif n == "flex_softcap_alibi":
                 run_flex()
+            elif n == "backward":
+                run_bwd()
             else:
                 run_prefill(extra[n], *ext_out[n])
             if record:
@@ -280,6 +294,14 @@ def main():
             "ms": round(ms["flex_softcap_alibi"], 4), "TFLOP/s": round(tf, 2),
             "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": fl,
             "config": "gqa_causal prefill with soft-cap 30 and ALiBi slopes (attn_fwd_flex)"}
+    if "backward" in ms:
+        bf = fl * 5 // 2  # five contractions against the forward's two
+        tf = bf / (ms["backward"] * 1e-3) / 1e12
+        out["backward"] = {
+            "ms": round(ms["backward"], 4), "TFLOP/s": round(tf, 2),
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": bf,
+            "config": "attn_bwd of the gqa_causal prefill (delta + dK/dV + dQ kernels); "
+                      "flops = 2.5 x forward (S, dP, dV, dK, dQ)"}
     if paged is not None:
         pb = decode_bytes(paged)
         gbs = pb / (ms["decode_paged"] * 1e-3) / 1e9

@@ -263,8 +263,17 @@ void attn_bwd_dkdv_kernel(
     stash(0);
     __syncthreads();
   }
+  // query rows my key may be seen by: [r_lo, r_hi) (none past k_lengths)
+  int r_lo = 0, r_hi = 0;
+  if (kj < kl) {
+    const long long lo = causal ? (long long)kj - input_pos : 0;            // p >= j
+    const long long hi = window > 0 ? (long long)kj + window - input_pos : Sq;  // p < j + w
+    r_lo = clamp_i64(lo, 0, Sq);
+    r_hi = clamp_i64(hi, 0, Sq);
+  }
+  const unsigned r_width = (unsigned)max(r_hi - r_lo, 0);
+
   for (int it = 0; it < n_items; ++it) {
-    if (it + 1 < n_items) fetch(it + 1);
     const char* st = smem + (it & 1) * L::kStage;
     int h, i0;
     item_rows(it, h, i0);
@@ -274,21 +283,28 @@ void attn_bwd_dkdv_kernel(
     const bool partial = i1 - i0 < kQTile ||
                          tile_class(geo, j0, kKvTile) != kTileFull;
 
-    // S and dP (64 queries x 32 keys), two 32-query blocks
+    // S and dP (64 queries x 32 keys), two 32-query blocks; each block's
+    // operand rows are read before its MFMAs so the reads overlap
     f32x16_t s[2], dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = dp[qb] = f32x16_t{};
       const char* qrow = st + L::kOffQ + (qb * 32 + lcol) * T::kRow + half * 16;
       const char* orow = st + L::kOffO + (qb * 32 + lcol) * T::kRow + half * 16;
+      bf16x8_t aq[KSTEPS], ao[KSTEPS];
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8_t a = *(const bf16x8_t*)(qrow + ks * 32);
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[ks], s[qb], 0, 0, 0);
-        const bf16x8_t o = *(const bf16x8_t*)(orow + ks * 32);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, vreg[ks], dp[qb], 0, 0, 0);
+        aq[ks] = *(const bf16x8_t*)(qrow + ks * 32);
+        ao[ks] = *(const bf16x8_t*)(orow + ks * 32);
+      }
+      s[qb] = dp[qb] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], kreg[ks], s[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[ks], vreg[ks], dp[qb], 0, 0, 0);
       }
     }
+    // the next tile's rows are requested now and land during the rest
+    if (it + 1 < n_items) fetch(it + 1);
     // P = exp2(s * scale * log2e - L2), dS = P (dP - delta); lane's queries are
     // i0 + qb*32 + 8*(r/4) + 4*half + r%4
     u32x4_t pk[4], dsk[4];  // packed bf16, one 16-query k-step each
@@ -299,18 +315,13 @@ void attn_bwd_dkdv_kernel(
         const int qo = qb * 32 + r4 * 8 + half * 4;
         const f32x4_t l4 = *(const f32x4_t*)(st + L::kOffL + qo * 4);
         const f32x4_t d4 = *(const f32x4_t*)(st + L::kOffDel + qo * 4);
+        const int t0 = i0 + qo - r_lo;
         float pv[4], dv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = r4 * 4 + e;
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], sl2, -l4[e]));
-          if (partial) {
-            const int i = i0 + qo + e;
-            const long long d = (long long)input_pos + i - kj;  // p - j
-            const bool ok = kj < kl && i < Sq && (!causal || d >= 0) &&
-                            (window <= 0 || d < window);
-            p = ok ? p : 0.f;
-          }
+          if (partial) p = (unsigned)(t0 + e) < r_width ? p : 0.f;
           pv[e] = p;
           dv[e] = p * (dp[qb][r] - d4[e]);
         }
@@ -327,14 +338,18 @@ void attn_bwd_dkdv_kernel(
     for (int db = 0; db < DBLK; ++db) {
       const char* ot = st + L::kOffOT + (db * 32 + lcol) * T::kRowT + half * 16;
       const char* qt = st + L::kOffQT + (db * 32 + lcol) * T::kRowT + half * 16;
+      bf16x8_t ao[4], aq[4];
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) {
-        const bf16x8_t ao = *(const bf16x8_t*)(ot + kq * 32);
+        ao[kq] = *(const bf16x8_t*)(ot + kq * 32);
+        aq[kq] = *(const bf16x8_t*)(qt + kq * 32);
+      }
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
         dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            ao, __builtin_bit_cast(bf16x8_t, pk[kq]), dvT[db], 0, 0, 0);
-        const bf16x8_t aq = *(const bf16x8_t*)(qt + kq * 32);
+            ao[kq], __builtin_bit_cast(bf16x8_t, pk[kq]), dvT[db], 0, 0, 0);
         dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            aq, __builtin_bit_cast(bf16x8_t, dsk[kq]), dkT[db], 0, 0, 0);
+            aq[kq], __builtin_bit_cast(bf16x8_t, dsk[kq]), dkT[db], 0, 0, 0);
       }
     }
     if (it + 1 < n_items) stash((it + 1) & 1);
@@ -475,24 +490,29 @@ void attn_bwd_dq_kernel(
   }
   for (int kt = kt_first; kt <= kt_last; ++kt) {
     const int it = kt - kt_first;
-    if (kt + 1 <= kt_last) fetch(kt + 1);
     const char* st = smem + (it & 1) * L::kStage;
     const int j0 = kt * kDqKeys;
     // S^T and dP^T (64 keys x 32 queries), two 32-key blocks
     f32x16_t s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = dp[kb] = f32x16_t{};
       const char* krow = st + L::kOffK + (kb * 32 + lrow) * T::kRow + half * 16;
       const char* vrow = st + L::kOffV + (kb * 32 + lrow) * T::kRow + half * 16;
+      bf16x8_t ak[KSTEPS], av[KSTEPS];
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8_t a = *(const bf16x8_t*)(krow + ks * 32);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
-        const bf16x8_t v = *(const bf16x8_t*)(vrow + ks * 32);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, oreg[ks], dp[kb], 0, 0, 0);
+        ak[ks] = *(const bf16x8_t*)(krow + ks * 32);
+        av[ks] = *(const bf16x8_t*)(vrow + ks * 32);
+      }
+      s[kb] = dp[kb] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qreg[ks], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks], oreg[ks], dp[kb], 0, 0, 0);
       }
     }
+    // the next tile's keys are requested now and land during the rest
+    if (kt + 1 <= kt_last) fetch(kt + 1);
     // lane's keys: j0 + kb*32 + 8*(r/4) + 4*half + r%4
     const bool partial = tile_class(geo, j0, kDqKeys) == kTilePartial;
     const int t_lo = rr.lo - (j0 + half * 4);
@@ -518,12 +538,13 @@ void attn_bwd_dq_kernel(
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
       const char* arow = st + L::kOffKT + (db * 32 + lrow) * T::kRowT + half * 16;
+      bf16x8_t a[4];
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        const bf16x8_t a = *(const bf16x8_t*)(arow + kq * 32);
+      for (int kq = 0; kq < 4; ++kq) a[kq] = *(const bf16x8_t*)(arow + kq * 32);
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq)
         dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            a, __builtin_bit_cast(bf16x8_t, dsk[kq]), dqT[db], 0, 0, 0);
-      }
+            a[kq], __builtin_bit_cast(bf16x8_t, dsk[kq]), dqT[db], 0, 0, 0);
     }
     if (kt + 1 <= kt_last) stash((it + 1) & 1);
     __syncthreads();
