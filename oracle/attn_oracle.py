@@ -38,6 +38,9 @@ plainly, in float64 NumPy:
 * the flex variants: ``SoftCapScore``, ``AliBiScore``, ``BiasScore``,
   ``PrefixMask`` / ``prefix_lm``, ``DocumentMask`` and ``q_lengths``
   (Tylo.jl "Primitives", ``flex_attention!`` and its mods);
+* block-sparse prefill: centroid / radius-bounded (RBS) and min/max block
+  scores, relative and top-k block masks, attention on the kept blocks
+  (mlx-arsenal "Radius-bounded block scores (RBS)");
 * the paged KV cache of a serving engine: a (num_blocks, block_size,
   num_kv_heads, head_size) cache addressed through per-sequence block tables
   and ``seq_lens`` (vllm_mlx.attention, ``get_kv_cache_shape`` and
@@ -61,6 +64,9 @@ repository's design notes):
   absolute positions; the bias and doc_q are indexed by the local query row;
   a prefix ORs keys j < prefix into the causal / window set; rows at or past
   q_lengths[b] attend to nothing;
+* block scores: radius quantiles per KV head with linear interpolation; a
+  ragged last block summarises its existing keys; top-k ties go to the lower
+  block index;
 * block tables: entry i of a sequence's row names the physical block holding
   its tokens [i * block_size, (i + 1) * block_size); a paged length is clamped
   to [0, max_blocks * block_size].
@@ -496,6 +502,163 @@ def flex_ref(Q, K, V, causal: bool = False, window: int = 0, input_pos: int = 0,
             P, M, L = softmax_stats(s)
             O[b, h, r] = combine(P, V[b, g])
             LSE[b, h, r] = lse_from_stats(M, L)
+    return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# block-sparse prefill: block-score estimators, block masks, masked attention
+# ---------------------------------------------------------------------------
+
+def key_block_stats(k: np.ndarray, block_size: int):
+    """Per key block of k (Sk, D): centroid c_b, radius r_b = max ||k - c_b||_2,
+    and the element-wise min / max (mlx-arsenal "Radius-bounded block scores":
+    centroid summary, RBS radius, SPADE's element-wise min/max box).  The last
+    block holds the remaining keys."""
+    k = np.asarray(k, dtype=np.float64)
+    Sk = k.shape[0]
+    nb = -(-Sk // block_size)
+    c = np.empty((nb, k.shape[1]))
+    r = np.empty(nb)
+    lo = np.empty((nb, k.shape[1]))
+    hi = np.empty((nb, k.shape[1]))
+    for b in range(nb):
+        blk = k[b * block_size:(b + 1) * block_size]
+        c[b] = blk.mean(axis=0)
+        r[b] = np.sqrt(((blk - c[b]) ** 2).sum(axis=1)).max()
+        lo[b] = blk.min(axis=0)
+        hi[b] = blk.max(axis=0)
+    return c, r, lo, hi
+
+
+def radius_weights(r: np.ndarray, low: float = 0.5, high: float = 0.9) -> np.ndarray:
+    """beta_b = clip((r_b - r_low) / (r_high - r_low), 0, 1) with r_low / r_high the
+    `low` / `high` quantiles (linear interpolation) of one head's block radii; when
+    the two coincide, beta_b = 1 for blocks strictly wider than r_low, else 0."""
+    r_low = float(np.quantile(r, low))
+    r_high = float(np.quantile(r, high))
+    if r_high == r_low:
+        return (r > r_low).astype(np.float64)
+    return np.clip((r - r_low) / (r_high - r_low), 0.0, 1.0)
+
+
+def _block_lse(ell: np.ndarray, block_size: int) -> np.ndarray:
+    """Log of the sum of exp over each query block's tokens: ell (Sq, nk) -> (nq, nk)."""
+    Sq = ell.shape[0]
+    nq = -(-Sq // block_size)
+    out = np.empty((nq, ell.shape[1]))
+    for a in range(nq):
+        rows = ell[a * block_size:(a + 1) * block_size]
+        m = rows.max(axis=0)
+        out[a] = m + np.log(np.exp(rows - m).sum(axis=0))
+    return out
+
+
+def rbs_block_scores_ref(Q, K, block_size: int = 64, low: float = 0.5, high: float = 0.9):
+    """Radius-bounded block scores (mlx-arsenal "Radius-bounded block scores (RBS)").
+
+    Per query token q and key block b: base = q.c_b / sqrt(D) and rescue =
+    (q.c_b + ||q|| r_b beta_b) / sqrt(D); each block score is the log of the sum of
+    exp over the query block's tokens.  Radii quantiles are taken per KV head.
+    Q (B, H, Sq, D), K (B, Hkv, Sk, D); returns (base, rescue) (B, H, nq, nk).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    B, H, Sq, D = Q.shape
+    Hkv = K.shape[1]
+    G = H // Hkv
+    nq, nk = -(-Sq // block_size), -(-K.shape[2] // block_size)
+    base = np.empty((B, H, nq, nk))
+    rescue = np.empty((B, H, nq, nk))
+    for b in range(B):
+        for g in range(Hkv):
+            c, r, _, _ = key_block_stats(K[b, g], block_size)
+            beta = radius_weights(r, low, high)
+            for h in range(g * G, (g + 1) * G):
+                qc = Q[b, h] @ c.T
+                qn = np.sqrt((Q[b, h] ** 2).sum(axis=1))[:, None]
+                base[b, h] = _block_lse(qc / math.sqrt(D), block_size)
+                rescue[b, h] = _block_lse((qc + qn * (r * beta)[None, :]) / math.sqrt(D),
+                                          block_size)
+    return base, rescue
+
+
+def minmax_block_scores_ref(Q, K, block_size: int = 64):
+    """SPADE-style box bound: per query token, sum_d max(q_d lo_bd, q_d hi_bd) /
+    sqrt(D) bounds q.k / sqrt(D) for every key of block b; block score = log-sum-exp
+    over the query block's tokens.  Returns (B, H, nq, nk)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    B, H, Sq, D = Q.shape
+    Hkv = K.shape[1]
+    G = H // Hkv
+    nq, nk = -(-Sq // block_size), -(-K.shape[2] // block_size)
+    out = np.empty((B, H, nq, nk))
+    for b in range(B):
+        for g in range(Hkv):
+            _, _, lo, hi = key_block_stats(K[b, g], block_size)
+            for h in range(g * G, (g + 1) * G):
+                q = Q[b, h][:, None, :]
+                bound = np.maximum(q * lo[None], q * hi[None]).sum(axis=2)
+                out[b, h] = _block_lse(bound / math.sqrt(D), block_size)
+    return out
+
+
+def relative_block_mask_ref(scores, alpha: float) -> np.ndarray:
+    """Keep the blocks whose exp(score) is at least alpha times the row maximum
+    (mlx-arsenal ``relative_block_mask``), i.e. score >= max + ln(alpha)."""
+    s = np.asarray(scores, dtype=np.float64)
+    return s >= s.max(axis=-1, keepdims=True) + math.log(alpha)
+
+
+def top_k_block_mask_ref(scores, k: int) -> np.ndarray:
+    """Keep the k highest-scoring blocks of each row (``top_k_block_mask``); equal
+    scores are ranked by block index, lower first."""
+    s = np.asarray(scores, dtype=np.float64)
+    keep = np.zeros(s.shape, dtype=bool)
+    flat = s.reshape(-1, s.shape[-1])
+    kf = keep.reshape(-1, s.shape[-1])
+    for row in range(flat.shape[0]):
+        order = sorted(range(flat.shape[1]), key=lambda j: (-flat[row, j], j))
+        kf[row, order[:k]] = True
+    return keep
+
+
+def band_block_mask_ref(nq: int, nk: int, diagonal: int) -> np.ndarray:
+    """Forced blocks |row - col| < diagonal (the recipe's band)."""
+    a = np.arange(nq)[:, None]
+    c = np.arange(nk)[None, :]
+    return np.abs(a - c) < diagonal
+
+
+def block_sparse_attn_ref(Q, K, V, keep, block_size: int = 64, causal: bool = False,
+                          window: int = 0, input_pos: int = 0, k_lengths=None,
+                          heads=None, rows=None):
+    """Attention restricted to the kept (query block, key block) pairs of ``keep``
+    (B, H, nq, nk), together with the causal / window / k_lengths mask: a pair is
+    allowed iff both allow it (the block mask expanded to tokens)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, Sq, D = Q.shape
+    _, Hkv, Sk, _ = K.shape
+    G = H // Hkv
+    scale = 1.0 / math.sqrt(D)
+    keep = np.asarray(keep, dtype=bool)
+    O = np.full((B, H, Sq, V.shape[3]), np.nan)
+    LSE = np.full((B, H, Sq), np.nan)
+    row_idx = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    tok_q = row_idx // block_size
+    tok_k = np.arange(Sk) // block_size
+    for b, h in pairs:
+        kl = None if k_lengths is None else int(k_lengths[b])
+        ok = allowed_mask(Sq, Sk, causal, window, input_pos, kl)[row_idx]
+        ok = ok & keep[b, h][tok_q][:, tok_k]
+        g = h // G
+        s = apply_mask(scores(Q[b, h, row_idx], K[b, g], scale), ok)
+        P, M, L = softmax_stats(s)
+        O[b, h, row_idx] = combine(P, V[b, g])
+        LSE[b, h, row_idx] = lse_from_stats(M, L)
     return O, LSE
 
 

@@ -885,3 +885,193 @@ def test_planted_bwd_mistakes(monkeypatch):
     monkeypatch.setattr(ora, "scores", lambda q, k, scale: real(q, k, 1.0))
     with pytest.raises(AssertionError):
         test_bwd_matches_torch_autograd()
+
+
+# ---------------------------------------------------------------------------
+# block-sparse prefill: estimators, block masks, masked attention
+# ---------------------------------------------------------------------------
+
+def test_key_block_stats_bruteforce():
+    rng = np.random.default_rng(90)
+    k = rng.standard_normal((11, 3))
+    c, r, lo, hi = ora.key_block_stats(k, 4)
+    assert c.shape == (3, 3)
+    for b, rows in enumerate([k[0:4], k[4:8], k[8:11]]):
+        for d in range(3):
+            assert abs(c[b, d] - math.fsum(rows[:, d]) / len(rows)) < 1e-15
+            assert lo[b, d] == min(rows[:, d]) and hi[b, d] == max(rows[:, d])
+        assert abs(r[b] - max(math.dist(x, c[b]) for x in rows)) < 1e-14
+
+
+def test_radius_weights_hand_worked():
+    # quantiles of [1..5]: median 3, 90th percentile 4.6 (linear interpolation)
+    np.testing.assert_allclose(ora.radius_weights(np.array([1., 2., 3., 4., 5.])),
+                               [0, 0, 0, 0.625, 1], atol=1e-15)
+    # equal quantiles: only blocks strictly wider than r_low get the bound
+    np.testing.assert_array_equal(ora.radius_weights(np.array([2., 2., 2., 2.])), [0, 0, 0, 0])
+    np.testing.assert_array_equal(ora.radius_weights(np.array([1., 2., 2., 2., 2.]), 0.5, 0.6),
+                                  [0, 0, 0, 0, 0])
+
+
+def _exact_block_scores(Q, K, bs):
+    """lse over a query block's tokens of the true max_k q.k/sqrt(D) in the key block."""
+    B, H, Sq, D = Q.shape
+    Hkv, Sk = K.shape[1], K.shape[2]
+    nq, nk = -(-Sq // bs), -(-Sk // bs)
+    out = np.empty((B, H, nq, nk))
+    for b in range(B):
+        for h in range(H):
+            s = Q[b, h] @ K[b, h // (H // Hkv)].T / math.sqrt(D)
+            for a in range(nq):
+                for c in range(nk):
+                    m = s[a * bs:(a + 1) * bs, c * bs:(c + 1) * bs].max(axis=1)
+                    out[b, h, a, c] = math.log(math.fsum(math.exp(x) for x in m))
+    return out
+
+
+def test_rbs_scores_mpmath_and_bounds():
+    rng = np.random.default_rng(91)
+    B, H, Hkv, Sq, Sk, D, bs = 1, 2, 1, 6, 9, 3, 4
+    Q = rng.standard_normal((B, H, Sq, D))
+    K = rng.standard_normal((B, Hkv, Sk, D))
+    base, rescue = ora.rbs_block_scores_ref(Q, K, bs)
+    c, r, _, _ = ora.key_block_stats(K[0, 0], bs)
+    beta = ora.radius_weights(r)
+    mpmath.mp.dps = 30
+    for h in range(H):
+        for a in range(2):
+            for blk in range(3):
+                tb, tr = [], []
+                for i in range(a * bs, min((a + 1) * bs, Sq)):
+                    q = [mpmath.mpf(x) for x in Q[0, h, i]]
+                    qc = mpmath.fsum(q[d] * mpmath.mpf(c[blk, d]) for d in range(D))
+                    qn = mpmath.sqrt(mpmath.fsum(x * x for x in q))
+                    tb.append(mpmath.exp(qc / mpmath.sqrt(D)))
+                    tr.append(mpmath.exp((qc + qn * mpmath.mpf(r[blk] * beta[blk])) / mpmath.sqrt(D)))
+                assert abs(float(mpmath.log(mpmath.fsum(tb))) - base[0, h, a, blk]) < 1e-12
+                assert abs(float(mpmath.log(mpmath.fsum(tr))) - rescue[0, h, a, blk]) < 1e-12
+    assert np.all(rescue >= base - 1e-12)
+    # with the full radius (beta = 1) the rescue score bounds the true block score
+    exact = _exact_block_scores(Q, K, bs)
+    full = beta == 1
+    assert full.any()
+    assert np.all(rescue[..., full] >= exact[..., full] - 1e-12)
+
+
+def test_minmax_scores_bound_and_single_key_blocks():
+    rng = np.random.default_rng(92)
+    Q = rng.standard_normal((1, 2, 10, 4))
+    K = rng.standard_normal((1, 2, 13, 4))
+    mm = ora.minmax_block_scores_ref(Q, K, 4)
+    assert np.all(mm >= _exact_block_scores(Q, K, 4) - 1e-12)
+    # one key per block: the box is a point, the bound is exact
+    np.testing.assert_allclose(ora.minmax_block_scores_ref(Q, K, 1),
+                               _exact_block_scores(Q, K, 1), atol=1e-12)
+
+
+def test_relative_and_topk_masks_hand_worked():
+    s = np.array([[0.0, -1.0, -2.0, -1.5], [3.0, 1.0, 3.0, 2.0]])
+    # ln 0.22 = -1.514: keep scores >= max - 1.514
+    np.testing.assert_array_equal(ora.relative_block_mask_ref(s, 0.22),
+                                  [[True, True, False, True], [True, False, True, True]])
+    np.testing.assert_array_equal(ora.top_k_block_mask_ref(s, 2),
+                                  [[True, True, False, False], [True, False, True, False]])
+    np.testing.assert_array_equal(ora.top_k_block_mask_ref(np.ones((1, 4)), 2),
+                                  [[True, True, False, False]])
+    np.testing.assert_array_equal(ora.band_block_mask_ref(3, 4, 1),
+                                  [[1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 1, 0]])
+
+
+def test_block_sparse_attention_vs_torch_and_special_cases():
+    rng = np.random.default_rng(93)
+    B, H, Hkv, S, D, bs = 1, 4, 2, 20, 8, 4
+    Q = rng.standard_normal((B, H, S, D))
+    K = rng.standard_normal((B, Hkv, S, D))
+    V = rng.standard_normal((B, Hkv, S, D))
+    nb = S // bs
+    keep = rng.random((B, H, nb, nb)) < 0.5
+    keep[:, :, np.arange(nb), np.arange(nb)] = True        # diagonal kept
+    keep[0, 1, 2] = False                                  # a row block with no key
+    O, L = ora.block_sparse_attn_ref(Q, K, V, keep, bs, causal=True)
+    tok = np.repeat(np.repeat(keep, bs, axis=2), bs, axis=3)
+    ok = tok & np.tril(np.ones((S, S), dtype=bool))
+    qt, kt, vt = (torch.from_numpy(x) for x in (Q, np.repeat(K, 2, axis=1), np.repeat(V, 2, axis=1)))
+    Ot = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(ok)).numpy()
+    has = ok.any(axis=3)
+    np.testing.assert_allclose(O[has], Ot[has], atol=1e-12)
+    assert np.all(O[~has] == 0) and np.all(np.isneginf(L[~has]))
+    assert (~has[0, 1, 8:12]).all()
+    # keeping every block is plain attention
+    Oa, La = ora.block_sparse_attn_ref(Q, K, V, np.ones_like(keep), bs, causal=True)
+    Or, Lr = ora.attn_ref(Q, K, V, True)
+    np.testing.assert_array_equal(Oa, Or)
+
+
+def _bs_pins_pass():
+    checks = [test_key_block_stats_bruteforce, test_radius_weights_hand_worked,
+              test_rbs_scores_mpmath_and_bounds, test_minmax_scores_bound_and_single_key_blocks,
+              test_relative_and_topk_masks_hand_worked,
+              test_block_sparse_attention_vs_torch_and_special_cases]
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError, TypeError):
+            return False
+    return True
+
+
+ORIG_STATS = ora.key_block_stats
+ORIG_RW = ora.radius_weights
+ORIG_REL = ora.relative_block_mask_ref
+ORIG_TOPK = ora.top_k_block_mask_ref
+
+
+def _mut_stats_sum(k, bs):
+    c, r, lo, hi = ORIG_STATS(k, bs)
+    return c * bs, r, lo, hi
+
+
+def _mut_stats_min_radius(k, bs):
+    k = np.asarray(k, dtype=np.float64)
+    c, r, lo, hi = ORIG_STATS(k, bs)
+    r = np.array([np.sqrt(((k[b * bs:(b + 1) * bs] - c[b]) ** 2).sum(axis=1)).min()
+                  for b in range(len(r))])
+    return c, r, lo, hi
+
+
+def _mut_rw_swapped(r, low=0.5, high=0.9):
+    return ORIG_RW(r, high, low)
+
+
+def _mut_rel_alpha(scores, alpha):
+    s = np.asarray(scores, dtype=np.float64)
+    return s >= s.max(axis=-1, keepdims=True) + alpha
+
+
+def _mut_topk_ties(scores, k):
+    s = np.asarray(scores, dtype=np.float64)
+    return ORIG_TOPK(s[..., ::-1], k)[..., ::-1]
+
+
+@pytest.mark.parametrize("target,mutant", [
+    ("key_block_stats", _mut_stats_sum),
+    ("key_block_stats", _mut_stats_min_radius),
+    ("radius_weights", _mut_rw_swapped),
+    ("relative_block_mask_ref", _mut_rel_alpha),
+    ("top_k_block_mask_ref", _mut_topk_ties),
+])
+def test_planted_block_sparse_mistakes(monkeypatch, target, mutant):
+    assert _bs_pins_pass()
+    monkeypatch.setattr(ora, target, mutant)
+    assert not _bs_pins_pass(), f"no pin caught the planted mistake in {target}"
+
+
+def test_planted_block_sparse_attention_mistake(monkeypatch):
+    real = ora.block_sparse_attn_ref
+
+    def transposed(Q, K, V, keep, *a, **kw):
+        return real(Q, K, V, np.swapaxes(np.asarray(keep), -1, -2), *a, **kw)
+
+    monkeypatch.setattr(ora, "block_sparse_attn_ref", transposed)
+    with pytest.raises(AssertionError):
+        test_block_sparse_attention_vs_torch_and_special_cases()
