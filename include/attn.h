@@ -180,6 +180,70 @@ int attn_bwd(void* dQ, void* dK, void* dV, const void* dO, const void* Q,
              int window, int input_pos, const int32_t* k_lengths,
              void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ---- block-sparse prefill (mlx-arsenal "Radius-bounded block scores (RBS)")
+ * Blocks are ATTN_BLOCK tokens on both sides; a block mask is uint8
+ * (B, H, nqb, nkb) with nqb = ceil(Sq / ATTN_BLOCK), nkb = ceil(Sk /
+ * ATTN_BLOCK), nonzero = keep. */
+#define ATTN_BLOCK 64
+#define ATTN_SPARSE_MAX_KEY_BLOCKS 2048
+#define ATTN_BLOCK_SCORES_RBS 0
+#define ATTN_BLOCK_SCORES_MINMAX 1
+#define ATTN_BLOCK_MASK_RELATIVE 0
+#define ATTN_BLOCK_MASK_TOPK 1
+#define ATTN_BLOCK_MASK_BAND 2
+
+/* Scratch bytes attn_block_scores needs (host-only); 0 for invalid sizes. */
+size_t attn_block_scores_workspace_bytes(int B, int Hkv, int Sk, int D);
+
+/* Block scores from bf16 Q (B, H, Sq, D) and K (B, Hkv, Sk, D), float32 out
+ * (B, H, nqb, nkb): for each query token and key block a logit, then the log
+ * of the sum of exp over the query block's tokens.
+ *   kind ATTN_BLOCK_SCORES_RBS: base = q.c / sqrt(D) (c the key block's
+ *     centroid) and, if `rescue` is not NULL, rescue = (q.c + ||q|| r beta) /
+ *     sqrt(D) with r the block radius max ||k - c|| and beta = clip((r - r_lo)
+ *     / (r_hi - r_lo), 0, 1), r_lo / r_hi the `low` / `high` quantiles (linear
+ *     interpolation) of the KV head's block radii (beta = [r > r_lo] when they
+ *     coincide); the page uses low = 0.5, high = 0.9;
+ *   kind ATTN_BLOCK_SCORES_MINMAX: base = sum_d max(q_d lo_d, q_d hi_d) /
+ *     sqrt(D) (element-wise min / max of the key block), rescue unused.
+ * workspace: NULL = allocated stream-ordered, else >=
+ * attn_block_scores_workspace_bytes bytes, 256-byte aligned.  Errors as
+ * attn_fwd; ATTN_EUNSUPPORTED past 4096 key blocks.  Defined by:
+ * mlx-arsenal "Radius-bounded block scores (RBS)" (the idea, the formulas,
+ * radius_bounded_block_scores, the min/max box bound). */
+int attn_block_scores(float* base, float* rescue, const void* Q, const void* K,
+                      int B, int H, int Hkv, int Sq, int Sk, int D, int kind,
+                      float low, float high, void* workspace, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Block mask rows from block scores: `rows` = B * H * nqb rows of nkb entries.
+ *   mode ATTN_BLOCK_MASK_RELATIVE: keep score >= row max + ln(alpha), alpha in
+ *     (0, 1] (relative_block_mask: within alpha of the row maximum);
+ *   mode ATTN_BLOCK_MASK_TOPK: keep the k best of each row, ties to the lower
+ *     block index (top_k_block_mask);
+ *   mode ATTN_BLOCK_MASK_BAND: keep |row block - key block| < diagonal (the
+ *     recipe's forced band; `scores` may be NULL);
+ * accumulate != 0 ORs into `keep` instead of overwriting (the recipe's union
+ * of branches).  Defined by: mlx-arsenal "Radius-bounded block scores (RBS)",
+ * relative_block_mask, top_k_block_mask and the rbs_block_mask recipe. */
+int attn_block_mask(uint8_t* keep, const float* scores, int rows, int nqb,
+                    int nkb, int mode, float alpha, int k, int diagonal,
+                    int accumulate, hipStream_t stream);
+
+/* attn_fwd restricted to the kept blocks of `keep` (B, H, nqb, nkb) uint8, on
+ * top of the causal / window / k_lengths mask (a pair counts iff both allow
+ * it).  Key tiles no row block of a 256-row workgroup keeps are never read.
+ * A row whose blocks keep nothing gets O = 0, LSE = -inf.  ATTN_EUNSUPPORTED
+ * past ATTN_SPARSE_MAX_KEY_BLOCKS key blocks.  Defined by: mlx-arsenal
+ * "Radius-bounded block scores (RBS)" (the block mask expanded to tokens);
+ * Tylo.jl "Primitives", flex_attention! block_mask (precomputed block
+ * sparsity). */
+int attn_fwd_block_sparse(void* O, const void* Q, const void* K, const void* V,
+                          float* LSE, int B, int H, int Hkv, int Sq, int Sk,
+                          int D, int causal, int window, int input_pos,
+                          const int32_t* k_lengths, const uint8_t* keep,
+                          hipStream_t stream);
+
 /* Split-KV (Flash-Decoding) single-query decode, bf16 Q/K/V/O.
  *   O        out (B, H, D) bf16
  *   Q        in  (B, H, D) bf16

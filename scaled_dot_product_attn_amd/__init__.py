@@ -24,6 +24,9 @@ LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 TILE_M, TILE_N = 256, 64  # prefill tile sizes (ATTN_FWD_TILE_M / _N)
+BLOCK = 64                 # block-sparse block size (ATTN_BLOCK)
+BLOCK_SCORES_RBS, BLOCK_SCORES_MINMAX = 0, 1
+BLOCK_MASK_RELATIVE, BLOCK_MASK_TOPK, BLOCK_MASK_BAND = 0, 1, 2
 
 _lib = None
 
@@ -46,6 +49,12 @@ _SIGS = {
     "attn_decode_ws": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "attn_block_scores_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "attn_block_scores": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                               ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "attn_block_mask": (_I, [_P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _I, _I, _P]),
+    "attn_fwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                   _P, _P, _P]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                       _P, _P, ctypes.c_size_t, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
@@ -165,6 +174,58 @@ def attn_fwd_flex(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
                              Sk, D, int(bool(causal)), int(window), int(input_pos),
                              _ptr(k_lengths), ctypes.byref(f), _stream(stream))
     _check(rc, "attn_fwd_flex")
+
+
+def attn_block_scores(base, rescue, Q, K, kind=0, low=0.5, high=0.9, workspace=None,
+                      stream=None) -> None:
+    """Block scores (B, H, ceil(Sq/64), ceil(Sk/64)) float32 into base (and rescue)."""
+    B, H, Sq, D = Q.shape
+    _, Hkv, Sk, _ = K.shape
+    for t in (Q, K):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("attn_block_scores takes bfloat16 Q and K")
+    for t in (base, rescue):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError("block scores are float32")
+    ws = _ptr(workspace) if workspace is not None else None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().attn_block_scores(_ptr(base), _ptr(rescue), _ptr(Q), _ptr(K), B, H, Hkv, Sq,
+                                 Sk, D, int(kind), float(low), float(high), ws, nbytes,
+                                 _stream(stream))
+    _check(rc, "attn_block_scores")
+
+
+def attn_block_mask(keep, scores=None, mode=0, alpha=1.0, k=0, diagonal=0, accumulate=False,
+                    stream=None) -> None:
+    """Block mask rows (..., nqb, nkb) uint8 from block scores of the same shape."""
+    if keep.dtype != torch.uint8:
+        raise ValueError("keep must be uint8")
+    nqb, nkb = keep.shape[-2], keep.shape[-1]
+    rows = keep.numel() // nkb
+    if scores is not None and (scores.dtype != torch.float32 or scores.shape != keep.shape):
+        raise ValueError("scores must be float32 with keep's shape")
+    rc = lib().attn_block_mask(_ptr(keep), _ptr(scores), rows, nqb, nkb, int(mode),
+                               float(alpha), int(k), int(diagonal), int(bool(accumulate)),
+                               _stream(stream))
+    _check(rc, "attn_block_mask")
+
+
+def attn_fwd_block_sparse(O, Q, K, V, keep, LSE=None, causal=False, window=0, input_pos=0,
+                          k_lengths=None, stream=None) -> None:
+    """bf16 prefill on the kept 64 x 64 blocks of keep (B, H, nqb, nkb) uint8."""
+    B, H, Sq, D = Q.shape
+    _, Hkv, Sk, _ = K.shape
+    for t in (O, Q, K, V):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("attn_fwd_block_sparse takes bfloat16 tensors")
+    if keep.dtype != torch.uint8 or tuple(keep.shape) != (B, H, -(-Sq // BLOCK), -(-Sk // BLOCK)):
+        raise ValueError("keep must be uint8 (B, H, ceil(Sq/64), ceil(Sk/64))")
+    if k_lengths is not None and k_lengths.dtype != torch.int32:
+        raise ValueError("k_lengths must be int32")
+    rc = lib().attn_fwd_block_sparse(_ptr(O), _ptr(Q), _ptr(K), _ptr(V), _ptr(LSE), B, H, Hkv,
+                                      Sq, Sk, D, int(bool(causal)), int(window), int(input_pos),
+                                      _ptr(k_lengths), _ptr(keep), _stream(stream))
+    _check(rc, "attn_fwd_block_sparse")
 
 
 def attn_bwd_workspace_bytes(B: int, H: int, Sq: int, D: int) -> int:

@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_decode.hip",
-           "attn_bwd.hip"]
+           "attn_bwd.hip", "attn_sparse.hip"]
 
 # Packed fp32 VALU forms are switched off for all device code.
 CFLAGS = [

@@ -7,6 +7,7 @@
 // return no tensor (Tylo.jl "Primitives", attention! "Returns nothing").
 #include <hip/hip_runtime.h>
 #include <limits.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/attn.h"
@@ -30,6 +31,16 @@ hipError_t launch_decode(void*, const void*, const void*, const void*,
                          const int32_t*, int, int, int, int, int, int, void*,
                          hipStream_t);
 size_t decode_workspace_bytes(int B, int H, int n_splits, int D);
+template <int D>
+hipError_t launch_fwd_sparse(void*, const void*, const void*, const void*,
+                             float*, int, int, int, int, int, int, int, int,
+                             const int32_t*, const uint8_t*, hipStream_t);
+size_t block_scores_workspace_bytes(int B, int Hkv, int Sk, int D);
+hipError_t launch_block_scores(float*, float*, const void*, const void*, int,
+                               int, int, int, int, int, int, float, float,
+                               void*, hipStream_t);
+hipError_t launch_block_mask(uint8_t*, const float*, long long, int, int, int,
+                             float, int, int, int, hipStream_t);
 hipError_t launch_bwd(void*, void*, void*, const void*, const void*,
                       const void*, const void*, const void*, const float*, int,
                       int, int, int, int, int, int, int, int, const int32_t*,
@@ -229,6 +240,78 @@ int attn_decode(void* O, const void* Q, const void* K, const void* V,
     rc = ATTN_EHIP;
   }
   return rc;
+}
+
+int attn_fwd_block_sparse(void* O, const void* Q, const void* K, const void* V,
+                          float* LSE, int B, int H, int Hkv, int Sq, int Sk,
+                          int D, int causal, int window, int input_pos,
+                          const int32_t* k_lengths, const uint8_t* keep,
+                          hipStream_t stream) {
+  int rc = check_fwd(O, Q, K, V, B, H, Hkv, Sq, Sk, D, causal, window);
+  if (rc != ATTN_OK || Sq == 0) return rc;
+  if (!keep) return ATTN_EINVAL;
+  if ((Sk + ATTN_BLOCK - 1) / ATTN_BLOCK > ATTN_SPARSE_MAX_KEY_BLOCKS)
+    return ATTN_EUNSUPPORTED;
+  hipError_t e =
+      D == 64 ? launch_fwd_sparse<64>(O, Q, K, V, LSE, B, H, Hkv, Sq, Sk, causal,
+                                      window, input_pos, k_lengths, keep, stream)
+              : launch_fwd_sparse<128>(O, Q, K, V, LSE, B, H, Hkv, Sq, Sk,
+                                       causal, window, input_pos, k_lengths,
+                                       keep, stream);
+  return hip_status(e);
+}
+
+size_t attn_block_scores_workspace_bytes(int B, int Hkv, int Sk, int D) {
+  if (B < 1 || Hkv < 1 || Sk < 1 || (D != 64 && D != 128)) return 0;
+  return block_scores_workspace_bytes(B, Hkv, Sk, D);
+}
+
+int attn_block_scores(float* base, float* rescue, const void* Q, const void* K,
+                      int B, int H, int Hkv, int Sq, int Sk, int D, int kind,
+                      float low, float high, void* workspace, size_t ws_bytes,
+                      hipStream_t stream) {
+  if (B < 1 || H < 1 || Hkv < 1 || Sq < 1 || Sk < 1) return ATTN_EINVAL;
+  if (H % Hkv != 0) return ATTN_EINVAL;
+  if (kind != ATTN_BLOCK_SCORES_RBS && kind != ATTN_BLOCK_SCORES_MINMAX)
+    return ATTN_EINVAL;
+  if (!(low >= 0.f && low <= 1.f && high >= 0.f && high <= 1.f)) return ATTN_EINVAL;
+  if (D != 64 && D != 128) return ATTN_EUNSUPPORTED;
+  if (Sq > INT_MAX - 256 || Sk > INT_MAX - 256) return ATTN_EUNSUPPORTED;
+  if ((Sk + ATTN_BLOCK - 1) / ATTN_BLOCK > 4096) return ATTN_EUNSUPPORTED;
+  if (!base || !Q || !K) return ATTN_EINVAL;
+  void* ws = workspace;
+  bool owned = false;
+  const size_t need = block_scores_workspace_bytes(B, Hkv, Sk, D);
+  if (ws) {
+    if (((uintptr_t)ws & 255) != 0 || ws_bytes < need) return ATTN_EINVAL;
+  } else {
+    if (hipMallocAsync(&ws, need, stream) != hipSuccess) {
+      (void)hipGetLastError();
+      return ATTN_EHIP;
+    }
+    owned = true;
+  }
+  int rc = hip_status(launch_block_scores(base, rescue, Q, K, B, H, Hkv, Sq, Sk,
+                                          D, kind, low, high, ws, stream));
+  if (owned && hipFreeAsync(ws, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    rc = ATTN_EHIP;
+  }
+  return rc;
+}
+
+int attn_block_mask(uint8_t* keep, const float* scores, int rows, int nqb,
+                    int nkb, int mode, float alpha, int k, int diagonal,
+                    int accumulate, hipStream_t stream) {
+  if (rows < 0 || nqb < 1 || nkb < 1 || !keep) return ATTN_EINVAL;
+  if (mode < ATTN_BLOCK_MASK_RELATIVE || mode > ATTN_BLOCK_MASK_BAND) return ATTN_EINVAL;
+  if (mode != ATTN_BLOCK_MASK_BAND && !scores) return ATTN_EINVAL;
+  if (mode == ATTN_BLOCK_MASK_RELATIVE && !(alpha > 0.f && alpha <= 1.f)) return ATTN_EINVAL;
+  if (mode == ATTN_BLOCK_MASK_TOPK && k < 0) return ATTN_EINVAL;
+  if (rows == 0) return ATTN_OK;
+  const float ln_alpha = mode == ATTN_BLOCK_MASK_RELATIVE ? (float)log((double)alpha) : 0.f;
+  return hip_status(launch_block_mask(keep, scores, rows, nqb, nkb, mode, ln_alpha,
+                                      k, diagonal, accumulate != 0, stream));
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int Sq, int D) {

@@ -74,6 +74,11 @@ constexpr float kLazyRescale = 8.0f;       // log2 headroom before m is raised
 constexpr int kBufferRsrcWord3 = 0x00020000;
 static_assert(kFwdTileM == ATTN_FWD_TILE_M && kFwdTileN == ATTN_FWD_TILE_N,
               "the exported tile plan must use the kernel's tile sizes");
+// block-sparse prefill: 64 x 64 blocks, at most this many key tiles per row
+constexpr int kSparseBlock = 64;
+constexpr int kSparseMaxTiles = ATTN_SPARSE_MAX_KEY_BLOCKS;
+static_assert(kSparseBlock == kFwdTileN && kFwdTileM % kSparseBlock == 0,
+              "a key tile is one block; a workgroup holds whole row blocks");
 
 // Kernel-side copy of attn_flex_t (see include/attn.h); strides in elements.
 struct FlexArgs {
@@ -131,14 +136,14 @@ __device__ inline int vt_group_pos(int quad_in_group) {
   return ((quad_in_group & 1) << 3) | ((quad_in_group >> 1) << 2);
 }
 
-template <int D, bool FLEX, bool BIAS>
+template <int D, bool FLEX, bool BIAS, bool SPARSE>
 __global__ __launch_bounds__(kFwdThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     __bf16* __restrict__ O, const __bf16* __restrict__ Q,
     const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     float* __restrict__ LSE, int B, int H, int Hkv, int Sq, int Sk, int causal,
     int window, int input_pos, const int32_t* __restrict__ k_lengths,
-    float scale_log2, FlexArgs fx) {
+    float scale_log2, FlexArgs fx, const uint8_t* __restrict__ keep) {
   using L = FwdLds<D>;
   constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int DBLK = D / 32;     // 32-wide blocks of the head dimension
@@ -146,6 +151,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   constexpr int VTHREADS = (kFwdTileN / 4) * (D / 8);        // threads staging V
 
   __shared__ __attribute__((aligned(16))) char smem[FLEX ? L::kTotalFlex : L::kTotal];
+  // block-sparse: the key tiles some row block of this workgroup keeps, and
+  // per listed tile the keep bits of the four 64-row blocks
+  __shared__ int16_t s_list[SPARSE ? kSparseMaxTiles : 1];
+  __shared__ uint8_t s_kbits[SPARSE ? kSparseMaxTiles : 1];
+  __shared__ int s_ntiles;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -225,6 +235,38 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     kt_first = geo.union_lo / kFwdTileN;
     kt_last = (geo.union_hi - 1) / kFwdTileN;
   }
+  // The tiles walked, in order: every tile of the union, or (block-sparse)
+  // those that some row block of the workgroup keeps, listed by wave 0.
+  int n_tiles = kt_last - kt_first + 1;
+  if constexpr (SPARSE) {
+    const int nqb = (Sq + kSparseBlock - 1) / kSparseBlock;
+    const int nkb = (Sk + kSparseBlock - 1) / kSparseBlock;
+    const int qb0 = i0 / kSparseBlock;
+    const uint8_t* krow = keep + ((size_t)(b * H + h) * nqb + qb0) * nkb;
+    if (wave == 0) {
+      int base = 0;
+      for (int c0 = kt_first; c0 <= kt_last; c0 += 64) {
+        const int kt = c0 + lane;
+        unsigned bits = 0;
+        if (kt <= kt_last) {
+#pragma unroll
+          for (int q = 0; q < kFwdTileM / kSparseBlock; ++q)
+            if (qb0 + q < nqb && krow[(size_t)q * nkb + kt]) bits |= 1u << q;
+        }
+        const uint64_t m = __builtin_amdgcn_ballot_w64(bits != 0);
+        if (bits) {
+          const int at = base + __builtin_popcountll(m & ((1ull << lane) - 1));
+          s_list[at] = (int16_t)kt;
+          s_kbits[at] = (uint8_t)bits;
+        }
+        base += __builtin_popcountll(m);
+      }
+      if (lane == 0) s_ntiles = base;
+    }
+    __syncthreads();
+    n_tiles = s_ntiles;
+  }
+  auto tile_at = [&](int idx) { return SPARSE ? (int)s_list[idx] : kt_first + idx; };
 
   // ---- staging: global -> registers -> LDS ----
   // K/V are read through buffer resources whose range is exactly the keys
@@ -333,10 +375,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   f32x16_t s[2];           // S^T of the current tile (two 32-key blocks)
   u32x4_t pb[2][2];        // P^T of the previous tile, packed bf16 (MFMA B operands)
 
-  // M-phase: O += P(kt-1) V(kt-1), then S(kt) = K(kt) Q^T
-  auto m_phase = [&](int kt, bool do_pv, bool do_s) {
+  // M-phase of the idx-th walked tile: O += P V of the previous one, then
+  // S = K Q^T of this one; tile idx sits in LDS buffer idx & 1
+  auto m_phase = [&](int idx, bool do_pv, bool do_s) {
     if (do_pv) {
-      const char* vb = smem + L::kOffV + ((kt - 1) & 1) * L::kBytesV;
+      const char* vb = smem + L::kOffV + ((idx - 1) & 1) * L::kBytesV;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
         const char* arow = vb + (db * 32 + lrow) * L::kRowV + half * 16;
@@ -353,7 +396,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     if (FLEX && do_s && has_bias) {
       // lane's keys of the tile: j0 + kb2*32 + q4*8 + half*4 + e, held in
       // register q4*4 + e of block kb2 (the S^T accumulator order)
-      const int jb = kt * kFwdTileN + half * 4;
+      const int jb = tile_at(idx) * kFwdTileN + half * 4;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -365,7 +408,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         }
     }
     if (do_s) {
-      const char* kb = smem + (kt & 1) * L::kBytesK;
+      const char* kb = smem + (idx & 1) * L::kBytesK;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         s[kb2] = f32x16_t{};
@@ -429,8 +472,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     }
   };
   // flex: a key whose document differs from the row's is blocked
-  auto doc_mask = [&](int kt) {
-    const char* db = smem + L::kOffDoc + (kt & 1) * L::kBytesDoc + half * 16;
+  auto doc_mask = [&](int idx) {
+    const char* db = smem + L::kOffDoc + (idx & 1) * L::kBytesDoc + half * 16;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -445,11 +488,21 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // flex scores are already in base-2 units
   const float sl2 = FLEX ? (transform ? 1.f : fx.qk_scale * kLog2e) : scale_log2;
 
-  auto v_phase = [&](int kt) {
+  auto v_phase = [&](int idx) {
+    const int kt = tile_at(idx);
     const int j0 = kt * kFwdTileN;
     if constexpr (FLEX) {
       if (transform) flex_scores(j0);
-      if (has_doc) doc_mask(kt);
+      if (has_doc) doc_mask(idx);
+    }
+    if constexpr (SPARSE) {
+      // this wave's 64-row block does not keep the tile: no key of it counts
+      if (!((s_kbits[idx] >> (wave >> 1)) & 1)) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb2][r] = -INFINITY;
+      }
     }
     if (tile_class(geo, j0, kFwdTileN) == kTilePartial || (FLEX && force_partial)) {
       // key j0 + half*4 + c is allowed iff c lies in [t_lo, t_lo + width);
@@ -496,24 +549,24 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         pb[kb2][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
       }
     l_run += psum;
-    if (kt + 1 <= kt_last) stash((kt + 1) & 1);
-    if (kt + 2 <= kt_last) fetch(kt + 2);
+    if (idx + 1 < n_tiles) stash((idx + 1) & 1);
+    if (idx + 2 < n_tiles) fetch(tile_at(idx + 2));
   };
 
-  if (kt_first <= kt_last) {
-    // prologue: tile kt_first in LDS, tile kt_first+1 in flight
-    fetch(kt_first);
-    stash(kt_first & 1);
-    if (kt_first + 1 <= kt_last) fetch(kt_first + 1);
+  if (n_tiles > 0) {
+    // prologue: the first tile in LDS, the second in flight
+    fetch(tile_at(0));
+    stash(0);
+    if (n_tiles > 1) fetch(tile_at(1));
     __syncthreads();
     if (grp == 1) __syncthreads();  // group B runs one phase behind
-    for (int kt = kt_first; kt <= kt_last; ++kt) {
-      m_phase(kt, kt > kt_first, true);
+    for (int idx = 0; idx < n_tiles; ++idx) {
+      m_phase(idx, idx > 0, true);
       __syncthreads();
-      v_phase(kt);
+      v_phase(idx);
       __syncthreads();
     }
-    m_phase(kt_last + 1, true, false);
+    m_phase(n_tiles, true, false);
     if (grp == 0) __syncthreads();  // matches group B's extra barrier
   }
 
@@ -551,11 +604,11 @@ hipError_t launch_fwd_bf16(void* O, const void* Q, const void* K,
   const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
   const long long total = (long long)nqt * H * B;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false>), dim3((unsigned)total),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, false>), dim3((unsigned)total),
                      dim3(kFwdThreads), 0, stream, (__bf16*)O,
                      (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                      B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                     scale_log2, FlexArgs{});
+                     scale_log2, FlexArgs{}, (const uint8_t*)nullptr);
   return hipGetLastError();
 }
 
@@ -581,17 +634,34 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
   fx.qk_scale = f->qk_scale > 0.f ? f->qk_scale : 1.f / sqrtf((float)D);
   // the bias tile costs 32 registers per lane: a kernel of its own
   if (fx.bias)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true>), dim3((unsigned)total),
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, false>), dim3((unsigned)total),
                        dim3(kFwdThreads), 0, stream, (__bf16*)O,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                        B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                       0.f, fx);
+                       0.f, fx, (const uint8_t*)nullptr);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false>), dim3((unsigned)total),
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false, false>), dim3((unsigned)total),
                        dim3(kFwdThreads), 0, stream, (__bf16*)O,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                        B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                       0.f, fx);
+                       0.f, fx, (const uint8_t*)nullptr);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fwd_sparse(void* O, const void* Q, const void* K,
+                             const void* V, float* LSE, int B, int H, int Hkv,
+                             int Sq, int Sk, int causal, int window,
+                             int input_pos, const int32_t* k_lengths,
+                             const uint8_t* keep, hipStream_t stream) {
+  const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
+  const long long total = (long long)nqt * H * B;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, true>), dim3((unsigned)total),
+                     dim3(kFwdThreads), 0, stream, (__bf16*)O,
+                     (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
+                     B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
+                     scale_log2, FlexArgs{}, keep);
   return hipGetLastError();
 }
 
@@ -604,7 +674,12 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
                                          const void*, float*, int, int, int,  \
                                          int, int, int, int, int,             \
                                          const int32_t*, const attn_flex_t*,  \
-                                         hipStream_t);
+                                         hipStream_t);                        \
+  template hipError_t launch_fwd_sparse<D>(void*, const void*, const void*,   \
+                                           const void*, float*, int, int,     \
+                                           int, int, int, int, int, int,      \
+                                           const int32_t*, const uint8_t*,    \
+                                           hipStream_t);
 ATTN_INST(64)
 ATTN_INST(128)
 #undef ATTN_INST

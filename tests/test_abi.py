@@ -38,7 +38,8 @@ def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("attn_fwd", "attn_fwd_f32", "attn_decode", "attn_decode_ws",
               "attn_decode_workspace_bytes", "attn_decode_paged", "attn_fwd_flex",
-              "attn_bwd", "attn_bwd_workspace_bytes",
+              "attn_bwd", "attn_bwd_workspace_bytes", "attn_block_scores",
+              "attn_block_scores_workspace_bytes", "attn_block_mask", "attn_fwd_block_sparse",
               "attn_mask_dump",
               "attn_tile_plan",
               "attn_status_string", "attn_version"):
@@ -122,6 +123,37 @@ def test_bwd_argument_errors(lib):
     assert bwd(ws=260, nbytes=need) == attn.ATTN_EINVAL
     assert lib.attn_bwd_workspace_bytes(0, 4, 8, 128) == 0
     assert bwd(Sq=0, Sk=0) == attn.ATTN_OK
+
+
+def test_block_sparse_argument_errors(lib):
+    def sc(kind=0, low=0.5, high=0.9, H=4, Hkv=2, Sq=64, Sk=64, D=128, base=1):
+        return lib.attn_block_scores(base, None, 1, 1, 1, H, Hkv, Sq, Sk, D, kind, low, high,
+                                     256, 1 << 30, None)
+    assert sc(kind=2) == attn.ATTN_EINVAL
+    assert sc(low=1.5) == attn.ATTN_EINVAL
+    assert sc(H=3) == attn.ATTN_EINVAL
+    assert sc(D=96) == attn.ATTN_EUNSUPPORTED
+    assert sc(Sk=64 * 4097) == attn.ATTN_EUNSUPPORTED
+    assert sc(base=None) == attn.ATTN_EINVAL
+    assert lib.attn_block_scores_workspace_bytes(1, 2, 64, 128) > 0
+    assert lib.attn_block_scores_workspace_bytes(1, 2, 64, 80) == 0
+
+    def mk(keep=1, scores=1, rows=4, mode=0, alpha=0.5, k=1):
+        return lib.attn_block_mask(keep, scores, rows, 2, 8, mode, alpha, k, 1, 0, None)
+    assert mk(keep=None) == attn.ATTN_EINVAL
+    assert mk(mode=3) == attn.ATTN_EINVAL
+    assert mk(alpha=0.0) == attn.ATTN_EINVAL
+    assert mk(alpha=1.5) == attn.ATTN_EINVAL
+    assert mk(mode=1, k=-1) == attn.ATTN_EINVAL
+    assert mk(scores=None) == attn.ATTN_EINVAL
+    assert mk(rows=0) == attn.ATTN_OK
+
+    def sp(keep=1, Sk=64, causal=1, window=0):
+        return lib.attn_fwd_block_sparse(1, 1, 1, 1, None, 1, 4, 2, 64, Sk, 128, causal,
+                                         window, 0, None, keep, None)
+    assert sp(keep=None) == attn.ATTN_EINVAL
+    assert sp(causal=0, window=3) == attn.ATTN_EINVAL
+    assert sp(Sk=64 * 2049) == attn.ATTN_EUNSUPPORTED
 
 
 def test_decode_argument_errors(lib):

@@ -674,3 +674,133 @@ def test_bwd_full_size_one_kv_group():
     dO, dQ, dK, dV = _bwd_run(w)
     errs = _bwd_check(w, dO, dQ, dK, dV, heads=[(0, h) for h in range(4)])
     _say("  " + ", ".join(f"{k} {e:.2e}/{s:.1f}" for k, (e, s) in errs.items()))
+
+
+# ---------------------------------------------------------------------------
+# block-sparse prefill: estimators, block masks, attention on kept blocks
+# ---------------------------------------------------------------------------
+
+def _nb(n):
+    return -(-n // attn.BLOCK)
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 2, 200, 300, 128), (2, 2, 2, 64, 130, 64),
+                                   (1, 8, 1, 256, 1000, 128)])
+def test_block_scores_parity(shape):
+    B, H, Hkv, Sq, Sk, D = shape
+    _say(f"block scores {shape}")
+    w = wl.prefill_random(B, H, Hkv, Sq, Sk, D, torch.bfloat16, seed=95)
+    q, k = w.q.to(DEV), w.k.to(DEV)
+    base = torch.empty(B, H, _nb(Sq), _nb(Sk), device=DEV)
+    resc = torch.empty_like(base)
+    mm = torch.empty_like(base)
+    attn.attn_block_scores(base, resc, q, k, attn.BLOCK_SCORES_RBS)
+    attn.attn_block_scores(mm, None, q, k, attn.BLOCK_SCORES_MINMAX)
+    torch.cuda.synchronize()
+    rb, rr = ora.rbs_block_scores_ref(_np(w.q), _np(w.k), attn.BLOCK)
+    rm = ora.minmax_block_scores_ref(_np(w.q), _np(w.k), attn.BLOCK)
+    for name, got, ref in (("base", base, rb), ("rescue", resc, rr), ("minmax", mm, rm)):
+        err = np.max(np.abs(_np(got) - ref) / np.maximum(1.0, np.abs(ref)))
+        assert err <= 1e-4, f"{name} relative error {err}"
+
+
+def test_block_masks_bitexact():
+    g = torch.Generator().manual_seed(96)
+    B, H, nqb, nkb = 2, 3, 5, 37
+    s = torch.randn(B, H, nqb, nkb, generator=g)
+    s[0, 0, 0, 3] = s[0, 0, 0, 7] = s[0, 0, 0].max() + 1.0   # a tie at the top
+    sd = s.to(DEV)
+    keep = torch.zeros(B, H, nqb, nkb, dtype=torch.uint8, device=DEV)
+    sn = s.numpy()
+    for alpha in (0.22, 0.18, 1.0):
+        attn.attn_block_mask(keep, sd, attn.BLOCK_MASK_RELATIVE, alpha=alpha)
+        torch.cuda.synchronize()
+        thr = sn.max(axis=-1, keepdims=True).astype(np.float32) + np.float32(math.log(alpha))
+        np.testing.assert_array_equal(keep.cpu().numpy().astype(bool), sn >= thr)
+    for kk in (0, 1, 5, 37):
+        attn.attn_block_mask(keep, sd, attn.BLOCK_MASK_TOPK, k=kk)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(keep.cpu().numpy().astype(bool),
+                                      ora.top_k_block_mask_ref(sn, kk))
+    # the recipe's union: relative | relative | band
+    attn.attn_block_mask(keep, sd, attn.BLOCK_MASK_RELATIVE, alpha=0.22)
+    attn.attn_block_mask(keep, -sd, attn.BLOCK_MASK_RELATIVE, alpha=0.18, accumulate=True)
+    attn.attn_block_mask(keep, None, attn.BLOCK_MASK_BAND, diagonal=2, accumulate=True)
+    torch.cuda.synchronize()
+    want = (ora.relative_block_mask_ref(sn, 0.22) | ora.relative_block_mask_ref(-sn, 0.18)
+            | ora.band_block_mask_ref(nqb, nkb, 2)[None, None])
+    np.testing.assert_array_equal(keep.cpu().numpy().astype(bool), want)
+
+
+SPARSE_CASES = [
+    # B, H, Hkv, Sq, Sk, D, causal, window, input_pos, k_lengths, density
+    (1, 4, 2, 512, 512, 128, True, 0, 0, None, 0.3),
+    (2, 4, 1, 300, 700, 128, False, 0, 0, [700, 450], 0.25),
+    (1, 8, 2, 257, 257, 64, True, 0, 0, None, 0.5),
+    (1, 4, 4, 384, 1024, 128, True, 256, 640, None, 0.4),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=lambda c: "x".join(map(str, c[:6])))
+def test_block_sparse_fwd_parity(case):
+    B, H, Hkv, Sq, Sk, D, causal, window, ip, kl, dens = case
+    _say(f"block-sparse fwd {case}")
+    w = wl.prefill_random(B, H, Hkv, Sq, Sk, D, torch.bfloat16, seed=97, causal=causal,
+                          window=window, input_pos=ip, k_lengths=kl)
+    g = torch.Generator().manual_seed(98)
+    keep = (torch.rand(B, H, _nb(Sq), _nb(Sk), generator=g) < dens).to(torch.uint8)
+    keep[0, 0, 1] = 0                     # one row block keeps nothing
+    q, k, v = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV)
+    O = torch.empty_like(q)
+    L = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    kld = None if kl is None else w.k_lengths.to(DEV)
+    attn.attn_fwd_block_sparse(O, q, k, v, keep.to(DEV), L, causal, window, ip, kld)
+    torch.cuda.synchronize()
+    Or, Lr = ora.block_sparse_attn_ref(_np(w.q), _np(w.k), _np(w.v), keep.numpy(), attn.BLOCK,
+                                       causal, window, ip, None if kl is None else kl)
+    err = np.max(np.abs(_np(O) - Or))
+    assert err <= TOL_BF16, f"O max-abs error {err}"
+    Ln = _np(L)
+    np.testing.assert_array_equal(np.isneginf(Ln), np.isneginf(Lr))
+    fin = np.isfinite(Lr)
+    assert np.max(np.abs(Ln[fin] - Lr[fin])) <= TOL_LSE
+    assert torch.all(O[0, 0, 64:128] == 0)
+
+
+def test_block_sparse_all_kept_equals_dense_bitwise():
+    w = wl.prefill_random(1, 8, 2, 600, 600, 128, torch.bfloat16, seed=99, causal=True)
+    q, k, v = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV)
+    keep = torch.ones(1, 8, _nb(600), _nb(600), dtype=torch.uint8, device=DEV)
+    O = torch.empty_like(q)
+    attn.attn_fwd_block_sparse(O, q, k, v, keep, None, True)
+    Od = attn.sdpa(q, k, v, True, return_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Od)
+
+
+def test_rbs_pipeline_on_image_workload():
+    _say("RBS pipeline on image_clustered")
+    w = wl.make("image_clustered", device=DEV)
+    B, H, S, D = w.q.shape
+    nb = _nb(S)
+    base = torch.empty(B, H, nb, nb, device=DEV)
+    resc = torch.empty_like(base)
+    attn.attn_block_scores(base, resc, w.q, w.k, attn.BLOCK_SCORES_RBS)
+    keep = torch.empty(B, H, nb, nb, dtype=torch.uint8, device=DEV)
+    attn.attn_block_mask(keep, base, attn.BLOCK_MASK_RELATIVE, alpha=0.22)
+    attn.attn_block_mask(keep, resc, attn.BLOCK_MASK_RELATIVE, alpha=0.18, accumulate=True)
+    attn.attn_block_mask(keep, None, attn.BLOCK_MASK_BAND, diagonal=1, accumulate=True)
+    O = torch.empty_like(w.q)
+    L = torch.empty(B, H, S, device=DEV)
+    attn.attn_fwd_block_sparse(O, w.q, w.k, w.v, keep, L, False)
+    torch.cuda.synchronize()
+    _say(f"  kept density {keep.float().mean().item():.3f}")
+    heads = [(0, 0), (0, 17)]
+    rows = _sample_rows(S, np.random.default_rng(100))
+    rb, rr = ora.rbs_block_scores_ref(_np(w.q[:, :1]), _np(w.k[:, :1]), attn.BLOCK)
+    assert np.max(np.abs(_np(base[:, :1]) - rb) / np.maximum(1, np.abs(rb))) <= 1e-4
+    Or, Lr = ora.block_sparse_attn_ref(_np(w.q), _np(w.k), _np(w.v), keep.cpu().numpy(),
+                                       attn.BLOCK, heads=heads, rows=rows)
+    sel = ~np.isnan(Lr)
+    err = np.max(np.abs(_np(O)[sel] - Or[sel]))
+    assert err <= TOL_BF16, err
