@@ -13,7 +13,8 @@ O) is reported beside it.  The window/offset and clustered-image workloads are
 timed too, as extra lines of context, and so is the same decode batch stored
 in a paged serving cache (block size 16, shuffled physical blocks;
 attn_decode_paged), and the causal GQA prefill with soft-capping and ALiBi
-(attn_fwd_flex), and its backward (attn_bwd).  ``cpu_baseline`` times the fp64 oracle
+(attn_fwd_flex), its backward (attn_bwd), and block-sparse attention on the
+image workload (top-10% key blocks by centroid score).  ``cpu_baseline`` times the fp64 oracle
 on the host on a bounded sample (whole heads) of the prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -198,13 +199,35 @@ def main():
     def run_bwd():
         attn.attn_bwd(dQ, dK, dV, dO, pre.q, pre.k, pre.v, Ob, Lb, True, workspace=bws)
 
+    # block-sparse: the image workload, centroid (RBS base) block scores, the
+    # top 10 % of key blocks per row block, attention on the kept blocks
+    if not args.no_extra:
+        img = extra["image_clustered"]
+        nbq = -(-img.q.shape[2] // attn.BLOCK)
+        nbk = -(-img.k.shape[2] // attn.BLOCK)
+        bs_scores = torch.empty(img.q.shape[0], img.q.shape[1], nbq, nbk, device=dev)
+        bs_keep = torch.empty(bs_scores.shape, dtype=torch.uint8, device=dev)
+        bs_ws = torch.empty(attn.attn_block_scores_workspace_bytes(
+            img.k.shape[0], img.k.shape[1], img.k.shape[2], img.k.shape[3]),
+            dtype=torch.uint8, device=dev)
+        bs_topk = max(1, -(-nbk // 10))
+        Obs, Lbs = torch.empty_like(img.q), torch.empty(img.q.shape[:3], device=dev)
+
+    def run_block_estimate():
+        attn.attn_block_scores(bs_scores, None, img.q, img.k, attn.BLOCK_SCORES_RBS,
+                               workspace=bs_ws)
+        attn.attn_block_mask(bs_keep, bs_scores, attn.BLOCK_MASK_TOPK, k=bs_topk)
+
+    def run_block_sparse():
+        attn.attn_fwd_block_sparse(Obs, img.q, img.k, img.v, bs_keep, Lbs, False)
+
     def run_flex():
         attn.attn_fwd_flex(Of, pre.q, pre.k, pre.v, Lf, True, softcap=30.0,
                            alibi_slopes=flex_slopes)
 
     names = ["prefill", "decode"] + list(extra) + (["decode_paged"] if paged is not None else [])
     if not args.no_extra:
-        names += ["flex_softcap_alibi", "backward"]
+        names += ["flex_softcap_alibi", "backward", "block_estimate", "block_sparse"]
     ev = {n: [] for n in names}
 
     def step(record):
@@ -223,6 +246,10 @@ def main():
                 run_flex()
             elif n == "backward":
                 run_bwd()
+            elif n == "block_estimate":
+                run_block_estimate()
+            elif n == "block_sparse":
+                run_block_sparse()
             else:
                 run_prefill(extra[n], *ext_out[n])
             if record:
@@ -302,6 +329,18 @@ def main():
             "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": bf,
             "config": "attn_bwd of the gqa_causal prefill (delta + dK/dV + dQ kernels); "
                       "flops = 2.5 x forward (S, dP, dV, dK, dQ)"}
+    if "block_sparse" in ms:
+        kept = int(bs_keep.sum().item())
+        bfl = 4 * img.q.shape[3] * kept * attn.BLOCK * attn.BLOCK
+        tf = bfl / (ms["block_sparse"] * 1e-3) / 1e12
+        out["block_sparse"] = {
+            "ms": round(ms["block_sparse"], 4), "TFLOP/s": round(tf, 2),
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": bfl,
+            "kept_fraction": round(kept / bs_keep.numel(), 4),
+            "estimate_ms": round(ms["block_estimate"], 4),
+            "config": "image_clustered, RBS-base block scores, top-10% key blocks per row "
+                      "block (attn_block_scores + attn_block_mask, then attn_fwd_block_sparse); "
+                      "flops = 4 D per pair of the kept blocks"}
     if paged is not None:
         pb = decode_bytes(paged)
         gbs = pb / (ms["decode_paged"] * 1e-3) / 1e9

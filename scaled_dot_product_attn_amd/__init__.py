@@ -176,6 +176,10 @@ def attn_fwd_flex(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
     _check(rc, "attn_fwd_flex")
 
 
+def attn_block_scores_workspace_bytes(B: int, Hkv: int, Sk: int, D: int) -> int:
+    return lib().attn_block_scores_workspace_bytes(B, Hkv, Sk, D)
+
+
 def attn_block_scores(base, rescue, Q, K, kind=0, low=0.5, high=0.9, workspace=None,
                       stream=None) -> None:
     """Block scores (B, H, ceil(Sq/64), ceil(Sk/64)) float32 into base (and rescue)."""

@@ -267,6 +267,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     n_tiles = s_ntiles;
   }
   auto tile_at = [&](int idx) { return SPARSE ? (int)s_list[idx] : kt_first + idx; };
+  // block-sparse: does this wave's 64-row block keep the idx-th walked tile?
+  // (uniform per wave; a wave skips the products and softmax of a tile it
+  // drops, and still takes part in the staging and the barriers)
+  auto wave_keeps = [&](int idx) {
+    return !SPARSE || ((s_kbits[idx] >> (wave >> 1)) & 1) != 0;
+  };
 
   // ---- staging: global -> registers -> LDS ----
   // K/V are read through buffer resources whose range is exactly the keys
@@ -378,6 +384,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // M-phase of the idx-th walked tile: O += P V of the previous one, then
   // S = K Q^T of this one; tile idx sits in LDS buffer idx & 1
   auto m_phase = [&](int idx, bool do_pv, bool do_s) {
+    if constexpr (SPARSE) {
+      do_pv = do_pv && wave_keeps(idx - 1);
+      do_s = do_s && wave_keeps(idx);
+    }
     if (do_pv) {
       const char* vb = smem + L::kOffV + ((idx - 1) & 1) * L::kBytesV;
 #pragma unroll
@@ -496,12 +506,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       if (has_doc) doc_mask(idx);
     }
     if constexpr (SPARSE) {
-      // this wave's 64-row block does not keep the tile: no key of it counts
-      if (!((s_kbits[idx] >> (wave >> 1)) & 1)) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb2][r] = -INFINITY;
+      // this wave's 64-row block drops the tile: no score, only the staging
+      if (!wave_keeps(idx)) {
+        if (idx + 1 < n_tiles) stash((idx + 1) & 1);
+        if (idx + 2 < n_tiles) fetch(tile_at(idx + 2));
+        return;
       }
     }
     if (tile_class(geo, j0, kFwdTileN) == kTilePartial || (FLEX && force_partial)) {
