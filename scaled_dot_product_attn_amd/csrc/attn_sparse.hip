@@ -144,13 +144,97 @@ __global__ __launch_bounds__(256) void attn_block_quantile_kernel(
   }
 }
 
-// Per (query block, query head, batch): block scores against every key block.
-// Lane = query token of the block; wave w takes key blocks w, w + 4, ...
-template <int D, bool MINMAX>
-__global__ __launch_bounds__(256) void attn_block_scores_kernel(
+// Centroid (RBS) scores per (query block, query head, batch), one wave:
+// block scores against every key block.  Lane = key block (blocks lane, lane + 64, ...), holding the
+// block's summary in registers; the query block (float32, with its row norms)
+// sits in LDS and every lane reads the same row (broadcast).  The log-sum-exp
+// over the block's query tokens is an online update inside each lane, so no
+// cross-lane reduction is needed.
+template <int D>
+__global__ __launch_bounds__(64) void attn_block_scores_kernel(
     float* __restrict__ base_out, float* __restrict__ rescue_out,
     const __bf16* __restrict__ Q, const float* __restrict__ stats,
     const float* __restrict__ quant, int H, int Hkv, int Sq, int nq, int nk,
+    float scale) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) float s_q[kBlock][D];
+  __shared__ float s_qn[kBlock];
+  const int a = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int g = h / (H / Hkv);
+  const int i0 = a * kBlock;
+  const int nrows = min(kBlock, Sq - i0);
+  // stage the query block as float32 and its row norms
+  {
+    const __bf16* qb = Q + ((size_t)(b * H + h) * Sq + i0) * D;
+    for (int x = lane; x < nrows * (D / 8); x += 64) {
+      const int r = x / (D / 8), c = x % (D / 8);
+      const u32x4_t w = *(const u32x4_t*)(qb + (size_t)r * D + c * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s_q[r][c * 8 + 2 * e] = bf16_lo(w[e]);
+        s_q[r][c * 8 + 2 * e + 1] = bf16_hi(w[e]);
+      }
+    }
+    __syncthreads();
+    if (lane < nrows) {
+      float n2 = 0.f;
+      for (int d = 0; d < D; ++d) n2 = __builtin_fmaf(s_q[lane][d], s_q[lane][d], n2);
+      s_qn[lane] = sqrtf(n2);
+    }
+    __syncthreads();
+  }
+  const float* st = stats + (size_t)(b * Hkv + g) * nk * (3 * D + 1);
+  const float r_low = quant[(size_t)(b * Hkv + g) * 2];
+  const float r_high = quant[(size_t)(b * Hkv + g) * 2 + 1];
+  const size_t row = ((size_t)(b * H + h) * nq + a) * nk;
+  for (int kb = lane; kb < nk; kb += 64) {
+    float v0[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) v0[d] = st[(size_t)kb * D + d];
+    const float r = st[(size_t)3 * nk * D + kb];
+    const float beta = r_high == r_low
+                           ? (r > r_low ? 1.f : 0.f)
+                           : fminf(fmaxf((r - r_low) / (r_high - r_low), 0.f), 1.f);
+    const float w = r * beta;
+    float m1 = -INFINITY, s1 = 0.f, m2 = -INFINITY, s2 = 0.f;
+    for (int r = 0; r < nrows; ++r) {
+      float part[8] = {};
+#pragma unroll
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const f32x4_t x = *(const f32x4_t*)&s_q[r][d4 * 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = d4 * 4 + e;
+          part[d & 7] = __builtin_fmaf(x[e], v0[d], part[d & 7]);
+        }
+      }
+      float acc = 0.f;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) acc += part[p];
+      const float e1 = acc * scale;
+      const float n1 = fmaxf(m1, e1);
+      s1 = s1 * __expf(m1 - n1) + __expf(e1 - n1);
+      m1 = n1;
+      const float e2 = __builtin_fmaf(s_qn[r], w, acc) * scale;
+      const float n2 = fmaxf(m2, e2);
+      s2 = s2 * __expf(m2 - n2) + __expf(e2 - n2);
+      m2 = n2;
+    }
+    base_out[row + kb] = m1 + __logf(s1);
+    if (rescue_out) rescue_out[row + kb] = m2 + __logf(s2);
+  }
+}
+
+// Min/max box-bound scores per (query block, query head, batch).  Lane = query
+// token of the block; wave w takes key blocks w, w + 4, ...; the block's lo /
+// hi rows are wave-uniform (scalar loads), the log-sum-exp over the block's
+// tokens is a wave reduction.  (The lane-per-key-block layout of the centroid
+// kernel would need both 2 x D summaries in registers.)
+template <int D>
+__global__ __launch_bounds__(256) void attn_block_minmax_kernel(
+    float* __restrict__ base_out, const __bf16* __restrict__ Q,
+    const float* __restrict__ stats, int H, int Hkv, int Sq, int nq, int nk,
     float scale) {
   const int a = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -171,45 +255,23 @@ __global__ __launch_bounds__(256) void attn_block_scores_kernel(
       }
     }
   }
-  float qn = 0.f;
-#pragma unroll
-  for (int d = 0; d < D; ++d) qn = __builtin_fmaf(q[d], q[d], qn);
-  qn = sqrtf(qn);
   const float* st = stats + (size_t)(b * Hkv + g) * nk * (3 * D + 1);
-  const float r_low = MINMAX ? 0.f : quant[(size_t)(b * Hkv + g) * 2];
-  const float r_high = MINMAX ? 0.f : quant[(size_t)(b * Hkv + g) * 2 + 1];
   const size_t row = ((size_t)(b * H + h) * nq + a) * nk;
   for (int kb = wave; kb < nk; kb += 4) {
-    float ell, ell_r = 0.f;
-    if constexpr (MINMAX) {
+    float ell;
+    {
       const float* lo = st + (size_t)nk * D + (size_t)kb * D;
       const float* hi = st + (size_t)2 * nk * D + (size_t)kb * D;
       float acc = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) acc += fmaxf(q[d] * lo[d], q[d] * hi[d]);
       ell = acc * scale;
-    } else {
-      const float* c = st + (size_t)kb * D;
-      float acc = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) acc = __builtin_fmaf(q[d], c[d], acc);
-      const float r = st[(size_t)3 * nk * D + kb];
-      const float beta = r_high == r_low ? (r > r_low ? 1.f : 0.f)
-                                         : fminf(fmaxf((r - r_low) / (r_high - r_low), 0.f), 1.f);
-      ell = acc * scale;
-      ell_r = __builtin_fmaf(qn * r, beta, acc) * scale;
     }
     // log-sum-exp over the block's live query tokens
     const float e1 = live ? ell : -INFINITY;
     const float m1 = wave_max(e1);
     const float s1 = wave_sum(live ? __expf(e1 - m1) : 0.f);
     if (lane == 0) base_out[row + kb] = m1 + __logf(s1);
-    if (!MINMAX && rescue_out) {
-      const float e2 = live ? ell_r : -INFINITY;
-      const float m2 = wave_max(e2);
-      const float s2 = wave_sum(live ? __expf(e2 - m2) : 0.f);
-      if (lane == 0) rescue_out[row + kb] = m2 + __logf(s2);
-    }
   }
 }
 
@@ -271,16 +333,16 @@ static hipError_t launch_scores_d(float* base, float* rescue, const void* Q,
   if (e != hipSuccess) return e;
   const float scale = 1.f / sqrtf((float)D);
   if (kind == 1) {
-    hipLaunchKernelGGL((attn_block_scores_kernel<D, true>), dim3(nq, H, B), dim3(256), 0,
-                       stream, base, (float*)nullptr, (const __bf16*)Q,
-                       (const float*)stats, (const float*)quant, H, Hkv, Sq, nq, nk, scale);
+    hipLaunchKernelGGL(attn_block_minmax_kernel<D>, dim3(nq, H, B), dim3(256), 0, stream,
+                       base, (const __bf16*)Q, (const float*)stats, H, Hkv, Sq, nq, nk,
+                       scale);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(attn_block_quantile_kernel, dim3(Hkv, B), dim3(256), 0, stream,
                      stats, quant, Hkv, nk, D, low, high);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_block_scores_kernel<D, false>), dim3(nq, H, B), dim3(256), 0,
+  hipLaunchKernelGGL(attn_block_scores_kernel<D>, dim3(nq, H, B), dim3(64), 0,
                      stream, base, rescue, (const __bf16*)Q, (const float*)stats,
                      (const float*)quant, H, Hkv, Sq, nq, nk, scale);
   return hipGetLastError();
