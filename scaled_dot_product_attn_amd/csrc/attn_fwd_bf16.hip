@@ -54,6 +54,10 @@
 #include "../../include/attn.h"
 #include "attn_common.h"
 
+#ifndef KFWD_OP_DEPTH
+#define KFWD_OP_DEPTH 6
+#endif
+
 namespace attn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -69,6 +73,7 @@ constexpr int kGroupThreads = kFwdThreads / 2;
 constexpr int kFwdTileM = kFwdWaves * 32;  // query rows per workgroup
 constexpr int kFwdTileN = 64;              // keys per tile
 constexpr float kLazyRescale = 8.0f;       // log2 headroom before m is raised
+constexpr int kFwdOpDepth = KFWD_OP_DEPTH; // LDS operand reads in flight per wave
 // Word 3 of a gfx9-family buffer resource (32-bit data format, no swizzle):
 // a raw buffer whose out-of-range reads return zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
@@ -143,7 +148,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     float* __restrict__ LSE, int B, int H, int Hkv, int Sq, int Sk, int causal,
     int window, int input_pos, const int32_t* __restrict__ k_lengths,
-    float scale_log2, FlexArgs fx, const uint8_t* __restrict__ keep) {
+    float scale_log2, FlexArgs fx, const uint8_t* __restrict__ keep,
+    int n_wg) {
   using L = FwdLds<D>;
   constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int DBLK = D / 32;     // 32-wide blocks of the head dimension
@@ -165,11 +171,32 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const int lrow = lane & 31;  // query row (within the wave) this lane owns
   const int half = lane >> 5;  // which half of each MFMA k-slice this lane feeds
 
-  // ---- work item: heaviest query tiles first, XCD-grouped by KV head ----
+  // ---- work items: heaviest query tiles first, XCD-grouped by KV head ----
   const int G = H / Hkv;
   const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
   const int total = nqt * H * B;
-  const int lid = blockIdx.x;
+  // Persistent launch (n_wg > 0 workgroups, a multiple of 8, one per CU): the
+  // workgroup on XCD x (= blockIdx % 8) walks that XCD's item positions in a
+  // snake order (c, 2C-1-c, 2C+c, ...), which pairs heavy and light causal
+  // tiles; the few items past 8 * (total / 8) come in a last round.
+  // Otherwise one workgroup per item.
+  const bool persistent = n_wg > 0;
+  const int per_xcd = total >> 3;
+  const int wg_x = n_wg >> 3;
+  const int rounds = persistent ? (per_xcd + wg_x - 1) / wg_x + 1 : 1;
+  for (int round = 0; round < rounds; ++round) {
+  int lid = blockIdx.x;
+  if (persistent) {
+    const int c = (int)blockIdx.x >> 3;
+    if (round < rounds - 1) {
+      const int pos = (round & 1) ? (round + 1) * wg_x - 1 - c : round * wg_x + c;
+      if (pos >= per_xcd) continue;
+      lid = (pos << 3) | ((int)blockIdx.x & 7);
+    } else {
+      lid = (per_xcd << 3) + (int)blockIdx.x;
+      if (lid >= total) continue;
+    }
+  }
   int wid = lid;
   {
     // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
@@ -381,12 +408,77 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   f32x16_t s[2];           // S^T of the current tile (two 32-key blocks)
   u32x4_t pb[2][2];        // P^T of the previous tile, packed bf16 (MFMA B operands)
 
+  // flex: the bias of this lane's row for the keys of the idx-th walked tile:
+  // j0 + kb2*32 + q4*8 + half*4 + e, held in register q4*4 + e of block kb2
+  // (the S^T accumulator order)
+  auto bias_loads = [&](int idx) {
+    const int jb = tile_at(idx) * kFwdTileN + half * 4;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jb + kb2 * 32 + (r >> 2) * 8 + (r & 3);
+        bias_t[kb2][r] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(bias_rsrc, (bias_row + j) * 4, 0, 0));
+      }
+  };
+
   // M-phase of the idx-th walked tile: O += P V of the previous one, then
   // S = K Q^T of this one; tile idx sits in LDS buffer idx & 1
   auto m_phase = [&](int idx, bool do_pv, bool do_s) {
     if constexpr (SPARSE) {
       do_pv = do_pv && wave_keeps(idx - 1);
       do_s = do_s && wave_keeps(idx);
+    }
+    if (!FLEX && do_pv && do_s) {
+      // Steady state: the 32 products of the phase with their LDS operand
+      // reads kept kFwdOpDepth ahead (left to itself the compiler keeps only
+      // one or two in flight and each MFMA waits for its read).  Consecutive
+      // products go to different accumulators.  (The flex kernels keep the
+      // plain order: their extra registers leave no room for the ring.)
+      const char* vb = smem + L::kOffV + ((idx - 1) & 1) * L::kBytesV;
+      const char* kb = smem + (idx & 1) * L::kBytesK;
+      constexpr int NPV = DBLK * 4;
+      constexpr int NOP = NPV + 2 * KSTEPS;
+      auto op_addr = [&](int i) -> const char* {
+        if (i < NPV) {
+          const int pr = i / DBLK, db = i % DBLK;  // pr = kb2 * 2 + st
+          return vb + (db * 32 + lrow) * L::kRowV + half * 16 + pr * 32;
+        }
+        const int j = i - NPV, ks = j >> 1, kb2 = j & 1;
+        return kb + (kb2 * 32 + lrow) * L::kRowK + half * 16 + ks * 32;
+      };
+      bf16x8_t ring[kFwdOpDepth];
+#pragma unroll
+      for (int i = 0; i < kFwdOpDepth; ++i) ring[i] = *(const bf16x8_t*)op_addr(i);
+      s[0] = s[1] = f32x16_t{};
+#pragma unroll
+      for (int i = 0; i < NOP; ++i) {
+        const bf16x8_t a = ring[i % kFwdOpDepth];
+        if (i + kFwdOpDepth < NOP)
+          ring[i % kFwdOpDepth] = *(const bf16x8_t*)op_addr(i + kFwdOpDepth);
+        if (i < NPV) {
+          const int pr = i / DBLK, db = i % DBLK;
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a, __builtin_bit_cast(bf16x8_t, pb[pr >> 1][pr & 1]), oacc[db], 0, 0, 0);
+        } else {
+          const int j = i - NPV, ks = j >> 1, kb2 = j & 1;
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb2], 0, 0, 0);
+        }
+      }
+      // hold the scheduler to that order: kFwdOpDepth reads, then one MFMA
+      // and one read alternately, then the last MFMAs (0x100 = LDS read,
+      // 0x008 = MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, kFwdOpDepth, 0);
+#pragma unroll
+      for (int i = 0; i < NOP - kFwdOpDepth; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kFwdOpDepth, 0);
+      // and keep the last products ahead of the barrier that ends the phase
+      asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+      return;
     }
     if (do_pv) {
       const char* vb = smem + L::kOffV + ((idx - 1) & 1) * L::kBytesV;
@@ -403,20 +495,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
           }
       }
     }
-    if (FLEX && do_s && has_bias) {
-      // lane's keys of the tile: j0 + kb2*32 + q4*8 + half*4 + e, held in
-      // register q4*4 + e of block kb2 (the S^T accumulator order)
-      const int jb = tile_at(idx) * kFwdTileN + half * 4;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = jb + kb2 * 32 + (r >> 2) * 8 + (r & 3);
-          bias_t[kb2][r] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(
-                         bias_rsrc, (bias_row + j) * 4, 0, 0));
-        }
-    }
+    if (FLEX && do_s && has_bias) bias_loads(idx);
     if (do_s) {
       const char* kb = smem + (idx & 1) * L::kBytesK;
 #pragma unroll
@@ -558,6 +637,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         pb[kb2][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
       }
     l_run += psum;
+    // Pin P here: left alone, the compiler sinks the exponentials past the
+    // barrier into the next MFMA phase (their only user), which serialises
+    // them with that phase's products instead of overlapping them with the
+    // other group's.
+    asm volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]),
+                 "+v"(l_run));
     if (idx + 1 < n_tiles) stash((idx + 1) & 1);
     if (idx + 2 < n_tiles) fetch(tile_at(idx + 2));
   };
@@ -602,6 +687,26 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       LSE[(size_t)(b * H + h) * Sq + qi] = lse;
     }
   }
+  __syncthreads();  // LDS is reused by the next item
+  }
+}
+
+// Number of persistent workgroups for `total` items (one per CU, a multiple
+// of 8), or 0 for a launch of one workgroup per item when there are too few
+// items to pair up.
+static int persistent_workgroups(long long total) {
+  static int cu_count[64];  // per device; 0 = not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = -1;
+    cu_count[dev] = n > 0 ? n : -1;
+  }
+  const int n_wg = (cu_count[dev] / 8) * 8;
+  if (n_wg < 8 || total < 2LL * n_wg) return 0;
+  return n_wg;
 }
 
 template <int D>
@@ -612,12 +717,14 @@ hipError_t launch_fwd_bf16(void* O, const void* Q, const void* K,
                            hipStream_t stream) {
   const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
   const long long total = (long long)nqt * H * B;
+  const int n_wg = persistent_workgroups(total);
+  const unsigned grid = n_wg > 0 ? (unsigned)n_wg : (unsigned)total;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, false>), dim3((unsigned)total),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, false>), dim3(grid),
                      dim3(kFwdThreads), 0, stream, (__bf16*)O,
                      (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                      B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                     scale_log2, FlexArgs{}, (const uint8_t*)nullptr);
+                     scale_log2, FlexArgs{}, (const uint8_t*)nullptr, n_wg);
   return hipGetLastError();
 }
 
@@ -629,6 +736,8 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
                            const attn_flex_t* f, hipStream_t stream) {
   const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
   const long long total = (long long)nqt * H * B;
+  const int n_wg = persistent_workgroups(total);
+  const unsigned grid = n_wg > 0 ? (unsigned)n_wg : (unsigned)total;
   FlexArgs fx{};
   fx.q_lengths = f->q_lengths;
   fx.alibi = f->alibi_slopes;
@@ -643,17 +752,17 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
   fx.qk_scale = f->qk_scale > 0.f ? f->qk_scale : 1.f / sqrtf((float)D);
   // the bias tile costs 32 registers per lane: a kernel of its own
   if (fx.bias)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, false>), dim3((unsigned)total),
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, false>), dim3(grid),
                        dim3(kFwdThreads), 0, stream, (__bf16*)O,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                        B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                       0.f, fx, (const uint8_t*)nullptr);
+                       0.f, fx, (const uint8_t*)nullptr, n_wg);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false, false>), dim3((unsigned)total),
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false, false>), dim3(grid),
                        dim3(kFwdThreads), 0, stream, (__bf16*)O,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                        B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                       0.f, fx, (const uint8_t*)nullptr);
+                       0.f, fx, (const uint8_t*)nullptr, n_wg);
   return hipGetLastError();
 }
 
@@ -665,12 +774,14 @@ hipError_t launch_fwd_sparse(void* O, const void* Q, const void* K,
                              const uint8_t* keep, hipStream_t stream) {
   const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
   const long long total = (long long)nqt * H * B;
+  const int n_wg = persistent_workgroups(total);
+  const unsigned grid = n_wg > 0 ? (unsigned)n_wg : (unsigned)total;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, true>), dim3((unsigned)total),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, true>), dim3(grid),
                      dim3(kFwdThreads), 0, stream, (__bf16*)O,
                      (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                      B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                     scale_log2, FlexArgs{}, keep);
+                     scale_log2, FlexArgs{}, keep, n_wg);
   return hipGetLastError();
 }
 
