@@ -114,6 +114,11 @@ struct FwdLds {
   static constexpr int kOffDoc = kTotal;
   static constexpr int kBytesDoc = kFwdTileN * 4;
   static constexpr int kTotalFlex = kTotal + 2 * kBytesDoc;
+  // output staging: per wave its 32 rows of D bf16, padded like K
+  static constexpr int kRowO = D * 2 + 16;
+  static constexpr int kBytesOWave = 32 * kRowO;
+  static constexpr int kOffO = kTotalFlex;
+  static constexpr int kTotalAll = kOffO + (kFwdThreads / 64) * kBytesOWave;
 };
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
@@ -156,7 +161,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   constexpr int KLOADS = kFwdTileN * D / 8 / kGroupThreads;  // K loads/thread
   constexpr int VTHREADS = (kFwdTileN / 4) * (D / 8);        // threads staging V
 
-  __shared__ __attribute__((aligned(16))) char smem[FLEX ? L::kTotalFlex : L::kTotal];
+  __shared__ __attribute__((aligned(16))) char smem[L::kTotalAll];
   // block-sparse: the key tiles some row block of this workgroup keeps, and
   // per listed tile the keep bits of the four 64-row blocks
   __shared__ int16_t s_list[SPARSE ? kSparseMaxTiles : 1];
@@ -666,9 +671,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
 
   // ---- epilogue ----
   const float l_tot = pair_sum(l_run);
-  if (qi < Sq) {
+  {
+    // O goes out through LDS: a lane holds 4-element pieces of its own row,
+    // so storing them directly writes 8 bytes into each of 64 rows per
+    // instruction; staged in the wave's own LDS rows and read back as 16-byte
+    // chunks, each 16 lanes write one whole row.  The wave only reads what it
+    // wrote, so no barrier is needed.
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* op = O + q_base + (size_t)qi * D;
+    char* ost = smem + L::kOffO + wave * L::kBytesOWave;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -678,14 +688,24 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
                                  oacc[db][r4 * 4 + 1] * inv),
                      pack_bf16x2(oacc[db][r4 * 4 + 2] * inv,
                                  oacc[db][r4 * 4 + 3] * inv)};
-        *(u32x2_t*)(op + d) = w;
+        *(u32x2_t*)(ost + lrow * L::kRowO + d * 2) = w;
       }
-    if (LSE && half == 0) {
-      const float lse = l_tot > 0.f
-                            ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994530942f
-                            : -INFINITY;
-      LSE[(size_t)(b * H + h) * Sq + qi] = lse;
+    __builtin_amdgcn_wave_barrier();
+    constexpr int CHUNKS = D / 8;  // 16-byte chunks per row
+#pragma unroll
+    for (int i = 0; i < 32 * CHUNKS / 64; ++i) {
+      const int c = i * 64 + lane;
+      const int row = c / CHUNKS, ch = c - row * CHUNKS;
+      const u32x4_t v = *(const u32x4_t*)(ost + row * L::kRowO + ch * 16);
+      const int qrow = i0 + wave * 32 + row;
+      if (qrow < Sq) *(u32x4_t*)(O + q_base + (size_t)qrow * D + ch * 8) = v;
     }
+  }
+  if (LSE && qi < Sq && half == 0) {
+    const float lse = l_tot > 0.f
+                          ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994530942f
+                          : -INFINITY;
+    LSE[(size_t)(b * H + h) * Sq + qi] = lse;
   }
   __syncthreads();  // LDS is reused by the next item
   }
