@@ -51,6 +51,10 @@ constexpr int kQTile = 64;         // query rows per step of the dK/dV kernel
 constexpr int kDqRows = 128;       // query rows per dQ workgroup
 constexpr int kDqKeys = 64;        // keys per step of the dQ kernel
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, out-of-range reads = 0
+#ifndef KBWD_OP_DEPTH
+#define KBWD_OP_DEPTH 4
+#endif
+constexpr int kBwdOpDepth = KBWD_OP_DEPTH;  // LDS operand reads in flight per wave
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
@@ -221,14 +225,17 @@ void attn_bwd_dkdv_kernel(
   const int st_t = BOTH ? tid : (tid % STG_PER);
   const int quad = st_t % (kQTile / 4);
   const int dch = st_t / (kQTile / 4);
-  auto item_rows = [&](int it, int& h, int& i0) {
-    const int hh = it / nq;
-    h = g * G + hh;
-    i0 = (qt_lo + (it - hh * nq)) * kQTile;
+  // items run over the query tiles of one head, then the next head; an
+  // item is kept as (head offset hh, tile q) and advanced without division
+  auto advance = [&](int& hh, int& q) {
+    if (++q == nq) {
+      q = 0;
+      ++hh;
+    }
   };
-  auto fetch = [&](int it) {
-    int h, i0;
-    item_rows(it, h, i0);
+  auto fetch = [&](int hh, int q) {
+    const int h = g * G + hh;
+    const int i0 = (qt_lo + q) * kQTile;
     const size_t rb = (size_t)(b * H + h) * Sq;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -259,7 +266,7 @@ void attn_bwd_dkdv_kernel(
 
   const float sl2 = scale * kLog2e;
   if (n_items > 0) {
-    fetch(0);
+    fetch(0, 0);
     stash(0);
     __syncthreads();
   }
@@ -273,38 +280,55 @@ void attn_bwd_dkdv_kernel(
   }
   const unsigned r_width = (unsigned)max(r_hi - r_lo, 0);
 
+  int cur_hh = 0, cur_q = 0;  // the item of iteration it
   for (int it = 0; it < n_items; ++it) {
     const char* st = smem + (it & 1) * L::kStage;
-    int h, i0;
-    item_rows(it, h, i0);
-    // mask per element unless every (row, key) pair of the tile is allowed
+    const int i0 = (qt_lo + cur_q) * kQTile;
+    int nxt_hh = cur_hh, nxt_q = cur_q;
+    advance(nxt_hh, nxt_q);
+    // mask per element unless every (row, key) pair of the tile is allowed:
+    // the keys all rows allow run from lo of the last row to hi of the first
     const int i1 = min(i0 + kQTile, Sq);
-    const KvGeometry geo = kv_geometry(i0, i1, kl, causal, window, input_pos);
-    const bool partial = i1 - i0 < kQTile ||
-                         tile_class(geo, j0, kKvTile) != kTileFull;
+    const RowRange first = row_range(i0, kl, causal, window, input_pos);
+    const RowRange last = row_range(i1 - 1, kl, causal, window, input_pos);
+    const bool partial =
+        i1 - i0 < kQTile || !(last.lo <= j0 && j0 + kKvTile <= first.hi);
 
-    // S and dP (64 queries x 32 keys), two 32-query blocks; each block's
-    // operand rows are read before its MFMAs so the reads overlap
+    // S and dP (64 queries x 32 keys), two 32-query blocks.  The LDS
+    // operands stream through a ring kept kBwdOpDepth reads ahead of the
+    // MFMAs (a whole block of operands in registers leaves too few for the
+    // accumulators); operand i: query block i / (2 KSTEPS), k-step
+    // (i / 2) % KSTEPS, Q rows for even i and dO rows for odd i.
     f32x16_t s[2], dp[2];
+    s[0] = s[1] = dp[0] = dp[1] = f32x16_t{};
+    {
+      constexpr int NOP = 4 * KSTEPS;
+      auto op = [&](int i) -> const bf16x8_t* {
+        const int qb = i / (2 * KSTEPS), ks = (i / 2) % KSTEPS;
+        const int off = (i & 1) ? L::kOffO : L::kOffQ;
+        return (const bf16x8_t*)(st + off + (qb * 32 + lcol) * T::kRow + half * 16 + ks * 32);
+      };
+      bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const char* qrow = st + L::kOffQ + (qb * 32 + lcol) * T::kRow + half * 16;
-      const char* orow = st + L::kOffO + (qb * 32 + lcol) * T::kRow + half * 16;
-      bf16x8_t aq[KSTEPS], ao[KSTEPS];
+      for (int i = 0; i < kBwdOpDepth; ++i) ring[i] = *op(i);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        aq[ks] = *(const bf16x8_t*)(qrow + ks * 32);
-        ao[ks] = *(const bf16x8_t*)(orow + ks * 32);
+      for (int i = 0; i < NOP; ++i) {
+        const bf16x8_t a = ring[i % kBwdOpDepth];
+        if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = *op(i + kBwdOpDepth);
+        const int qb = i / (2 * KSTEPS), ks = (i / 2) % KSTEPS;
+        if (i & 1)
+          dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vreg[ks], dp[qb], 0, 0, 0);
+        else
+          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[ks], s[qb], 0, 0, 0);
       }
-      s[qb] = dp[qb] = f32x16_t{};
+      __builtin_amdgcn_sched_group_barrier(0x100, kBwdOpDepth, 0);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], kreg[ks], s[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[ks], vreg[ks], dp[qb], 0, 0, 0);
+      for (int i = 0; i < NOP - kBwdOpDepth; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, kBwdOpDepth, 0);
     }
-    // the next tile's rows are requested now and land during the rest
-    if (it + 1 < n_items) fetch(it + 1);
     // P = exp2(s * scale * log2e - L2), dS = P (dP - delta); lane's queries are
     // i0 + qb*32 + 8*(r/4) + 4*half + r%4
     u32x4_t pk[4], dsk[4];  // packed bf16, one 16-query k-step each
@@ -333,27 +357,45 @@ void attn_bwd_dkdv_kernel(
         dsk[kq][w + 1] = pack_bf16x2(dv[2], dv[3]);
       }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (d x keys), k over the 64 queries
+    // the next tile's rows are requested now and land during the rest
+    if (it + 1 < n_items) fetch(nxt_hh, nxt_q);
+    // dV^T += dO^T P, dK^T += Q^T dS (d x keys), k over the 64 queries;
+    // operand i: d block i / 8, query k-step (i / 2) % 4, dO^T rows for even
+    // i and Q^T rows for odd i, through the same kind of ring
+    {
+      constexpr int NOP = DBLK * 8;
+      auto op = [&](int i) -> const bf16x8_t* {
+        const int db = i / 8, kq = (i / 2) % 4;
+        const int off = (i & 1) ? L::kOffQT : L::kOffOT;
+        return (const bf16x8_t*)(st + off + (db * 32 + lcol) * T::kRowT + half * 16 + kq * 32);
+      };
+      bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const char* ot = st + L::kOffOT + (db * 32 + lcol) * T::kRowT + half * 16;
-      const char* qt = st + L::kOffQT + (db * 32 + lcol) * T::kRowT + half * 16;
-      bf16x8_t ao[4], aq[4];
+      for (int i = 0; i < kBwdOpDepth; ++i) ring[i] = *op(i);
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        ao[kq] = *(const bf16x8_t*)(ot + kq * 32);
-        aq[kq] = *(const bf16x8_t*)(qt + kq * 32);
+      for (int i = 0; i < NOP; ++i) {
+        const bf16x8_t a = ring[i % kBwdOpDepth];
+        if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = *op(i + kBwdOpDepth);
+        const int db = i / 8, kq = (i / 2) % 4;
+        if (i & 1)
+          dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a, __builtin_bit_cast(bf16x8_t, dsk[kq]), dkT[db], 0, 0, 0);
+        else
+          dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a, __builtin_bit_cast(bf16x8_t, pk[kq]), dvT[db], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, kBwdOpDepth, 0);
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            ao[kq], __builtin_bit_cast(bf16x8_t, pk[kq]), dvT[db], 0, 0, 0);
-        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            aq[kq], __builtin_bit_cast(bf16x8_t, dsk[kq]), dkT[db], 0, 0, 0);
+      for (int i = 0; i < NOP - kBwdOpDepth; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, kBwdOpDepth, 0);
     }
     if (it + 1 < n_items) stash((it + 1) & 1);
     __syncthreads();
+    cur_hh = nxt_hh;
+    cur_q = nxt_q;
   }
 
   // ---- store: lane owns key kj, holds d = db*32 + 8*(r/4) + 4*half + r%4 ----
@@ -492,24 +534,38 @@ void attn_bwd_dq_kernel(
     const int it = kt - kt_first;
     const char* st = smem + (it & 1) * L::kStage;
     const int j0 = kt * kDqKeys;
-    // S^T and dP^T (64 keys x 32 queries), two 32-key blocks
+    // S^T and dP^T (64 keys x 32 queries), two 32-key blocks; operand i: key
+    // block i / (2 KSTEPS), k-step (i / 2) % KSTEPS, K rows for even i and V
+    // rows for odd i, through a ring kBwdOpDepth reads ahead of the MFMAs
     f32x16_t s[2], dp[2];
+    s[0] = s[1] = dp[0] = dp[1] = f32x16_t{};
+    {
+      constexpr int NOP = 4 * KSTEPS;
+      auto op = [&](int i) -> const bf16x8_t* {
+        const int kb = i / (2 * KSTEPS), ks = (i / 2) % KSTEPS;
+        const int off = (i & 1) ? L::kOffV : L::kOffK;
+        return (const bf16x8_t*)(st + off + (kb * 32 + lrow) * T::kRow + half * 16 + ks * 32);
+      };
+      bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const char* krow = st + L::kOffK + (kb * 32 + lrow) * T::kRow + half * 16;
-      const char* vrow = st + L::kOffV + (kb * 32 + lrow) * T::kRow + half * 16;
-      bf16x8_t ak[KSTEPS], av[KSTEPS];
+      for (int i = 0; i < kBwdOpDepth; ++i) ring[i] = *op(i);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        ak[ks] = *(const bf16x8_t*)(krow + ks * 32);
-        av[ks] = *(const bf16x8_t*)(vrow + ks * 32);
+      for (int i = 0; i < NOP; ++i) {
+        const bf16x8_t a = ring[i % kBwdOpDepth];
+        if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = *op(i + kBwdOpDepth);
+        const int kb = i / (2 * KSTEPS), ks = (i / 2) % KSTEPS;
+        if (i & 1)
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, oreg[ks], dp[kb], 0, 0, 0);
+        else
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb], 0, 0, 0);
       }
-      s[kb] = dp[kb] = f32x16_t{};
+      __builtin_amdgcn_sched_group_barrier(0x100, kBwdOpDepth, 0);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qreg[ks], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks], oreg[ks], dp[kb], 0, 0, 0);
+      for (int i = 0; i < NOP - kBwdOpDepth; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, kBwdOpDepth, 0);
     }
     // the next tile's keys are requested now and land during the rest
     if (kt + 1 <= kt_last) fetch(kt + 1);
@@ -534,17 +590,31 @@ void attn_bwd_dq_kernel(
         }
         dsk[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dv[0], dv[1]);
       }
-    // dQ^T (d x queries) += K^T (d x keys) dS^T (keys x queries)
+    // dQ^T (d x queries) += K^T (d x keys) dS^T (keys x queries); operand i:
+    // d block i / 4, key k-step i % 4
+    {
+      constexpr int NOP = DBLK * 4;
+      auto op = [&](int i) -> const bf16x8_t* {
+        return (const bf16x8_t*)(st + L::kOffKT + ((i / 4) * 32 + lrow) * T::kRowT + half * 16 +
+                                 (i % 4) * 32);
+      };
+      bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const char* arow = st + L::kOffKT + (db * 32 + lrow) * T::kRowT + half * 16;
-      bf16x8_t a[4];
+      for (int i = 0; i < kBwdOpDepth; ++i) ring[i] = *op(i);
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq) a[kq] = *(const bf16x8_t*)(arow + kq * 32);
+      for (int i = 0; i < NOP; ++i) {
+        const bf16x8_t a = ring[i % kBwdOpDepth];
+        if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = *op(i + kBwdOpDepth);
+        dqT[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, __builtin_bit_cast(bf16x8_t, dsk[i % 4]), dqT[i / 4], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kBwdOpDepth, 0);
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq)
-        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            a[kq], __builtin_bit_cast(bf16x8_t, dsk[kq]), dqT[db], 0, 0, 0);
+      for (int i = 0; i < NOP - kBwdOpDepth; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kBwdOpDepth, 0);
     }
     if (kt + 1 <= kt_last) stash((it + 1) & 1);
     __syncthreads();
