@@ -13,8 +13,9 @@
 // Block masks: keep the blocks within alpha of the row maximum (relative),
 // the k best of a row (top-k, ties to the lower index), or a diagonal band.
 //
-// These are small, HBM/latency-bound kernels (float32 vector ALU, no matrix
-// cores): one pass over K for the block statistics, one over Q for the scores.
+// The block statistics and masks are small float32 vector-ALU kernels (one
+// pass over K); the centroid scores, a Q C^T contraction, run on the matrix
+// cores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -144,134 +145,175 @@ __global__ __launch_bounds__(256) void attn_block_quantile_kernel(
   }
 }
 
-// Centroid (RBS) scores per (query block, query head, batch), one wave:
-// block scores against every key block.  Lane = key block (blocks lane, lane + 64, ...), holding the
-// block's summary in registers; the query block (float32, with its row norms)
-// sits in LDS and every lane reads the same row (broadcast).  The log-sum-exp
-// over the block's query tokens is an online update inside each lane, so no
-// cross-lane reduction is needed.
-template <int D>
-__global__ __launch_bounds__(64) void attn_block_scores_kernel(
+// Block scores on the matrix cores.  A workgroup of four waves takes
+// four query blocks of one (query head, batch); wave w scores block 4x + w
+// against every key block.  Per chunk of 64 key blocks the workgroup stages
+// the centroids in LDS split into three bf16 planes, c = c0 + c1 + c2 (each
+// the bf16 rounding of what the previous ones leave), so that the bf16 MFMA
+// products q.c0 + q.c1 + q.c2 with exact bf16 q and float32 accumulation give
+// q.c to within 2^-27 |q||c| per term, float32 quality.  S = Q C^T comes out
+// in the accumulator layout (lane: one key block, 16 query rows per 32 x 32
+// tile), so the log-sum-exp over the 64 query rows is in-lane plus one
+// exchange with lane ^ 32; the rescue term adds ||q_i|| r_b beta_b before
+// the exponential.
+// BOX: the min/max box bound instead of the centroid.  With m = (lo + hi) / 2
+// and r = (hi - lo) / 2 per dimension, max(q lo, q hi) = q m + |q| r for
+// either sign of q, so the bound is the contraction [q, |q|] . [m; r]: six
+// planes (m and r, three each) and |q| by clearing the sign bits.
+template <int D, bool BOX>
+__global__ __launch_bounds__(256) void attn_block_scores_kernel(
     float* __restrict__ base_out, float* __restrict__ rescue_out,
     const __bf16* __restrict__ Q, const float* __restrict__ stats,
     const float* __restrict__ quant, int H, int Hkv, int Sq, int nq, int nk,
     float scale) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  __shared__ __attribute__((aligned(16))) float s_q[kBlock][D];
-  __shared__ float s_qn[kBlock];
-  const int a = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  typedef float f32x16_t __attribute__((ext_vector_type(16)));
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  constexpr int KSTEPS = D / 16;
+  constexpr int ROW = D * 2 + 16;     // padded bf16 centroid row in LDS
+  constexpr int PLANE = kBlock * ROW;
+  constexpr int NPL = BOX ? 6 : 3;    // bf16 planes staged per chunk
+  __shared__ __attribute__((aligned(16))) char s_c[NPL * PLANE];
+  __shared__ float s_qn[4][kBlock];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lcol = lane & 31, half = lane >> 5;
+  const int a = blockIdx.x * 4 + wave;  // this wave's query block
+  const bool live = a < nq;
   const int g = h / (H / Hkv);
   const int i0 = a * kBlock;
-  const int nrows = min(kBlock, Sq - i0);
-  // stage the query block as float32 and its row norms
-  {
-    const __bf16* qb = Q + ((size_t)(b * H + h) * Sq + i0) * D;
-    for (int x = lane; x < nrows * (D / 8); x += 64) {
-      const int r = x / (D / 8), c = x % (D / 8);
-      const u32x4_t w = *(const u32x4_t*)(qb + (size_t)r * D + c * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s_q[r][c * 8 + 2 * e] = bf16_lo(w[e]);
-        s_q[r][c * 8 + 2 * e + 1] = bf16_hi(w[e]);
-      }
-    }
-    __syncthreads();
-    if (lane < nrows) {
-      float n2 = 0.f;
-      for (int d = 0; d < D; ++d) n2 = __builtin_fmaf(s_q[lane][d], s_q[lane][d], n2);
-      s_qn[lane] = sqrtf(n2);
-    }
-    __syncthreads();
-  }
-  const float* st = stats + (size_t)(b * Hkv + g) * nk * (3 * D + 1);
-  const float r_low = quant[(size_t)(b * Hkv + g) * 2];
-  const float r_high = quant[(size_t)(b * Hkv + g) * 2 + 1];
-  const size_t row = ((size_t)(b * H + h) * nq + a) * nk;
-  for (int kb = lane; kb < nk; kb += 64) {
-    float v0[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) v0[d] = st[(size_t)kb * D + d];
-    const float r = st[(size_t)3 * nk * D + kb];
-    const float beta = r_high == r_low
-                           ? (r > r_low ? 1.f : 0.f)
-                           : fminf(fmaxf((r - r_low) / (r_high - r_low), 0.f), 1.f);
-    const float w = r * beta;
-    float m1 = -INFINITY, s1 = 0.f, m2 = -INFINITY, s2 = 0.f;
-    for (int r = 0; r < nrows; ++r) {
-      float part[8] = {};
-#pragma unroll
-      for (int d4 = 0; d4 < D / 4; ++d4) {
-        const f32x4_t x = *(const f32x4_t*)&s_q[r][d4 * 4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = d4 * 4 + e;
-          part[d & 7] = __builtin_fmaf(x[e], v0[d], part[d & 7]);
-        }
-      }
-      float acc = 0.f;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) acc += part[p];
-      const float e1 = acc * scale;
-      const float n1 = fmaxf(m1, e1);
-      s1 = s1 * __expf(m1 - n1) + __expf(e1 - n1);
-      m1 = n1;
-      const float e2 = __builtin_fmaf(s_qn[r], w, acc) * scale;
-      const float n2 = fmaxf(m2, e2);
-      s2 = s2 * __expf(m2 - n2) + __expf(e2 - n2);
-      m2 = n2;
-    }
-    base_out[row + kb] = m1 + __logf(s1);
-    if (rescue_out) rescue_out[row + kb] = m2 + __logf(s2);
-  }
-}
 
-// Min/max box-bound scores per (query block, query head, batch).  Lane = query
-// token of the block; wave w takes key blocks w, w + 4, ...; the block's lo /
-// hi rows are wave-uniform (scalar loads), the log-sum-exp over the block's
-// tokens is a wave reduction.  (The lane-per-key-block layout of the centroid
-// kernel would need both 2 x D summaries in registers.)
-template <int D>
-__global__ __launch_bounds__(256) void attn_block_minmax_kernel(
-    float* __restrict__ base_out, const __bf16* __restrict__ Q,
-    const float* __restrict__ stats, int H, int Hkv, int Sq, int nq, int nk,
-    float scale) {
-  const int a = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loads
-  const int g = h / (H / Hkv);
-  const int i = a * kBlock + lane;
-  const bool live = i < Sq;
-  float q[D];
-  {
-    const u32x4_t* qp = (const u32x4_t*)(Q + ((size_t)(b * H + h) * Sq + (live ? i : 0)) * D);
+  // Q rows as A operands: qa[rt][ks] = row rt*32 + lcol, d = 16 ks + 8 half..
+  bf16x8_t qa[2][KSTEPS];
+  float qn2[2] = {0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const u32x4_t w = qp[c];
+  for (int rt = 0; rt < 2; ++rt) {
+    const int i = i0 + rt * 32 + lcol;
+    const bool ok = live && i < Sq;
+    const __bf16* qp = Q + ((size_t)(b * H + h) * Sq + (ok ? i : 0)) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4_t w = ok ? *(const u32x4_t*)(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
+      qa[rt][ks] = __builtin_bit_cast(bf16x8_t, w);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        q[c * 8 + 2 * e] = bf16_lo(w[e]);
-        q[c * 8 + 2 * e + 1] = bf16_hi(w[e]);
+        const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
+        qn2[rt] = __builtin_fmaf(x0, x0, __builtin_fmaf(x1, x1, qn2[rt]));
       }
     }
   }
-  const float* st = stats + (size_t)(b * Hkv + g) * nk * (3 * D + 1);
-  const size_t row = ((size_t)(b * H + h) * nq + a) * nk;
-  for (int kb = wave; kb < nk; kb += 4) {
-    float ell;
-    {
-      const float* lo = st + (size_t)nk * D + (size_t)kb * D;
-      const float* hi = st + (size_t)2 * nk * D + (size_t)kb * D;
-      float acc = 0.f;
+  // ||q|| of the wave's 64 rows into LDS (the two halves of a row sit in lanes l, l ^ 32)
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc += fmaxf(q[d] * lo[d], q[d] * hi[d]);
-      ell = acc * scale;
+  for (int rt = 0; rt < 2; ++rt) {
+    const float t = qn2[rt] + __shfl_xor(qn2[rt], 32);
+    if (half == 0) s_qn[wave][rt * 32 + lcol] = sqrtf(t);
+  }
+  __syncthreads();
+  // query rows of the block below Sq; the lane's rows of the accumulator
+  // layout are rt*32 + 8 (r/4) + 4 half + r%4
+  const int nrows = live ? min(kBlock, Sq - i0) : 0;
+  auto row_of = [&](int rt, int r) { return rt * 32 + (r >> 2) * 8 + half * 4 + (r & 3); };
+
+  const float* st = stats + (size_t)(b * Hkv + g) * nk * (3 * D + 1);
+  // radius quantiles of the head (centroid scores only; the box bound has none)
+  const float r_low = BOX ? 0.f : quant[(size_t)(b * Hkv + g) * 2];
+  const float r_high = BOX ? 0.f : quant[(size_t)(b * Hkv + g) * 2 + 1];
+  const size_t orow = ((size_t)(b * H + h) * nq + (live ? a : 0)) * nk;
+
+  for (int c0 = 0; c0 < nk; c0 += kBlock) {
+    // stage centroids c0 .. c0 + 63 (zeros past nk) as three bf16 planes
+    __syncthreads();  // the previous chunk's reads are done
+    auto split3 = [&](const f32x4_t c, char* dst) {
+      bf16x4_t p0, p1, p2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 h0 = (__bf16)c[e];
+        const float r1 = c[e] - (float)h0;
+        const __bf16 h1 = (__bf16)r1;
+        const float r2 = r1 - (float)h1;
+        p0[e] = h0;
+        p1[e] = h1;
+        p2[e] = (__bf16)r2;
+      }
+      *(bf16x4_t*)(dst) = p0;
+      *(bf16x4_t*)(dst + PLANE) = p1;
+      *(bf16x4_t*)(dst + 2 * PLANE) = p2;
+    };
+    for (int x = tid; x < kBlock * (D / 4); x += 256) {
+      const int kb = x / (D / 4), d4 = x % (D / 4);
+      const bool in = c0 + kb < nk;
+      char* dst = s_c + kb * ROW + d4 * 8;
+      const size_t off = (size_t)(c0 + kb) * D + d4 * 4;
+      if constexpr (BOX) {
+        const f32x4_t lo = in ? *(const f32x4_t*)(st + (size_t)nk * D + off) : f32x4_t{};
+        const f32x4_t hi = in ? *(const f32x4_t*)(st + (size_t)2 * nk * D + off) : f32x4_t{};
+        split3((lo + hi) * 0.5f, dst);
+        split3((hi - lo) * 0.5f, dst + 3 * PLANE);
+      } else {
+        split3(in ? *(const f32x4_t*)(st + off) : f32x4_t{}, dst);
+      }
     }
-    // log-sum-exp over the block's live query tokens
-    const float e1 = live ? ell : -INFINITY;
-    const float m1 = wave_max(e1);
-    const float s1 = wave_sum(live ? __expf(e1 - m1) : 0.f);
-    if (lane == 0) base_out[row + kb] = m1 + __logf(s1);
+    __syncthreads();
+    if (!live) continue;
+    // S = Q C^T in tiles of 32 rows x 32 key blocks, one column tile at a time
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+        for (int pl = 0; pl < NPL; ++pl) {
+          const bf16x8_t bop = *(const bf16x8_t*)(s_c + pl * PLANE + (ct * 32 + lcol) * ROW +
+                                                 ks * 32 + half * 16);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            bf16x8_t x = qa[rt][ks];
+            if (BOX && pl >= 3)  // |q|
+              x = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t, x) & 0x7fff7fffu);
+            acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, bop, acc[rt], 0, 0, 0);
+          }
+        }
+      // log-sum-exp over the query rows, per key block (the lane's column)
+      const int kb = c0 + ct * 32 + lcol;
+      float w = 0.f;
+      if (!BOX && rescue_out && kb < nk) {
+        const float r = st[(size_t)3 * nk * D + kb];
+        const float beta = r_high == r_low
+                               ? (r > r_low ? 1.f : 0.f)
+                               : fminf(fmaxf((r - r_low) / (r_high - r_low), 0.f), 1.f);
+        w = r * beta;
+      }
+      float m1 = -INFINITY, m2 = -INFINITY;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row_of(rt, r);
+          if (row >= nrows) continue;
+          m1 = fmaxf(m1, acc[rt][r] * scale);
+          m2 = fmaxf(m2, __builtin_fmaf(s_qn[wave][row], w, acc[rt][r]) * scale);
+        }
+      m1 = fmaxf(m1, __shfl_xor(m1, 32));
+      m2 = fmaxf(m2, __shfl_xor(m2, 32));
+      float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row_of(rt, r);
+          if (row >= nrows) continue;
+          s1 += __expf(acc[rt][r] * scale - m1);
+          s2 += __expf(__builtin_fmaf(s_qn[wave][row], w, acc[rt][r]) * scale - m2);
+        }
+      s1 += __shfl_xor(s1, 32);
+      s2 += __shfl_xor(s2, 32);
+      if (half == 0 && kb < nk) {
+        base_out[orow + kb] = m1 + __logf(s1);
+        if (!BOX && rescue_out) rescue_out[orow + kb] = m2 + __logf(s2);
+      }
+    }
   }
 }
 
@@ -333,16 +375,16 @@ static hipError_t launch_scores_d(float* base, float* rescue, const void* Q,
   if (e != hipSuccess) return e;
   const float scale = 1.f / sqrtf((float)D);
   if (kind == 1) {
-    hipLaunchKernelGGL(attn_block_minmax_kernel<D>, dim3(nq, H, B), dim3(256), 0, stream,
-                       base, (const __bf16*)Q, (const float*)stats, H, Hkv, Sq, nq, nk,
-                       scale);
+    hipLaunchKernelGGL((attn_block_scores_kernel<D, true>), dim3((nq + 3) / 4, H, B), dim3(256),
+                       0, stream, base, nullptr, (const __bf16*)Q, (const float*)stats,
+                       (const float*)nullptr, H, Hkv, Sq, nq, nk, scale);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(attn_block_quantile_kernel, dim3(Hkv, B), dim3(256), 0, stream,
                      stats, quant, Hkv, nk, D, low, high);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_block_scores_kernel<D>, dim3(nq, H, B), dim3(64), 0,
+  hipLaunchKernelGGL((attn_block_scores_kernel<D, false>), dim3((nq + 3) / 4, H, B), dim3(256), 0,
                      stream, base, rescue, (const __bf16*)Q, (const float*)stats,
                      (const float*)quant, H, Hkv, Sq, nq, nk, scale);
   return hipGetLastError();
