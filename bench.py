@@ -132,6 +132,79 @@ def cpu_baseline(w, seconds: float):
                       f"(Sq=Sk={Sq}, D={D}), fp64 NumPy, {dt:.1f} s"}
 
 
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_rows(pre, dec, dO, slopes, img, keep, seconds: float):
+    """The fp64 oracle beside each row after the hot path, each on a bounded
+    sample of the same inputs the GPU ran (whole (batch, head) pairs, whole
+    sequences), as a rate in the row's own unit."""
+    import numpy as np
+    from oracle import attn_oracle as ora
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    cores = _cores()
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    # decode: whole sequences, longest first until `seconds`
+    lens = dec.lengths.cpu().long()
+    order = sorted(range(len(lens)), key=lambda b: -int(lens[b]))
+    done_b, nbytes, dt = [], 0, 0.0
+    Hkv, D = dec.k.shape[1], dec.k.shape[3]
+    for b in order:
+        L = int(lens[b])
+        q = f64(dec.q[b:b + 1])
+        k, v = f64(dec.k[b:b + 1, :, :L]), f64(dec.v[b:b + 1, :, :L])
+        dt += timed(lambda: ora.decode_ref(q, k, v, np.array([L])))
+        nbytes += L * Hkv * D * 2 * 2 + dec.q.shape[1] * D * 2 * 2
+        done_b.append(b)
+        if dt >= seconds:
+            break
+    out["decode"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores,
+                     "kind": "oracle",
+                     "sample": f"{len(done_b)} of {len(lens)} sequences (the longest), "
+                               f"decode_ref, {dt:.1f} s"}
+    # prefill-shaped rows: one (batch, head) pair each
+    B, H, Sq, D = pre.q.shape
+    pairs = allowed_pairs(Sq, pre.k.shape[2], pre.causal, pre.window, pre.input_pos,
+                          pre.k.shape[2])
+    q, k, v = f64(pre.q[:1]), f64(pre.k[:1]), f64(pre.v[:1])
+    dt = timed(lambda: ora.flex_ref(q, k, v, True, softcap=30.0,
+                                    alibi_slopes=f64(slopes), heads=[(0, 0)]))
+    out["flex_softcap_alibi"] = {
+        "value": round(4 * D * pairs / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+        "kind": "oracle", "sample": f"1 of {B * H} (batch, head) pairs, flex_ref, {dt:.1f} s"}
+    g = f64(dO[:1])
+    dt = timed(lambda: ora.attn_bwd_ref(q, k, v, g, True, heads=[(0, 0)]))
+    out["backward"] = {
+        "value": round(10 * D * pairs / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+        "kind": "oracle", "sample": f"1 of {B * H} (batch, head) pairs, attn_bwd_ref, {dt:.1f} s"}
+    # block-sparse: one head of the image workload
+    qi, ki, vi = f64(img.q[:1, :1]), f64(img.k[:1, :1]), f64(img.v[:1, :1])
+    kp = keep[:1, :1].cpu().numpy().astype(bool)
+    kept = int(kp.sum())
+    dt = timed(lambda: ora.block_sparse_attn_ref(qi, ki, vi, kp))
+    out["block_sparse"] = {
+        "value": round(4 * qi.shape[3] * kept * 64 * 64 / dt / 1e12, 5), "unit": "TFLOP/s",
+        "cores": cores, "kind": "oracle",
+        "sample": f"1 of {img.q.shape[1]} heads, block_sparse_attn_ref, {dt:.1f} s"}
+    dt = timed(lambda: ora.rbs_block_scores_ref(qi, ki))
+    out["block_estimate"] = {
+        "value": round(dt * img.q.shape[1] * 1e3, 1), "unit": "ms (whole workload, "
+        "extrapolated)", "cores": cores, "kind": "oracle",
+        "sample": f"1 of {img.q.shape[1]} heads, rbs_block_scores_ref, {dt:.1f} s"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +426,14 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
+        if extra:
+            log("fp64 oracle beside the other rows")
+            rows = cpu_rows(pre, dec, dO, flex_slopes, img, bs_keep, args.cpu_seconds / 5)
+            for n, r in rows.items():
+                if n in out:
+                    out[n]["cpu_oracle"] = r
+                elif n == "block_estimate" and "block_sparse" in out:
+                    out["block_sparse"]["estimate_cpu_oracle"] = r
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
