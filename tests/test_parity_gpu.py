@@ -799,6 +799,13 @@ def test_rbs_pipeline_on_image_workload():
     rows = _sample_rows(S, np.random.default_rng(100))
     rb, rr = ora.rbs_block_scores_ref(_np(w.q[:, :1]), _np(w.k[:, :1]), attn.BLOCK)
     assert np.max(np.abs(_np(base[:, :1]) - rb) / np.maximum(1, np.abs(rb))) <= 1e-4
+    assert np.max(np.abs(_np(resc[:, :1]) - rr) / np.maximum(1, np.abs(rr))) <= 1e-4
+    # the min/max box bound at the full size too (one head against the oracle)
+    mm = torch.empty_like(base)
+    attn.attn_block_scores(mm, None, w.q, w.k, attn.BLOCK_SCORES_MINMAX)
+    torch.cuda.synchronize()
+    rm = ora.minmax_block_scores_ref(_np(w.q[:, 17:18]), _np(w.k[:, 17:18]), attn.BLOCK)
+    assert np.max(np.abs(_np(mm[:, 17:18]) - rm) / np.maximum(1, np.abs(rm))) <= 1e-4
     Or, Lr = ora.block_sparse_attn_ref(_np(w.q), _np(w.k), _np(w.v), keep.cpu().numpy(),
                                        attn.BLOCK, heads=heads, rows=rows)
     sel = ~np.isnan(Lr)
