@@ -146,8 +146,14 @@ __device__ inline int vt_group_pos(int quad_in_group) {
   return ((quad_in_group & 1) << 3) | ((quad_in_group >> 1) << 2);
 }
 
+// Threads of a workgroup: eight waves in two ping-pong groups, or for the
+// block-sparse instantiation four waves (128 rows, two 64-row blocks) without
+// groups, two workgroups per CU (see the block-sparse notes below).
+template <bool SPARSE>
+constexpr int fwd_threads() { return SPARSE ? 256 : kFwdThreads; }
+
 template <int D, bool FLEX, bool BIAS, bool SPARSE>
-__global__ __launch_bounds__(kFwdThreads)
+__global__ __launch_bounds__(fwd_threads<SPARSE>())
 __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     __bf16* __restrict__ O, const __bf16* __restrict__ Q,
     const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -158,12 +164,25 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   using L = FwdLds<D>;
   constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int DBLK = D / 32;     // 32-wide blocks of the head dimension
-  constexpr int KLOADS = kFwdTileN * D / 8 / kGroupThreads;  // K loads/thread
-  constexpr int VTHREADS = (kFwdTileN / 4) * (D / 8);        // threads staging V
+  // Block-sparse workgroups are four waves, 128 rows: a 256-row workgroup
+  // walks the union of the tiles its four 64-row blocks keep, and those sets
+  // overlap little (on the image workload the union is 3.4x each block's
+  // set, 1.9x for two blocks), so most of its steps would keep one block's
+  // two waves busy while the rest wait at the barriers.  Without the second
+  // group both K and V are staged by every thread, the phases are separated
+  // by plain barriers, and two workgroups share a CU.
+  constexpr bool PP = !SPARSE;                 // ping-pong between two groups
+  constexpr int NT = fwd_threads<SPARSE>();
+  constexpr int TM = NT / 2;                   // query rows per workgroup
+  constexpr int GT = PP ? NT / 2 : NT;         // threads staging each of K, V
+  constexpr int KLOADS = kFwdTileN * D / 8 / GT;       // K loads/thread
+  constexpr int VTHREADS = (kFwdTileN / 4) * (D / 8);  // threads staging V
+  static_assert(TM % kSparseBlock == 0, "row blocks per workgroup");
 
-  __shared__ __attribute__((aligned(16))) char smem[L::kTotalAll];
+  // (the block-sparse kernel stages O in the K/V rings, after a barrier)
+  __shared__ __attribute__((aligned(16))) char smem[SPARSE ? L::kTotal : L::kTotalAll];
   // block-sparse: the key tiles some row block of this workgroup keeps, and
-  // per listed tile the keep bits of the four 64-row blocks
+  // per listed tile the keep bits of its 64-row blocks
   __shared__ int16_t s_list[SPARSE ? kSparseMaxTiles : 1];
   __shared__ uint8_t s_kbits[SPARSE ? kSparseMaxTiles : 1];
   __shared__ int s_ntiles;
@@ -171,14 +190,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int grp = wave >> 2;              // 0: group A, 1: group B
-  const int gtid = tid & (kGroupThreads - 1);  // thread index within the group
+  const int grp = PP ? wave >> 2 : 0;     // 0: group A, 1: group B
+  const int gtid = tid & (GT - 1);        // thread index within the group
   const int lrow = lane & 31;  // query row (within the wave) this lane owns
   const int half = lane >> 5;  // which half of each MFMA k-slice this lane feeds
 
   // ---- work items: heaviest query tiles first, XCD-grouped by KV head ----
   const int G = H / Hkv;
-  const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
+  const int nqt = (Sq + TM - 1) / TM;
   const int total = nqt * H * B;
   // Persistent launch (n_wg > 0 workgroups, a multiple of 8, one per CU): the
   // workgroup on XCD x (= blockIdx % 8) walks that XCD's item positions in a
@@ -220,8 +239,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const int h = g * G + hg;
   const int qt = causal ? (nqt - 1 - qt_rank) : qt_rank;
 
-  const int i0 = qt * kFwdTileM;
-  const int i1 = min(i0 + kFwdTileM, Sq);
+  const int i0 = qt * TM;
+  const int i1 = min(i0 + TM, Sq);
   const int kl = k_lengths ? min(max(k_lengths[b], 0), Sk) : Sk;
   // flex: rows at or past q_lengths[b] attend to nothing; the geometry covers
   // the live rows, and a workgroup with dead rows (or a document mask) masks
@@ -282,7 +301,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         unsigned bits = 0;
         if (kt <= kt_last) {
 #pragma unroll
-          for (int q = 0; q < kFwdTileM / kSparseBlock; ++q)
+          for (int q = 0; q < TM / kSparseBlock; ++q)
             if (qb0 + q < nqb && krow[(size_t)q * nkb + kt]) bits |= 1u << q;
         }
         const uint64_t m = __builtin_amdgcn_ballot_w64(bits != 0);
@@ -347,16 +366,37 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   u32x4_t stg_doc = {0, 0, 0, 0};
 
   u32x4_t stg[4];
+  u32x4_t stgv[PP ? 1 : 4];   // V staged alongside K (no groups)
   const int vkq = gtid & 15;  // key quad within the tile (V staging)
   const int vdc = gtid >> 4;  // 8-wide d chunk (V staging)
-  const bool v_stager = VTHREADS == kGroupThreads || gtid < VTHREADS;
+  const bool v_stager = VTHREADS == GT || gtid < VTHREADS;
 
   auto fetch = [&](int kt) {
     const int rel0 = kt * kFwdTileN - geo.union_lo;  // tile start, in valid keys
+    auto fetch_v = [&](u32x4_t (&dst)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = rel0 + vkq * 4 + i;
+        dst[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         vrsrc, (key * D + vdc * 8) * 2, 0, 0));
+      }
+    };
+    if constexpr (!PP) {
+#pragma unroll
+      for (int i = 0; i < KLOADS; ++i) {
+        const int c = i * GT + gtid;
+        stg[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         krsrc, ((rel0 + c / (D / 8)) * D + (c % (D / 8)) * 8) * 2, 0, 0));
+      }
+      if (v_stager) fetch_v(stgv);
+      return;
+    }
     if (grp == 0) {
 #pragma unroll
       for (int i = 0; i < KLOADS; ++i) {
-        const int c = i * kGroupThreads + gtid;
+        const int c = i * GT + gtid;
         const int key = rel0 + c / (D / 8);
         const int dch = c % (D / 8);
         stg[i] = __builtin_bit_cast(
@@ -368,37 +408,20 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                          doc_rsrc, (rel0 + gtid * 4) * 4, 0, 0));
     } else if (v_stager) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = rel0 + vkq * 4 + i;
-        stg[i] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                         vrsrc, (key * D + vdc * 8) * 2, 0, 0));
-      }
+      fetch_v(stg);
     }
   };
 
   auto stash = [&](int buf) {
-    if (grp == 0) {
-      char* kb = smem + buf * L::kBytesK;
-#pragma unroll
-      for (int i = 0; i < KLOADS; ++i) {
-        const int c = i * kGroupThreads + gtid;
-        const int key = c / (D / 8);
-        const int dch = c % (D / 8);
-        *(u32x4_t*)(kb + key * L::kRowK + dch * 16) = stg[i];
-      }
-      if (FLEX && has_doc && gtid < kFwdTileN / 4)
-        *(u32x4_t*)(smem + L::kOffDoc + buf * L::kBytesDoc + gtid * 16) = stg_doc;
-    } else if (v_stager) {
+    auto stash_v = [&](const u32x4_t (&src)[4]) {
       // 4 keys x 8 d  ->  8 rows of V^T, 4 keys (8 bytes) each
       char* vb = smem + L::kOffV + buf * L::kBytesV;
       const int grp16 = vkq >> 2;
       const int pos = grp16 * 16 + vt_group_pos(vkq & 3);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t r0 = stg[0][m], r1 = stg[1][m], r2 = stg[2][m],
-                       r3 = stg[3][m];
+        const uint32_t r0 = src[0][m], r1 = src[1][m], r2 = src[2][m],
+                       r3 = src[3][m];
         u32x2_t even = {__builtin_amdgcn_perm(r1, r0, 0x05040100u),
                         __builtin_amdgcn_perm(r3, r2, 0x05040100u)};
         u32x2_t odd = {__builtin_amdgcn_perm(r1, r0, 0x07060302u),
@@ -407,6 +430,23 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         *(u32x2_t*)(vb + d * L::kRowV + pos * 2) = even;
         *(u32x2_t*)(vb + (d + 1) * L::kRowV + pos * 2) = odd;
       }
+    };
+    if (!PP || grp == 0) {
+      char* kb = smem + buf * L::kBytesK;
+#pragma unroll
+      for (int i = 0; i < KLOADS; ++i) {
+        const int c = i * GT + gtid;
+        const int key = c / (D / 8);
+        const int dch = c % (D / 8);
+        *(u32x4_t*)(kb + key * L::kRowK + dch * 16) = stg[i];
+      }
+      if (FLEX && has_doc && gtid < kFwdTileN / 4)
+        *(u32x4_t*)(smem + L::kOffDoc + buf * L::kBytesDoc + gtid * 16) = stg_doc;
+    }
+    if constexpr (!PP) {
+      if (v_stager) stash_v(stgv);
+    } else if (grp == 1 && v_stager) {
+      stash_v(stg);
     }
   };
 
@@ -658,7 +698,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     stash(0);
     if (n_tiles > 1) fetch(tile_at(1));
     __syncthreads();
-    if (grp == 1) __syncthreads();  // group B runs one phase behind
+    if (PP && grp == 1) __syncthreads();  // group B runs one phase behind
     for (int idx = 0; idx < n_tiles; ++idx) {
       m_phase(idx, idx > 0, true);
       __syncthreads();
@@ -666,7 +706,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       __syncthreads();
     }
     m_phase(n_tiles, true, false);
-    if (grp == 0) __syncthreads();  // matches group B's extra barrier
+    if (PP && grp == 0) __syncthreads();  // matches group B's extra barrier
   }
 
   // ---- epilogue ----
@@ -678,7 +718,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     // chunks, each 16 lanes write one whole row.  The wave only reads what it
     // wrote, so no barrier is needed.
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    char* ost = smem + L::kOffO + wave * L::kBytesOWave;
+    // (without groups the staging area is the K/V rings, free once every
+    // wave is past its last products)
+    if constexpr (!PP) __syncthreads();
+    char* ost = smem + (PP ? L::kOffO : 0) + wave * L::kBytesOWave;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -714,7 +757,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
 // Number of persistent workgroups for `total` items (one per CU, a multiple
 // of 8), or 0 for a launch of one workgroup per item when there are too few
 // items to pair up.
-static int persistent_workgroups(long long total) {
+static int persistent_workgroups(long long total, int per_cu = 1) {
   static int cu_count[64];  // per device; 0 = not queried yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -724,7 +767,7 @@ static int persistent_workgroups(long long total) {
       n = -1;
     cu_count[dev] = n > 0 ? n : -1;
   }
-  const int n_wg = (cu_count[dev] / 8) * 8;
+  const int n_wg = (cu_count[dev] / 8) * 8 * per_cu;
   if (n_wg < 8 || total < 2LL * n_wg) return 0;
   return n_wg;
 }
@@ -792,13 +835,14 @@ hipError_t launch_fwd_sparse(void* O, const void* Q, const void* K,
                              int Sq, int Sk, int causal, int window,
                              int input_pos, const int32_t* k_lengths,
                              const uint8_t* keep, hipStream_t stream) {
-  const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
+  constexpr int NT = fwd_threads<true>();
+  const int nqt = (Sq + NT / 2 - 1) / (NT / 2);
   const long long total = (long long)nqt * H * B;
-  const int n_wg = persistent_workgroups(total);
+  const int n_wg = persistent_workgroups(total, 2);  // two workgroups per CU
   const unsigned grid = n_wg > 0 ? (unsigned)n_wg : (unsigned)total;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, true>), dim3(grid),
-                     dim3(kFwdThreads), 0, stream, (__bf16*)O,
+                     dim3(NT), 0, stream, (__bf16*)O,
                      (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                      B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
                      scale_log2, FlexArgs{}, keep, n_wg);
