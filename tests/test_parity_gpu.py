@@ -271,6 +271,7 @@ DEC_CASES = [
     (2, 8, 1, 64, 1, 500, 4),
     (6, 32, 8, 128, 512, 4096, 8),
     (2, 4, 4, 64, 64, 64, 64),
+    (3, 16, 1, 128, 200, 900, 8),   # 16 heads per KV head: four head chunks
 ]
 
 
