@@ -49,7 +49,7 @@ constexpr int kKeysPerWave = 32;
 constexpr int kKvTile = 128;       // keys per dK/dV workgroup
 constexpr int kQTile = 64;         // query rows per step of the dK/dV kernel
 constexpr int kDqRows = 128;       // query rows per dQ workgroup
-constexpr int kDqKeys = 64;        // keys per step of the dQ kernel
+constexpr int kDqKeys = 32;        // keys per step of the dQ kernel
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, out-of-range reads = 0
 #ifndef KBWD_OP_DEPTH
 #define KBWD_OP_DEPTH 4
@@ -419,19 +419,30 @@ void attn_bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (128-row query tile, head, batch)
 // ---------------------------------------------------------------------------
+// Per stage the K and V rows of one kDqKeys-key tile, unpadded, with the
+// 16-byte chunks of row r stored at chunk c ^ dq_swizzle<D>(r).  The swizzle
+// keeps both read patterns free of bank conflicts: 16 lanes reading one
+// chunk of 16 consecutive rows (row operands of S and dP), and 32 lanes of a
+// transposing read covering 4 consecutive rows (from a multiple of 4) x 4
+// aligned consecutive chunks (the K^T operands of dQ).
 template <int D>
 struct DqLds {
-  using T = TileLds<D, kDqKeys>;
-  // per stage: K, K^T and V of one 64-key tile
+  static constexpr int kRow = D * 2;
   static constexpr int kOffK = 0;
-  static constexpr int kOffKT = kOffK + T::kBytes;
-  static constexpr int kOffV = kOffKT + T::kBytesT;
-  static constexpr int kStage = kOffV + T::kBytes;
+  static constexpr int kOffV = kDqKeys * kRow;
+  static constexpr int kStage = 2 * kDqKeys * kRow;
   static constexpr int kTotal = 2 * kStage;
 };
+template <int D>
+__device__ inline int dq_swizzle(int r) {
+  // D = 128: a bijection of r % 16 whose values for 4 consecutive rows
+  // differ in bits 2-3; D = 64 (8 chunks, two rows per 256 bytes): a
+  // bijection on rows of one parity whose bit 2 differs for rows r and r + 2
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(
     __bf16* __restrict__ dQ, const __bf16* __restrict__ dO,
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -440,9 +451,9 @@ void attn_bwd_dq_kernel(
     int causal, int window, int input_pos, const int32_t* __restrict__ k_lengths,
     float scale) {
   using L = DqLds<D>;
-  using T = TileLds<D, kDqKeys>;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
   __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
 
   const int tid = threadIdx.x;
@@ -496,35 +507,36 @@ void attn_bwd_dq_kernel(
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(V + valid_base), (short)0, nvalid * D * 2, kRsrcWord3);
 
-  // staging: threads hold 4 keys x 8 d of K (both layouts) and of V
-  constexpr int STG_PER = (kDqKeys / 4) * (D / 8);
-  constexpr bool BOTH = STG_PER == kThreads;
-  const int st_t = BOTH ? tid : (tid % STG_PER);
-  const int quad = st_t % (kDqKeys / 4);
-  const int dch = st_t / (kDqKeys / 4);
-  u32x4_t sk[4], sv[4];
+  // staging: every thread moves NCH chunks of K and of V per tile; 16
+  // consecutive threads cover 16 consecutive chunks (coalesced loads, writes
+  // free of bank conflicts)
+  constexpr int NCH = kDqKeys * CPR / kThreads;
+  static_assert(NCH * kThreads == kDqKeys * CPR, "whole tiles per stage");
+  u32x4_t sk[NCH], sv[NCH];
   auto fetch = [&](int kt) {
     const int rel0 = kt * kDqKeys - geo.union_lo;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int off = ((rel0 + quad * 4 + r) * D + dch * 8) * 2;
-      if (BOTH || tid < STG_PER)
-        sk[r] = __builtin_bit_cast(u32x4_t,
-                                   __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
-      if (BOTH || tid >= STG_PER)
-        sv[r] = __builtin_bit_cast(u32x4_t,
-                                   __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * kThreads;
+      const int off = ((rel0 + c / CPR) * D + (c % CPR) * 8) * 2;
+      sk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+      sv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
     }
   };
   auto stash = [&](int buf) {
     char* st = smem + buf * L::kStage;
-    if (BOTH || tid < STG_PER)
-      stash_rows<D, kDqKeys, true>(st + L::kOffK, st + L::kOffKT, sk, quad, dch);
-    if (BOTH || tid >= STG_PER)
-      stash_rows<D, kDqKeys, false>(st + L::kOffV, nullptr, sv, quad, dch);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * kThreads;
+      const int r = c / CPR;
+      const int at = r * L::kRow + (((c % CPR) ^ dq_swizzle<D>(r)) << 4);
+      *(u32x4_t*)(st + L::kOffK + at) = sk[i];
+      *(u32x4_t*)(st + L::kOffV + at) = sv[i];
+    }
   };
 
   const float sl2 = scale * kLog2e;
+  constexpr int KB = kDqKeys / 32;  // 32-key blocks per step
   if (kt_first <= kt_last) {
     fetch(kt_first);
     stash(0);
@@ -534,17 +546,19 @@ void attn_bwd_dq_kernel(
     const int it = kt - kt_first;
     const char* st = smem + (it & 1) * L::kStage;
     const int j0 = kt * kDqKeys;
-    // S^T and dP^T (64 keys x 32 queries), two 32-key blocks; operand i: key
-    // block i / (2 KSTEPS), k-step (i / 2) % KSTEPS, K rows for even i and V
-    // rows for odd i, through a ring kBwdOpDepth reads ahead of the MFMAs
-    f32x16_t s[2], dp[2];
-    s[0] = s[1] = dp[0] = dp[1] = f32x16_t{};
+    // S^T and dP^T (kDqKeys keys x 32 queries) in 32-key blocks; operand i:
+    // key block i / (2 KSTEPS), k-step (i / 2) % KSTEPS, K rows for even i and
+    // V rows for odd i, through a ring kBwdOpDepth reads ahead of the MFMAs
+    f32x16_t s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = dp[kb] = f32x16_t{};
     {
-      constexpr int NOP = 4 * KSTEPS;
+      constexpr int NOP = 2 * KB * KSTEPS;
       auto op = [&](int i) -> const bf16x8_t* {
         const int kb = i / (2 * KSTEPS), ks = (i / 2) % KSTEPS;
         const int off = (i & 1) ? L::kOffV : L::kOffK;
-        return (const bf16x8_t*)(st + off + (kb * 32 + lrow) * T::kRow + half * 16 + ks * 32);
+        const int r = kb * 32 + lrow;
+        return (const bf16x8_t*)(st + off + r * L::kRow + (((2 * ks + half) ^ dq_swizzle<D>(r)) << 4));
       };
       bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
@@ -573,9 +587,9 @@ void attn_bwd_dq_kernel(
     const bool partial = tile_class(geo, j0, kDqKeys) == kTilePartial;
     const int t_lo = rr.lo - (j0 + half * 4);
     const unsigned width = (unsigned)max(rr.hi - rr.lo, 0);
-    u32x4_t dsk[4];
+    u32x4_t dsk[2 * KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float dv[2];
@@ -591,28 +605,47 @@ void attn_bwd_dq_kernel(
         dsk[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dv[0], dv[1]);
       }
     // dQ^T (d x queries) += K^T (d x keys) dS^T (keys x queries); operand i:
-    // d block i / 4, key k-step i % 4
+    // d block i / (2 KB), key k-step i % (2 KB).  K^T comes from the K rows by
+    // transposing reads (ds_read_b64_tr_b16: within 16 lanes, lane i points at
+    // 4 d-values of key kb + i/4 and lane j receives d-value j of keys
+    // kb..kb+3); a lane's 8 keys are 16ks + 4(l/32) + {0..3} and
+    // 16ks + 8 + 4(l/32) + {0..3}, the order dS^T has in the S^T registers.
     {
-      constexpr int NOP = DBLK * 4;
-      auto op = [&](int i) -> const bf16x8_t* {
-        return (const bf16x8_t*)(st + L::kOffKT + ((i / 4) * 32 + lrow) * T::kRowT + half * 16 +
-                                 (i % 4) * 32);
+      constexpr int KST = 2 * KB;
+      constexpr int NOP = DBLK * KST;
+      const int tgrp = lane >> 4, tj = lane & 15;
+      auto op = [&](int i) -> bf16x8_t {
+        const int db = i / KST, kst = i % KST;
+        const int d = db * 32 + (tgrp & 1) * 16 + (tj & 3) * 4;
+        typedef short i16x4_t __attribute__((ext_vector_type(4)));
+        i16x4_t part[2];
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          const int key = kst * 16 + h8 * 8 + (tgrp >> 1) * 4 + (tj >> 2);
+          const char* a = st + L::kOffK + key * L::kRow +
+                          (((d >> 3) ^ dq_swizzle<D>(key)) << 4) + (d & 7) * 2;
+          part[h8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)a);
+        }
+        return __builtin_bit_cast(bf16x8_t,
+                                  __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
       };
       bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
-      for (int i = 0; i < kBwdOpDepth; ++i) ring[i] = *op(i);
+      for (int i = 0; i < kBwdOpDepth; ++i) ring[i] = op(i);
 #pragma unroll
       for (int i = 0; i < NOP; ++i) {
         const bf16x8_t a = ring[i % kBwdOpDepth];
-        if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = *op(i + kBwdOpDepth);
-        dqT[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            a, __builtin_bit_cast(bf16x8_t, dsk[i % 4]), dqT[i / 4], 0, 0, 0);
+        if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = op(i + kBwdOpDepth);
+        dqT[i / KST] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, __builtin_bit_cast(bf16x8_t, dsk[i % KST]), dqT[i / KST], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, kBwdOpDepth, 0);
+      // (two transposing reads per operand)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kBwdOpDepth, 0);
 #pragma unroll
       for (int i = 0; i < NOP - kBwdOpDepth; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kBwdOpDepth, 0);
     }
