@@ -24,9 +24,11 @@
 // Contractions on v_mfma_f32_32x32x16_bf16 with the forward's conventions:
 // A operands are rows read from LDS, B operands are per-lane registers, and a
 // product whose result feeds the next contraction as a B operand is formed
-// transposed so that the accumulator already has the B layout; the LDS copies
-// read as A operands of those second contractions (dO^T, Q^T, K^T) keep their
-// inner index in the permuted order the accumulator registers hold it in.
+// transposed so that the accumulator already has the B layout.  The A
+// operands of those second contractions (dO^T, Q^T, K^T) are transposing LDS
+// reads (ds_read_b64_tr_b16) of the row-major tiles, which deliver the inner
+// index in the permuted order the accumulator registers hold it in; no
+// transposed copy is staged.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,45 +65,38 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Position of element e of quad q4 of a 16-group in the permuted order of the
-// accumulator registers: quads 1 and 2 trade places.
-__device__ inline int perm16(int q4) {
-  return ((q4 & 1) << 3) | ((q4 >> 1) << 2);
+// Tiles in LDS are row-major, rows of D bf16 unpadded, with the 16-byte
+// chunk c of row r stored at chunk c ^ bwd_swizzle<D>(r).  The swizzle keeps
+// both read patterns free of bank conflicts: 16 lanes reading one chunk of 16
+// consecutive rows (row operands), and 32 lanes of a transposing read covering
+// 4 consecutive rows (from a multiple of 4) x 4 aligned consecutive chunks.
+// D = 128: a bijection of r % 16 whose values for 4 consecutive rows differ
+// in bits 2-3.  D = 64 (8 chunks, two rows per 256 bytes): a bijection on the
+// rows of one parity whose bit 2 differs for rows r and r + 2.
+template <int D>
+__device__ inline int bwd_swizzle(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-// Row-major tile of R rows x D bf16 (rows padded by 16 bytes) and its
-// transpose D rows x R bf16 in permuted order (rows padded by 16 bytes).
-template <int D, int R>
-struct TileLds {
-  static constexpr int kRow = D * 2 + 16;
-  static constexpr int kBytes = R * kRow;
-  static constexpr int kRowT = R * 2 + 16;
-  static constexpr int kBytesT = D * kRowT;
-};
-
-// Each staging thread holds 4 consecutive rows x 8 d (one 16-byte chunk per
-// row) of an R x D tile; writes them row-major and, if T, transposed.
-template <int D, int R, bool T>
-__device__ inline void stash_rows(char* rowmajor, char* transposed,
-                                  const u32x4_t (&x)[4], int quad, int dch) {
-  using L = TileLds<D, R>;
+// A operand (32 rows x 16 k) of the transpose of a row-major tile: rows are
+// d = 32 db + (l % 32), the k-slice of lane l is tile rows 16 ks + 4 (l / 32)
+// + {0..3} and 16 ks + 8 + 4 (l / 32) + {0..3} (the permuted order in which
+// an accumulator holds its rows).  Two ds_read_b64_tr_b16: within 16 lanes,
+// lane i points at 4 d-values of tile row kb + i / 4 and lane j receives
+// d-value j of tile rows kb .. kb + 3.
+template <int D>
+__device__ inline bf16x8_t tr_operand(const char* tile, int row_bytes, int ks, int db, int lane) {
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  const int grp = lane >> 4, j = lane & 15;
+  const int d = db * 32 + (grp & 1) * 16 + (j & 3) * 4;
+  i16x4_t part[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *(u32x4_t*)(rowmajor + (quad * 4 + i) * L::kRow + dch * 16) = x[i];
-  if constexpr (T) {
-    const int pos = (quad >> 2) * 16 + perm16(quad & 3);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t r0 = x[0][m], r1 = x[1][m], r2 = x[2][m], r3 = x[3][m];
-      u32x2_t even = {__builtin_amdgcn_perm(r1, r0, 0x05040100u),
-                      __builtin_amdgcn_perm(r3, r2, 0x05040100u)};
-      u32x2_t odd = {__builtin_amdgcn_perm(r1, r0, 0x07060302u),
-                     __builtin_amdgcn_perm(r3, r2, 0x07060302u)};
-      const int d = dch * 8 + 2 * m;
-      *(u32x2_t*)(transposed + d * L::kRowT + pos * 2) = even;
-      *(u32x2_t*)(transposed + (d + 1) * L::kRowT + pos * 2) = odd;
-    }
+  for (int h8 = 0; h8 < 2; ++h8) {
+    const int r = ks * 16 + h8 * 8 + (grp >> 1) * 4 + (j >> 2);
+    const char* a = tile + r * row_bytes + (((d >> 3) ^ bwd_swizzle<D>(r)) << 4) + (d & 7) * 2;
+    part[h8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)a);
   }
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 }  // namespace bwd
@@ -142,15 +137,15 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (128-key tile, KV head, batch)
 // ---------------------------------------------------------------------------
+// Per stage the Q and dO rows, L2 and delta of one 64-row query tile; rows
+// unpadded with the chunk swizzle of bwd_swizzle (the transposed operands
+// dO^T and Q^T come from transposing reads of these rows).
 template <int D>
 struct DkdvLds {
-  using T = TileLds<D, kQTile>;
-  // per stage: Q, Q^T, dO, dO^T, L2 and delta of one 64-row query tile
+  static constexpr int kRow = D * 2;
   static constexpr int kOffQ = 0;
-  static constexpr int kOffQT = kOffQ + T::kBytes;
-  static constexpr int kOffO = kOffQT + T::kBytesT;
-  static constexpr int kOffOT = kOffO + T::kBytes;
-  static constexpr int kOffL = kOffOT + T::kBytesT;
+  static constexpr int kOffO = kOffQ + kQTile * kRow;
+  static constexpr int kOffL = kOffO + kQTile * kRow;
   static constexpr int kOffDel = kOffL + kQTile * 4;
   static constexpr int kStage = kOffDel + kQTile * 4;
   static constexpr int kTotal = 2 * kStage;
@@ -166,9 +161,9 @@ void attn_bwd_dkdv_kernel(
     int B, int H, int Hkv, int Sq, int Sk, int causal, int window,
     int input_pos, const int32_t* __restrict__ k_lengths, float scale) {
   using L = DkdvLds<D>;
-  using T = TileLds<D, kQTile>;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
   __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
 
   const int tid = threadIdx.x;
@@ -216,15 +211,12 @@ void attn_bwd_dkdv_kernel(
   const int nq = qt_hi - qt_lo;
   const int n_items = nq * G;
 
-  // staging: for D = 128 every thread stages 4 rows x 8 d of Q and of dO; for
-  // D = 64 threads 0-127 stage Q and 128-255 stage dO
-  constexpr int STG_PER = (kQTile / 4) * (D / 8);  // threads per tensor
-  constexpr bool BOTH = STG_PER == kThreads;
-  u32x4_t sq[4], so[4];
+  // staging: every thread moves NCH chunks of Q and of dO per tile; 16
+  // consecutive threads cover 16 consecutive chunks
+  constexpr int NCH = kQTile * CPR / kThreads;
+  static_assert(NCH * kThreads == kQTile * CPR, "whole tiles per stage");
+  u32x4_t sq[NCH], so[NCH];
   float sl = 0.f, sd = 0.f;
-  const int st_t = BOTH ? tid : (tid % STG_PER);
-  const int quad = st_t % (kQTile / 4);
-  const int dch = st_t / (kQTile / 4);
   // items run over the query tiles of one head, then the next head; an
   // item is kept as (head offset hh, tile q) and advanced without division
   auto advance = [&](int& hh, int& q) {
@@ -238,13 +230,12 @@ void attn_bwd_dkdv_kernel(
     const int i0 = (qt_lo + q) * kQTile;
     const size_t rb = (size_t)(b * H + h) * Sq;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + quad * 4 + r;
-      const size_t off = (rb + (i < Sq ? i : 0)) * D + dch * 8;
-      if (BOTH || tid < STG_PER)
-        sq[r] = i < Sq ? *(const u32x4_t*)(Q + off) : u32x4_t{0, 0, 0, 0};
-      if (BOTH || tid >= STG_PER)
-        so[r] = i < Sq ? *(const u32x4_t*)(dO + off) : u32x4_t{0, 0, 0, 0};
+    for (int n = 0; n < NCH; ++n) {
+      const int c = tid + n * kThreads;
+      const int i = i0 + c / CPR;
+      const size_t off = (rb + (i < Sq ? i : 0)) * D + (c % CPR) * 8;
+      sq[n] = i < Sq ? *(const u32x4_t*)(Q + off) : u32x4_t{0, 0, 0, 0};
+      so[n] = i < Sq ? *(const u32x4_t*)(dO + off) : u32x4_t{0, 0, 0, 0};
     }
     if (tid < kQTile) {
       const int i = i0 + tid;
@@ -254,10 +245,14 @@ void attn_bwd_dkdv_kernel(
   };
   auto stash = [&](int buf) {
     char* st = smem + buf * L::kStage;
-    if (BOTH || tid < STG_PER)
-      stash_rows<D, kQTile, true>(st + L::kOffQ, st + L::kOffQT, sq, quad, dch);
-    if (BOTH || tid >= STG_PER)
-      stash_rows<D, kQTile, true>(st + L::kOffO, st + L::kOffOT, so, quad, dch);
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) {
+      const int c = tid + n * kThreads;
+      const int r = c / CPR;
+      const int at = r * L::kRow + (((c % CPR) ^ bwd_swizzle<D>(r)) << 4);
+      *(u32x4_t*)(st + L::kOffQ + at) = sq[n];
+      *(u32x4_t*)(st + L::kOffO + at) = so[n];
+    }
     if (tid < kQTile) {
       ((float*)(st + L::kOffL))[tid] = sl;
       ((float*)(st + L::kOffDel))[tid] = sd;
@@ -306,7 +301,8 @@ void attn_bwd_dkdv_kernel(
       auto op = [&](int i) -> const bf16x8_t* {
         const int qb = i / (2 * KSTEPS), ks = (i / 2) % KSTEPS;
         const int off = (i & 1) ? L::kOffO : L::kOffQ;
-        return (const bf16x8_t*)(st + off + (qb * 32 + lcol) * T::kRow + half * 16 + ks * 32);
+        const int r = qb * 32 + lcol;
+        return (const bf16x8_t*)(st + off + r * L::kRow + (((2 * ks + half) ^ bwd_swizzle<D>(r)) << 4));
       };
       bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
@@ -360,22 +356,25 @@ void attn_bwd_dkdv_kernel(
     // the next tile's rows are requested now and land during the rest
     if (it + 1 < n_items) fetch(nxt_hh, nxt_q);
     // dV^T += dO^T P, dK^T += Q^T dS (d x keys), k over the 64 queries;
-    // operand i: d block i / 8, query k-step (i / 2) % 4, dO^T rows for even
-    // i and Q^T rows for odd i, through the same kind of ring
+    // operand i: d block i / 8, query k-step (i / 2) % 4, dO^T for even i and
+    // Q^T for odd i, by transposing reads of the dO and Q rows (a lane's 8
+    // queries are 16kq + 4(l/32) + {0..3} and 16kq + 8 + 4(l/32) + {0..3},
+    // the order P and dS have in the accumulator registers), through the same
+    // kind of ring
     {
       constexpr int NOP = DBLK * 8;
-      auto op = [&](int i) -> const bf16x8_t* {
+      auto op = [&](int i) -> bf16x8_t {
         const int db = i / 8, kq = (i / 2) % 4;
-        const int off = (i & 1) ? L::kOffQT : L::kOffOT;
-        return (const bf16x8_t*)(st + off + (db * 32 + lcol) * T::kRowT + half * 16 + kq * 32);
+        const int off = (i & 1) ? L::kOffQ : L::kOffO;
+        return tr_operand<D>(st + off, L::kRow, kq, db, lane);
       };
       bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
-      for (int i = 0; i < kBwdOpDepth; ++i) ring[i] = *op(i);
+      for (int i = 0; i < kBwdOpDepth; ++i) ring[i] = op(i);
 #pragma unroll
       for (int i = 0; i < NOP; ++i) {
         const bf16x8_t a = ring[i % kBwdOpDepth];
-        if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = *op(i + kBwdOpDepth);
+        if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = op(i + kBwdOpDepth);
         const int db = i / 8, kq = (i / 2) % 4;
         if (i & 1)
           dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -384,11 +383,12 @@ void attn_bwd_dkdv_kernel(
           dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               a, __builtin_bit_cast(bf16x8_t, pk[kq]), dvT[db], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, kBwdOpDepth, 0);
+      // (two transposing reads per operand)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kBwdOpDepth, 0);
 #pragma unroll
       for (int i = 0; i < NOP - kBwdOpDepth; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kBwdOpDepth, 0);
     }
@@ -419,12 +419,8 @@ void attn_bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (128-row query tile, head, batch)
 // ---------------------------------------------------------------------------
-// Per stage the K and V rows of one kDqKeys-key tile, unpadded, with the
-// 16-byte chunks of row r stored at chunk c ^ dq_swizzle<D>(r).  The swizzle
-// keeps both read patterns free of bank conflicts: 16 lanes reading one
-// chunk of 16 consecutive rows (row operands of S and dP), and 32 lanes of a
-// transposing read covering 4 consecutive rows (from a multiple of 4) x 4
-// aligned consecutive chunks (the K^T operands of dQ).
+// Per stage the K and V rows of one kDqKeys-key tile, unpadded and swizzled
+// (bwd_swizzle); K^T operands of dQ are transposing reads of the K rows.
 template <int D>
 struct DqLds {
   static constexpr int kRow = D * 2;
@@ -433,13 +429,6 @@ struct DqLds {
   static constexpr int kStage = 2 * kDqKeys * kRow;
   static constexpr int kTotal = 2 * kStage;
 };
-template <int D>
-__device__ inline int dq_swizzle(int r) {
-  // D = 128: a bijection of r % 16 whose values for 4 consecutive rows
-  // differ in bits 2-3; D = 64 (8 chunks, two rows per 256 bytes): a
-  // bijection on rows of one parity whose bit 2 differs for rows r and r + 2
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
-}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -529,7 +518,7 @@ void attn_bwd_dq_kernel(
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * kThreads;
       const int r = c / CPR;
-      const int at = r * L::kRow + (((c % CPR) ^ dq_swizzle<D>(r)) << 4);
+      const int at = r * L::kRow + (((c % CPR) ^ bwd_swizzle<D>(r)) << 4);
       *(u32x4_t*)(st + L::kOffK + at) = sk[i];
       *(u32x4_t*)(st + L::kOffV + at) = sv[i];
     }
@@ -558,7 +547,7 @@ void attn_bwd_dq_kernel(
         const int kb = i / (2 * KSTEPS), ks = (i / 2) % KSTEPS;
         const int off = (i & 1) ? L::kOffV : L::kOffK;
         const int r = kb * 32 + lrow;
-        return (const bf16x8_t*)(st + off + r * L::kRow + (((2 * ks + half) ^ dq_swizzle<D>(r)) << 4));
+        return (const bf16x8_t*)(st + off + r * L::kRow + (((2 * ks + half) ^ bwd_swizzle<D>(r)) << 4));
       };
       bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
@@ -613,22 +602,8 @@ void attn_bwd_dq_kernel(
     {
       constexpr int KST = 2 * KB;
       constexpr int NOP = DBLK * KST;
-      const int tgrp = lane >> 4, tj = lane & 15;
       auto op = [&](int i) -> bf16x8_t {
-        const int db = i / KST, kst = i % KST;
-        const int d = db * 32 + (tgrp & 1) * 16 + (tj & 3) * 4;
-        typedef short i16x4_t __attribute__((ext_vector_type(4)));
-        i16x4_t part[2];
-#pragma unroll
-        for (int h8 = 0; h8 < 2; ++h8) {
-          const int key = kst * 16 + h8 * 8 + (tgrp >> 1) * 4 + (tj >> 2);
-          const char* a = st + L::kOffK + key * L::kRow +
-                          (((d >> 3) ^ dq_swizzle<D>(key)) << 4) + (d & 7) * 2;
-          part[h8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)a);
-        }
-        return __builtin_bit_cast(bf16x8_t,
-                                  __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        return tr_operand<D>(st + L::kOffK, L::kRow, i % KST, i / KST, lane);
       };
       bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
