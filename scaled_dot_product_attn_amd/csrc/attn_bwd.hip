@@ -289,15 +289,18 @@ void attn_bwd_dkdv_kernel(
     const bool partial =
         i1 - i0 < kQTile || !(last.lo <= j0 && j0 + kKvTile <= first.hi);
 
-    // S and dP (64 queries x 32 keys), two 32-query blocks.  The LDS
+    // S and dP (kQTile queries x 32 keys) in 32-query blocks.  The LDS
     // operands stream through a ring kept kBwdOpDepth reads ahead of the
     // MFMAs (a whole block of operands in registers leaves too few for the
     // accumulators); operand i: query block i / (2 KSTEPS), k-step
     // (i / 2) % KSTEPS, Q rows for even i and dO rows for odd i.
-    f32x16_t s[2], dp[2];
-    s[0] = s[1] = dp[0] = dp[1] = f32x16_t{};
+    constexpr int QB = kQTile / 32;  // 32-query blocks per step
+    constexpr int KQ = 2 * QB;       // 16-query k-steps per step
+    f32x16_t s[QB], dp[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[qb] = dp[qb] = f32x16_t{};
     {
-      constexpr int NOP = 4 * KSTEPS;
+      constexpr int NOP = 2 * QB * KSTEPS;
       auto op = [&](int i) -> const bf16x8_t* {
         const int qb = i / (2 * KSTEPS), ks = (i / 2) % KSTEPS;
         const int off = (i & 1) ? L::kOffO : L::kOffQ;
@@ -327,9 +330,9 @@ void attn_bwd_dkdv_kernel(
     }
     // P = exp2(s * scale * log2e - L2), dS = P (dP - delta); lane's queries are
     // i0 + qb*32 + 8*(r/4) + 4*half + r%4
-    u32x4_t pk[4], dsk[4];  // packed bf16, one 16-query k-step each
+    u32x4_t pk[KQ], dsk[KQ];  // packed bf16, one 16-query k-step each
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int qo = qb * 32 + r4 * 8 + half * 4;
@@ -355,16 +358,16 @@ void attn_bwd_dkdv_kernel(
     }
     // the next tile's rows are requested now and land during the rest
     if (it + 1 < n_items) fetch(nxt_hh, nxt_q);
-    // dV^T += dO^T P, dK^T += Q^T dS (d x keys), k over the 64 queries;
-    // operand i: d block i / 8, query k-step (i / 2) % 4, dO^T for even i and
+    // dV^T += dO^T P, dK^T += Q^T dS (d x keys), k over the kQTile queries;
+    // operand i: d block i / (2 KQ), query k-step (i / 2) % KQ, dO^T for even i and
     // Q^T for odd i, by transposing reads of the dO and Q rows (a lane's 8
     // queries are 16kq + 4(l/32) + {0..3} and 16kq + 8 + 4(l/32) + {0..3},
     // the order P and dS have in the accumulator registers), through the same
     // kind of ring
     {
-      constexpr int NOP = DBLK * 8;
+      constexpr int NOP = DBLK * 2 * KQ;
       auto op = [&](int i) -> bf16x8_t {
-        const int db = i / 8, kq = (i / 2) % 4;
+        const int db = i / (2 * KQ), kq = (i / 2) % KQ;
         const int off = (i & 1) ? L::kOffQ : L::kOffO;
         return tr_operand<D>(st + off, L::kRow, kq, db, lane);
       };
@@ -375,7 +378,7 @@ void attn_bwd_dkdv_kernel(
       for (int i = 0; i < NOP; ++i) {
         const bf16x8_t a = ring[i % kBwdOpDepth];
         if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = op(i + kBwdOpDepth);
-        const int db = i / 8, kq = (i / 2) % 4;
+        const int db = i / (2 * KQ), kq = (i / 2) % KQ;
         if (i & 1)
           dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               a, __builtin_bit_cast(bf16x8_t, dsk[kq]), dkT[db], 0, 0, 0);
