@@ -211,11 +211,18 @@ void attn_bwd_dkdv_kernel(
   const int nq = qt_hi - qt_lo;
   const int n_items = nq * G;
 
-  // staging: every thread moves NCH chunks of Q and of dO per tile; 16
-  // consecutive threads cover 16 consecutive chunks
+  // staging: the Q and dO rows of a tile go from global memory straight into
+  // LDS (buffer_load ... lds: lane l of an instruction fills the 16 bytes at
+  // the wave's LDS address + 16 l, from any global address), so a stage costs
+  // no registers and no wait until the barrier that publishes it.  LDS slot s
+  // (in 16-byte chunks) of a tensor is written by instruction s / 256, wave
+  // (s / 64) % 4, lane s % 64, and holds row s / CPR at chunk s % CPR: the
+  // lane loads the logical chunk that the swizzle puts there.  Rows past Sq
+  // read zeros through the resource's range check.  L2 and delta (64 floats
+  // each) go through registers.
   constexpr int NCH = kQTile * CPR / kThreads;
   static_assert(NCH * kThreads == kQTile * CPR, "whole tiles per stage");
-  u32x4_t sq[NCH], so[NCH];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   float sl = 0.f, sd = 0.f;
   // items run over the query tiles of one head, then the next head; an
   // item is kept as (head offset hh, tile q) and advanced without division
@@ -225,17 +232,26 @@ void attn_bwd_dkdv_kernel(
       ++hh;
     }
   };
-  auto fetch = [&](int hh, int q) {
+  auto fetch = [&](int hh, int q, int buf) {
     const int h = g * G + hh;
     const int i0 = (qt_lo + q) * kQTile;
     const size_t rb = (size_t)(b * H + h) * Sq;
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Q + rb * D), (short)0, Sq * D * 2, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(dO + rb * D), (short)0, Sq * D * 2, kRsrcWord3);
+    char* st = smem + buf * L::kStage;
 #pragma unroll
     for (int n = 0; n < NCH; ++n) {
-      const int c = tid + n * kThreads;
-      const int i = i0 + c / CPR;
-      const size_t off = (rb + (i < Sq ? i : 0)) * D + (c % CPR) * 8;
-      sq[n] = i < Sq ? *(const u32x4_t*)(Q + off) : u32x4_t{0, 0, 0, 0};
-      so[n] = i < Sq ? *(const u32x4_t*)(dO + off) : u32x4_t{0, 0, 0, 0};
+      const int slot = (n * 4 + wave_u) * 64 + lane;
+      const int r = slot / CPR;
+      const int c = (slot % CPR) ^ bwd_swizzle<D>(r);
+      const int off = ((i0 + r) * D + c * 8) * 2;
+      const int at = (n * 4 + wave_u) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qrs, (__attribute__((address_space(3))) void*)(st + L::kOffQ + at), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ors, (__attribute__((address_space(3))) void*)(st + L::kOffO + at), 16, off, 0, 0, 0);
     }
     if (tid < kQTile) {
       const int i = i0 + tid;
@@ -243,25 +259,20 @@ void attn_bwd_dkdv_kernel(
       sd = i < Sq ? delta[rb + i] : 0.f;
     }
   };
+  // after fetch: L2 and delta into the stage, and this thread's direct loads
+  // complete (the barrier that follows publishes the whole stage)
   auto stash = [&](int buf) {
     char* st = smem + buf * L::kStage;
-#pragma unroll
-    for (int n = 0; n < NCH; ++n) {
-      const int c = tid + n * kThreads;
-      const int r = c / CPR;
-      const int at = r * L::kRow + (((c % CPR) ^ bwd_swizzle<D>(r)) << 4);
-      *(u32x4_t*)(st + L::kOffQ + at) = sq[n];
-      *(u32x4_t*)(st + L::kOffO + at) = so[n];
-    }
     if (tid < kQTile) {
       ((float*)(st + L::kOffL))[tid] = sl;
       ((float*)(st + L::kOffDel))[tid] = sd;
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
   const float sl2 = scale * kLog2e;
   if (n_items > 0) {
-    fetch(0, 0);
+    fetch(0, 0, 0);
     stash(0);
     __syncthreads();
   }
@@ -356,8 +367,8 @@ void attn_bwd_dkdv_kernel(
         dsk[kq][w + 1] = pack_bf16x2(dv[2], dv[3]);
       }
     }
-    // the next tile's rows are requested now and land during the rest
-    if (it + 1 < n_items) fetch(nxt_hh, nxt_q);
+    // the next tile's rows stream into the other stage during the rest
+    if (it + 1 < n_items) fetch(nxt_hh, nxt_q, (it + 1) & 1);
     // dV^T += dO^T P, dK^T += Q^T dS (d x keys), k over the kQTile queries;
     // operand i: d block i / (2 KQ), query k-step (i / 2) % KQ, dO^T for even i and
     // Q^T for odd i, by transposing reads of the dO and Q rows (a lane's 8
