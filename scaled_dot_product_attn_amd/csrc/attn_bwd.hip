@@ -510,39 +510,37 @@ void attn_bwd_dq_kernel(
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(V + valid_base), (short)0, nvalid * D * 2, kRsrcWord3);
 
-  // staging: every thread moves NCH chunks of K and of V per tile; 16
-  // consecutive threads cover 16 consecutive chunks (coalesced loads, writes
-  // free of bank conflicts)
+  // staging: K and V rows go from global memory straight into LDS
+  // (buffer_load ... lds, as in the dK/dV kernel): slot s of a tensor is
+  // written by instruction s / 256, wave (s / 64) % 4, lane s % 64 and holds
+  // row s / CPR at chunk s % CPR; keys outside [union_lo, union_hi) read zeros
   constexpr int NCH = kDqKeys * CPR / kThreads;
   static_assert(NCH * kThreads == kDqKeys * CPR, "whole tiles per stage");
-  u32x4_t sk[NCH], sv[NCH];
-  auto fetch = [&](int kt) {
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto fetch = [&](int kt, int buf) {
     const int rel0 = kt * kDqKeys - geo.union_lo;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * kThreads;
-      const int off = ((rel0 + c / CPR) * D + (c % CPR) * 8) * 2;
-      sk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
-      sv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
-    }
-  };
-  auto stash = [&](int buf) {
     char* st = smem + buf * L::kStage;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / CPR;
-      const int at = r * L::kRow + (((c % CPR) ^ bwd_swizzle<D>(r)) << 4);
-      *(u32x4_t*)(st + L::kOffK + at) = sk[i];
-      *(u32x4_t*)(st + L::kOffV + at) = sv[i];
+    for (int n = 0; n < NCH; ++n) {
+      const int slot = (n * 4 + wave_u) * 64 + lane;
+      const int r = slot / CPR;
+      const int c = (slot % CPR) ^ bwd_swizzle<D>(r);
+      const int off = ((rel0 + r) * D + c * 8) * 2;
+      const int at = (n * 4 + wave_u) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krs, (__attribute__((address_space(3))) void*)(st + L::kOffK + at), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (__attribute__((address_space(3))) void*)(st + L::kOffV + at), 16, off, 0, 0, 0);
     }
   };
+  // this thread's direct loads complete (the barrier that follows publishes the stage)
+  auto stage_done = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   const float sl2 = scale * kLog2e;
   constexpr int KB = kDqKeys / 32;  // 32-key blocks per step
   if (kt_first <= kt_last) {
-    fetch(kt_first);
-    stash(0);
+    fetch(kt_first, 0);
+    stage_done();
     __syncthreads();
   }
   for (int kt = kt_first; kt <= kt_last; ++kt) {
@@ -585,7 +583,7 @@ void attn_bwd_dq_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, kBwdOpDepth, 0);
     }
     // the next tile's keys are requested now and land during the rest
-    if (kt + 1 <= kt_last) fetch(kt + 1);
+    if (kt + 1 <= kt_last) fetch(kt + 1, (it + 1) & 1);
     // lane's keys: j0 + kb*32 + 8*(r/4) + 4*half + r%4
     const bool partial = tile_class(geo, j0, kDqKeys) == kTilePartial;
     const int t_lo = rr.lo - (j0 + half * 4);
@@ -638,7 +636,7 @@ void attn_bwd_dq_kernel(
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kBwdOpDepth, 0);
     }
-    if (kt + 1 <= kt_last) stash((it + 1) & 1);
+    if (kt + 1 <= kt_last) stage_done();
     __syncthreads();
   }
 
