@@ -15,8 +15,10 @@
 //                          the group and every 64-row query tile that can see
 //                          its keys, keeping dK^T and dV^T in registers;
 //   attn_bwd_dq_kernel     one workgroup per (128-row query tile, head,
-//                          batch), one wave per 32 rows, walking the 64-key
-//                          tiles its rows can see (the forward's structure).
+//                          batch), one wave per 32 rows, walking the 32-key
+//                          tiles its rows can see (the forward's structure),
+//                          two workgroups per compute unit.
+// Both stage their LDS tiles with direct global-to-LDS loads.
 // dQ is computed by its own kernel rather than by atomics from the dK/dV
 // kernel: it costs two more contractions per pair but no read-modify-write
 // traffic and gives deterministic results.
@@ -607,10 +609,8 @@ void attn_bwd_dq_kernel(
       }
     // dQ^T (d x queries) += K^T (d x keys) dS^T (keys x queries); operand i:
     // d block i / (2 KB), key k-step i % (2 KB).  K^T comes from the K rows by
-    // transposing reads (ds_read_b64_tr_b16: within 16 lanes, lane i points at
-    // 4 d-values of key kb + i/4 and lane j receives d-value j of keys
-    // kb..kb+3); a lane's 8 keys are 16ks + 4(l/32) + {0..3} and
-    // 16ks + 8 + 4(l/32) + {0..3}, the order dS^T has in the S^T registers.
+    // transposing reads (tr_operand), in the key order dS^T has in the S^T
+    // registers.
     {
       constexpr int KST = 2 * KB;
       constexpr int NOP = DBLK * KST;
