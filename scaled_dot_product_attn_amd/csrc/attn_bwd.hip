@@ -10,10 +10,12 @@
 //
 // Three kernels:
 //   attn_bwd_delta_kernel  delta and the base-2 LSE per query row (HBM-bound);
-//   attn_bwd_dkdv_kernel   one workgroup per (128-key tile, KV head, batch),
-//                          one wave per 32 keys; it walks every query head of
-//                          the group and every 64-row query tile that can see
-//                          its keys, keeping dK^T and dV^T in registers;
+//   attn_bwd_dkdv8_kernel  one workgroup per (128-key tile, KV head, batch),
+//                          eight waves: two per 32 keys, each taking one
+//                          32-row half of every 64-row query tile; it walks
+//                          every query head of the group and every query tile
+//                          that can see its keys, keeping partial dK^T and
+//                          dV^T in registers (summed through LDS at the end);
 //   attn_bwd_dq_kernel     one workgroup per (128-row query tile, head,
 //                          batch), one wave per 32 rows, walking the 32-key
 //                          tiles its rows can see (the forward's structure),
@@ -24,9 +26,10 @@
 // traffic and gives deterministic results.
 //
 // Contractions on v_mfma_f32_32x32x16_bf16 with the forward's conventions:
-// A operands are rows read from LDS, B operands are per-lane registers, and a
-// product whose result feeds the next contraction as a B operand is formed
-// transposed so that the accumulator already has the B layout.  The A
+// A operands are rows read from LDS, B operands are per-lane registers or
+// rows read from LDS, and a product whose result feeds the next contraction
+// as a B operand is formed transposed so that the accumulator already has the
+// B layout.  The A
 // operands of those second contractions (dO^T, Q^T, K^T) are transposing LDS
 // reads (ds_read_b64_tr_b16) of the row-major tiles, which deliver the inner
 // index in the permuted order the accumulator registers hold it in; no
@@ -48,7 +51,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;      // four waves
+constexpr int kThreads = 256;      // four waves (dQ)
 constexpr int kKeysPerWave = 32;
 constexpr int kKvTile = 128;       // keys per dK/dV workgroup
 constexpr int kQTile = 64;         // query rows per step of the dK/dV kernel
@@ -137,32 +140,44 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (128-key tile, KV head, batch)
+// dK, dV with eight waves: the two waves on a SIMD share a 32-key block and
+// take the two 32-row halves of every 64-row query tile, each accumulating a
+// partial dK^T and dV^T that are summed through LDS at the end.  K and V of
+// the workgroup's 128 keys stay in LDS and are read as B operands, so a wave
+// holds its two accumulators, one 32 x 32 S/dP pair and its operands in
+// fewer than 256 registers and two waves share each SIMD.
 // ---------------------------------------------------------------------------
-// Per stage the Q and dO rows, L2 and delta of one 64-row query tile; rows
-// unpadded with the chunk swizzle of bwd_swizzle (the transposed operands
-// dO^T and Q^T come from transposing reads of these rows).
+constexpr int kThreads8 = 512;
+
 template <int D>
-struct DkdvLds {
+struct Dkdv8Lds {
   static constexpr int kRow = D * 2;
+  static constexpr int kOffK = 0;                   // K rows of the key tile
+  static constexpr int kOffV = kKvTile * kRow;      // V rows of the key tile
+  static constexpr int kOffStage = 2 * kKvTile * kRow;
+  // per stage: Q, dO, L2 and delta of one 64-row query tile
   static constexpr int kOffQ = 0;
-  static constexpr int kOffO = kOffQ + kQTile * kRow;
-  static constexpr int kOffL = kOffO + kQTile * kRow;
+  static constexpr int kOffO = kQTile * kRow;
+  static constexpr int kOffL = 2 * kQTile * kRow;
   static constexpr int kOffDel = kOffL + kQTile * 4;
   static constexpr int kStage = kOffDel + kQTile * 4;
-  static constexpr int kTotal = 2 * kStage;
+  static constexpr int kTotal = kOffStage + 2 * kStage;
+  // final reduction: per key block the partial dK^T and dV^T of the
+  // second-half wave, 16 DBLK floats per lane, aliasing everything above
+  static constexpr int kRed = 4 * 2 * 64 * 16 * (D / 32) * 4;
+  static_assert(kRed <= kTotal, "reduction area fits");
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv8_kernel(
     __bf16* __restrict__ dK, __bf16* __restrict__ dV,
     const __bf16* __restrict__ dO, const __bf16* __restrict__ Q,
     const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const float* __restrict__ delta, const float* __restrict__ L2,
     int B, int H, int Hkv, int Sq, int Sk, int causal, int window,
     int input_pos, const int32_t* __restrict__ k_lengths, float scale) {
-  using L = DkdvLds<D>;
+  using L = Dkdv8Lds<D>;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int CPR = D / 8;  // 16-byte chunks per row
@@ -171,6 +186,9 @@ void attn_bwd_dkdv_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int kb = wave & 3;     // 32-key block of the tile
+  const int qh = wave >> 2;    // which 32-row half of each query tile
   const int lcol = lane & 31;  // key column this lane owns
   const int half = lane >> 5;
 
@@ -181,18 +199,28 @@ void attn_bwd_dkdv_kernel(
   const int j0 = kt * kKvTile;
   const int j1 = min(j0 + kKvTile, Sk);
   const int kl = k_lengths ? min(max(k_lengths[b], 0), Sk) : Sk;
-  const int kj = j0 + wave * kKeysPerWave + lcol;  // this lane's key
+  const int kj = j0 + kb * kKeysPerWave + lcol;  // this lane's key
 
-  // K and V rows of my key as B operands (zero past Sk)
-  bf16x8_t kreg[KSTEPS], vreg[KSTEPS];
+  // the tile's K and V rows into LDS (direct loads, swizzled; keys past Sk read zeros)
   {
-    const size_t base = ((size_t)(b * Hkv + g) * Sk + (kj < Sk ? kj : 0)) * D + half * 8;
+    const size_t kvb = ((size_t)(b * Hkv + g) * Sk + j0) * D;
+    const int nbytes = (Sk - j0) * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(K + kvb), (short)0, nbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(V + kvb), (short)0, nbytes, kRsrcWord3);
+    constexpr int NKV = kKvTile * CPR / kThreads8;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4_t k4 = kj < Sk ? *(const u32x4_t*)(K + base + ks * 16) : u32x4_t{0, 0, 0, 0};
-      u32x4_t v4 = kj < Sk ? *(const u32x4_t*)(V + base + ks * 16) : u32x4_t{0, 0, 0, 0};
-      kreg[ks] = __builtin_bit_cast(bf16x8_t, k4);
-      vreg[ks] = __builtin_bit_cast(bf16x8_t, v4);
+    for (int n = 0; n < NKV; ++n) {
+      const int slot = (n * 8 + wave_u) * 64 + lane;
+      const int r = slot / CPR;
+      const int c = (slot % CPR) ^ bwd_swizzle<D>(r);
+      const int off = (r * D + c * 8) * 2;
+      const int at = (n * 8 + wave_u) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krs, (__attribute__((address_space(3))) void*)(smem + L::kOffK + at), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (__attribute__((address_space(3))) void*)(smem + L::kOffV + at), 16, off, 0, 0, 0);
     }
   }
 
@@ -217,17 +245,14 @@ void attn_bwd_dkdv_kernel(
   // LDS (buffer_load ... lds: lane l of an instruction fills the 16 bytes at
   // the wave's LDS address + 16 l, from any global address), so a stage costs
   // no registers and no wait until the barrier that publishes it.  LDS slot s
-  // (in 16-byte chunks) of a tensor is written by instruction s / 256, wave
-  // (s / 64) % 4, lane s % 64, and holds row s / CPR at chunk s % CPR: the
+  // (in 16-byte chunks) of a tensor is written by instruction s / 512, wave
+  // (s / 64) % 8, lane s % 64, and holds row s / CPR at chunk s % CPR: the
   // lane loads the logical chunk that the swizzle puts there.  Rows past Sq
   // read zeros through the resource's range check.  L2 and delta (64 floats
   // each) go through registers.
-  constexpr int NCH = kQTile * CPR / kThreads;
-  static_assert(NCH * kThreads == kQTile * CPR, "whole tiles per stage");
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  constexpr int NCH = kQTile * CPR / kThreads8;
+  static_assert(NCH * kThreads8 == kQTile * CPR, "whole tiles per stage");
   float sl = 0.f, sd = 0.f;
-  // items run over the query tiles of one head, then the next head; an
-  // item is kept as (head offset hh, tile q) and advanced without division
   auto advance = [&](int& hh, int& q) {
     if (++q == nq) {
       q = 0;
@@ -242,14 +267,14 @@ void attn_bwd_dkdv_kernel(
         (void*)(Q + rb * D), (short)0, Sq * D * 2, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(dO + rb * D), (short)0, Sq * D * 2, kRsrcWord3);
-    char* st = smem + buf * L::kStage;
+    char* st = smem + L::kOffStage + buf * L::kStage;
 #pragma unroll
     for (int n = 0; n < NCH; ++n) {
-      const int slot = (n * 4 + wave_u) * 64 + lane;
+      const int slot = (n * 8 + wave_u) * 64 + lane;
       const int r = slot / CPR;
       const int c = (slot % CPR) ^ bwd_swizzle<D>(r);
       const int off = ((i0 + r) * D + c * 8) * 2;
-      const int at = (n * 4 + wave_u) * 1024;
+      const int at = (n * 8 + wave_u) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           qrs, (__attribute__((address_space(3))) void*)(st + L::kOffQ + at), 16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -261,10 +286,8 @@ void attn_bwd_dkdv_kernel(
       sd = i < Sq ? delta[rb + i] : 0.f;
     }
   };
-  // after fetch: L2 and delta into the stage, and this thread's direct loads
-  // complete (the barrier that follows publishes the whole stage)
   auto stash = [&](int buf) {
-    char* st = smem + buf * L::kStage;
+    char* st = smem + L::kOffStage + buf * L::kStage;
     if (tid < kQTile) {
       ((float*)(st + L::kOffL))[tid] = sl;
       ((float*)(st + L::kOffDel))[tid] = sd;
@@ -273,11 +296,9 @@ void attn_bwd_dkdv_kernel(
   };
 
   const float sl2 = scale * kLog2e;
-  if (n_items > 0) {
-    fetch(0, 0, 0);
-    stash(0);
-    __syncthreads();
-  }
+  if (n_items > 0) fetch(0, 0, 0);
+  stash(0);  // also completes the K/V tile loads
+  __syncthreads();
   // query rows my key may be seen by: [r_lo, r_hi) (none past k_lengths)
   int r_lo = 0, r_hi = 0;
   if (kj < kl) {
@@ -287,102 +308,100 @@ void attn_bwd_dkdv_kernel(
     r_hi = clamp_i64(hi, 0, Sq);
   }
   const unsigned r_width = (unsigned)max(r_hi - r_lo, 0);
+  const char* krow = smem + L::kOffK + (kb * 32 + lcol) * L::kRow;
+  const char* vrow = smem + L::kOffV + (kb * 32 + lcol) * L::kRow;
+  const int ksw = bwd_swizzle<D>(kb * 32 + lcol);
 
   int cur_hh = 0, cur_q = 0;  // the item of iteration it
   for (int it = 0; it < n_items; ++it) {
-    const char* st = smem + (it & 1) * L::kStage;
+    const char* st = smem + L::kOffStage + (it & 1) * L::kStage;
     const int i0 = (qt_lo + cur_q) * kQTile;
     int nxt_hh = cur_hh, nxt_q = cur_q;
     advance(nxt_hh, nxt_q);
-    // mask per element unless every (row, key) pair of the tile is allowed:
-    // the keys all rows allow run from lo of the last row to hi of the first
     const int i1 = min(i0 + kQTile, Sq);
     const RowRange first = row_range(i0, kl, causal, window, input_pos);
     const RowRange last = row_range(i1 - 1, kl, causal, window, input_pos);
     const bool partial =
         i1 - i0 < kQTile || !(last.lo <= j0 && j0 + kKvTile <= first.hi);
 
-    // S and dP (kQTile queries x 32 keys) in 32-query blocks.  The LDS
-    // operands stream through a ring kept kBwdOpDepth reads ahead of the
-    // MFMAs (a whole block of operands in registers leaves too few for the
-    // accumulators); operand i: query block i / (2 KSTEPS), k-step
-    // (i / 2) % KSTEPS, Q rows for even i and dO rows for odd i.
-    constexpr int QB = kQTile / 32;  // 32-query blocks per step
-    constexpr int KQ = 2 * QB;       // 16-query k-steps per step
-    f32x16_t s[QB], dp[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s[qb] = dp[qb] = f32x16_t{};
+    // S and dP (this wave's 32 queries x its 32 keys): operand pair i: k-step
+    // i / 2, (Q row, K row) for even i and (dO row, V row) for odd i
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
     {
-      constexpr int NOP = 2 * QB * KSTEPS;
-      auto op = [&](int i) -> const bf16x8_t* {
-        const int qb = i / (2 * KSTEPS), ks = (i / 2) % KSTEPS;
+      constexpr int NOP = 2 * KSTEPS;
+      const int qr = qh * 32 + lcol;
+      const int qsw = bwd_swizzle<D>(qr);
+      auto opa = [&](int i) -> bf16x8_t {
+        const int ks = i / 2;
         const int off = (i & 1) ? L::kOffO : L::kOffQ;
-        const int r = qb * 32 + lcol;
-        return (const bf16x8_t*)(st + off + r * L::kRow + (((2 * ks + half) ^ bwd_swizzle<D>(r)) << 4));
+        return *(const bf16x8_t*)(st + off + qr * L::kRow + (((2 * ks + half) ^ qsw) << 4));
       };
-      bf16x8_t ring[kBwdOpDepth];
+      auto opb = [&](int i) -> bf16x8_t {
+        const int ks = i / 2;
+        return *(const bf16x8_t*)(((i & 1) ? vrow : krow) + (((2 * ks + half) ^ ksw) << 4));
+      };
+      bf16x8_t ra[kBwdOpDepth], rb[kBwdOpDepth];
 #pragma unroll
-      for (int i = 0; i < kBwdOpDepth; ++i) ring[i] = *op(i);
+      for (int i = 0; i < kBwdOpDepth; ++i) {
+        ra[i] = opa(i);
+        rb[i] = opb(i);
+      }
 #pragma unroll
       for (int i = 0; i < NOP; ++i) {
-        const bf16x8_t a = ring[i % kBwdOpDepth];
-        if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = *op(i + kBwdOpDepth);
-        const int qb = i / (2 * KSTEPS), ks = (i / 2) % KSTEPS;
+        const bf16x8_t a = ra[i % kBwdOpDepth], bb = rb[i % kBwdOpDepth];
+        if (i + kBwdOpDepth < NOP) {
+          ra[i % kBwdOpDepth] = opa(i + kBwdOpDepth);
+          rb[i % kBwdOpDepth] = opb(i + kBwdOpDepth);
+        }
         if (i & 1)
-          dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vreg[ks], dp[qb], 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, dp, 0, 0, 0);
         else
-          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[ks], s[qb], 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, s, 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, kBwdOpDepth, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kBwdOpDepth, 0);
 #pragma unroll
       for (int i = 0; i < NOP - kBwdOpDepth; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kBwdOpDepth, 0);
     }
     // P = exp2(s * scale * log2e - L2), dS = P (dP - delta); lane's queries are
-    // i0 + qb*32 + 8*(r/4) + 4*half + r%4
-    u32x4_t pk[KQ], dsk[KQ];  // packed bf16, one 16-query k-step each
+    // i0 + 32 qh + 8*(r/4) + 4*half + r%4
+    u32x4_t pk[2], dsk[2];  // packed bf16, one 16-query k-step each
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int qo = qh * 32 + r4 * 8 + half * 4;
+      const f32x4_t l4 = *(const f32x4_t*)(st + L::kOffL + qo * 4);
+      const f32x4_t d4 = *(const f32x4_t*)(st + L::kOffDel + qo * 4);
+      const int t0 = i0 + qo - r_lo;
+      float pv[4], dv[4];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int qo = qb * 32 + r4 * 8 + half * 4;
-        const f32x4_t l4 = *(const f32x4_t*)(st + L::kOffL + qo * 4);
-        const f32x4_t d4 = *(const f32x4_t*)(st + L::kOffDel + qo * 4);
-        const int t0 = i0 + qo - r_lo;
-        float pv[4], dv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = r4 * 4 + e;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], sl2, -l4[e]));
-          if (partial) p = (unsigned)(t0 + e) < r_width ? p : 0.f;
-          pv[e] = p;
-          dv[e] = p * (dp[qb][r] - d4[e]);
-        }
-        const int kq = qb * 2 + (r4 >> 1);
-        const int w = (r4 & 1) * 2;
-        pk[kq][w] = pack_bf16x2(pv[0], pv[1]);
-        pk[kq][w + 1] = pack_bf16x2(pv[2], pv[3]);
-        dsk[kq][w] = pack_bf16x2(dv[0], dv[1]);
-        dsk[kq][w + 1] = pack_bf16x2(dv[2], dv[3]);
+      for (int e = 0; e < 4; ++e) {
+        const int r = r4 * 4 + e;
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[e]));
+        if (partial) p = (unsigned)(t0 + e) < r_width ? p : 0.f;
+        pv[e] = p;
+        dv[e] = p * (dp[r] - d4[e]);
       }
+      const int kq = r4 >> 1;
+      const int w = (r4 & 1) * 2;
+      pk[kq][w] = pack_bf16x2(pv[0], pv[1]);
+      pk[kq][w + 1] = pack_bf16x2(pv[2], pv[3]);
+      dsk[kq][w] = pack_bf16x2(dv[0], dv[1]);
+      dsk[kq][w + 1] = pack_bf16x2(dv[2], dv[3]);
     }
     // the next tile's rows stream into the other stage during the rest
     if (it + 1 < n_items) fetch(nxt_hh, nxt_q, (it + 1) & 1);
-    // dV^T += dO^T P, dK^T += Q^T dS (d x keys), k over the kQTile queries;
-    // operand i: d block i / (2 KQ), query k-step (i / 2) % KQ, dO^T for even i and
-    // Q^T for odd i, by transposing reads of the dO and Q rows (a lane's 8
-    // queries are 16kq + 4(l/32) + {0..3} and 16kq + 8 + 4(l/32) + {0..3},
-    // the order P and dS have in the accumulator registers), through the same
-    // kind of ring
+    // dV^T += dO^T P, dK^T += Q^T dS (d x keys), k over this wave's 32
+    // queries: operand i: d block i / 4, query k-step (i / 2) % 2, dO^T for
+    // even i and Q^T for odd i (transposing reads of the half's rows)
     {
-      constexpr int NOP = DBLK * 2 * KQ;
+      constexpr int NOP = DBLK * 4;
       auto op = [&](int i) -> bf16x8_t {
-        const int db = i / (2 * KQ), kq = (i / 2) % KQ;
+        const int db = i / 4, kq = (i / 2) % 2;
         const int off = (i & 1) ? L::kOffQ : L::kOffO;
-        return tr_operand<D>(st + off, L::kRow, kq, db, lane);
+        return tr_operand<D>(st + off + qh * 32 * L::kRow, L::kRow, kq, db, lane);
       };
       bf16x8_t ring[kBwdOpDepth];
 #pragma unroll
@@ -391,7 +410,7 @@ void attn_bwd_dkdv_kernel(
       for (int i = 0; i < NOP; ++i) {
         const bf16x8_t a = ring[i % kBwdOpDepth];
         if (i + kBwdOpDepth < NOP) ring[i % kBwdOpDepth] = op(i + kBwdOpDepth);
-        const int db = i / (2 * KQ), kq = (i / 2) % KQ;
+        const int db = i / 4, kq = (i / 2) % 2;
         if (i & 1)
           dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               a, __builtin_bit_cast(bf16x8_t, dsk[kq]), dkT[db], 0, 0, 0);
@@ -399,7 +418,6 @@ void attn_bwd_dkdv_kernel(
           dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               a, __builtin_bit_cast(bf16x8_t, pk[kq]), dvT[db], 0, 0, 0);
       }
-      // (two transposing reads per operand)
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kBwdOpDepth, 0);
 #pragma unroll
       for (int i = 0; i < NOP - kBwdOpDepth; ++i) {
@@ -413,6 +431,35 @@ void attn_bwd_dkdv_kernel(
     cur_hh = nxt_hh;
     cur_q = nxt_q;
   }
+
+  // ---- the second-half waves hand their partial sums to the first-half ones ----
+  // (every LDS read of the loop is behind its closing barrier)
+  f32x4_t* red = (f32x4_t*)smem + (kb * 2) * (DBLK * 4) * 64 + lane;
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        red[(db * 4 + q4) * 64] = f32x4_t{dkT[db][q4 * 4], dkT[db][q4 * 4 + 1],
+                                          dkT[db][q4 * 4 + 2], dkT[db][q4 * 4 + 3]};
+        red[(DBLK * 4 + db * 4 + q4) * 64] = f32x4_t{dvT[db][q4 * 4], dvT[db][q4 * 4 + 1],
+                                                     dvT[db][q4 * 4 + 2], dvT[db][q4 * 4 + 3]};
+      }
+  }
+  __syncthreads();
+  if (qh == 1) return;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4_t a = red[(db * 4 + q4) * 64];
+      const f32x4_t c = red[(DBLK * 4 + db * 4 + q4) * 64];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dkT[db][q4 * 4 + e] += a[e];
+        dvT[db][q4 * 4 + e] += c[e];
+      }
+    }
 
   // ---- store: lane owns key kj, holds d = db*32 + 8*(r/4) + 4*half + r%4 ----
   if (kj < Sk) {
@@ -681,7 +728,7 @@ static hipError_t launch_bwd_d(void* dQ, void* dK, void* dV, const void* dO,
   }
   if (Sk > 0) {
     const int nkt = (Sk + kKvTile - 1) / kKvTile;
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(nkt, Hkv, B), dim3(kThreads), 0,
+    hipLaunchKernelGGL(attn_bwd_dkdv8_kernel<D>, dim3(nkt, Hkv, B), dim3(kThreads8), 0,
                        stream, (__bf16*)dK, (__bf16*)dV, (const __bf16*)dO,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V,
                        (const float*)delta, (const float*)L2, B, H, Hkv, Sq, Sk,
