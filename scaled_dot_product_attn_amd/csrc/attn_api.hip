@@ -330,6 +330,8 @@ int attn_bwd(void* dQ, void* dK, void* dV, const void* dO, const void* Q,
   if (Sk > 0 && (!dK || !dV || !K || !V)) return ATTN_EINVAL;
   if (Sq > 0 && (!dQ || !dO || !LSE)) return ATTN_EINVAL;
   if ((long long)B * H * Sq > INT_MAX / 2) return ATTN_EUNSUPPORTED;
+  // the Q and dO rows of one head are addressed through 32-bit buffer offsets
+  if ((long long)Sq * D * 4 + 65536 > INT_MAX) return ATTN_EUNSUPPORTED;
   if (Sq == 0)  // no query: the key gradients are zero, no scratch needed
     return hip_status(launch_bwd(dQ, dK, dV, dO, Q, K, V, O, LSE, B, H, Hkv,
                                  Sq, Sk, D, causal, window, input_pos,

@@ -114,6 +114,8 @@ def test_bwd_argument_errors(lib):
                             window, 0, None, ws, nbytes, None)
     assert bwd(H=3) == attn.ATTN_EINVAL
     assert bwd(D=96) == attn.ATTN_EUNSUPPORTED
+    # a head's Q / dO rows past the 32-bit byte offsets of the staging loads
+    assert bwd(H=2, Hkv=2, Sq=(1 << 31) // (128 * 4), Sk=8) == attn.ATTN_EUNSUPPORTED
     assert bwd(causal=0, window=2) == attn.ATTN_EINVAL
     for k in ("dQ", "dK", "dV", "dO", "L"):
         assert bwd(**{k: None}) == attn.ATTN_EINVAL, k
