@@ -48,61 +48,105 @@ using namespace sparse;
 
 // Per (key block, KV head, batch): centroid, per-dimension min / max, radius.
 // stats layout per (b, g): c (nk, D), lo (nk, D), hi (nk, D), r (nk).
+// One pass over the block: 16-byte loads with 16 (D = 128) or 8 (D = 64)
+// consecutive threads per row, each thread holding RPT rows x 8 d-values in
+// registers; per-dimension sums / min / max reduce over the rows by lane
+// shuffles and then across the four waves in LDS, row distances to the
+// centroid over the row's threads by shuffles.
 template <int D>
 __global__ __launch_bounds__(256) void attn_block_stats_kernel(
     const __bf16* __restrict__ K, float* __restrict__ stats, int Hkv, int Sk,
     int nk) {
-  __shared__ float s_part[3][256 / D][D];
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;       // rows one pass of the workgroup covers
+  constexpr int RPT = kBlock / RPP;    // rows per thread
+  __shared__ float s_part[3][4][D];
   __shared__ float s_c[D];
-  __shared__ float s_r[256 / 64];
+  __shared__ float s_r[4];
   const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int d = tid % D, part = tid / D;       // 256 / D threads per dimension
-  constexpr int PARTS = 256 / D;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid % CPR;             // this thread's chunk: d = 8 c .. 8 c + 7
   const int j0 = kb * kBlock;
   const int n = min(kBlock, Sk - j0);
   const __bf16* kp = K + ((size_t)(b * Hkv + g) * Sk + j0) * D;
-  float sum = 0.f, lo = INFINITY, hi = -INFINITY;
-  for (int j = part; j < n; j += PARTS) {
-    const float x = (float)kp[(size_t)j * D + d];
-    sum += x;
-    lo = fminf(lo, x);
-    hi = fmaxf(hi, x);
+  float x[RPT][8];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = tid / CPR + i * RPP;
+    u32x4_t v = {0, 0, 0, 0};
+    if (r < n) v = *(const u32x4_t*)(kp + (size_t)r * D + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      x[i][2 * w] = bf16_lo(v[w]);
+      x[i][2 * w + 1] = bf16_hi(v[w]);
+    }
   }
-  s_part[0][part][d] = sum;
-  s_part[1][part][d] = lo;
-  s_part[2][part][d] = hi;
+  // per-dimension partials over this thread's rows, then over the wave's rows
+  float su[8], lo[8], hi[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    su[e] = 0.f;
+    lo[e] = INFINITY;
+    hi[e] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      if (tid / CPR + i * RPP < n) {
+        su[e] += x[i][e];
+        lo[e] = fminf(lo[e], x[i][e]);
+        hi[e] = fmaxf(hi[e], x[i][e]);
+      }
+    }
+#pragma unroll
+    for (int o = CPR; o < 64; o <<= 1) {
+      su[e] += __shfl_xor(su[e], o);
+      lo[e] = fminf(lo[e], __shfl_xor(lo[e], o));
+      hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], o));
+    }
+  }
+  if (lane < CPR) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s_part[0][wave][c * 8 + e] = su[e];
+      s_part[1][wave][c * 8 + e] = lo[e];
+      s_part[2][wave][c * 8 + e] = hi[e];
+    }
+  }
   __syncthreads();
   float* base = stats + (size_t)(b * Hkv + g) * nk * (3 * D + 1);
   if (tid < D) {
-    float su = 0.f, l = INFINITY, h = -INFINITY;
+    float sm = 0.f, l = INFINITY, h = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < PARTS; ++p) {
-      su += s_part[0][p][tid];
-      l = fminf(l, s_part[1][p][tid]);
-      h = fmaxf(h, s_part[2][p][tid]);
+    for (int w = 0; w < 4; ++w) {
+      sm += s_part[0][w][tid];
+      l = fminf(l, s_part[1][w][tid]);
+      h = fmaxf(h, s_part[2][w][tid]);
     }
-    const float c = su / (float)n;
-    s_c[tid] = c;
-    base[(size_t)kb * D + tid] = c;
+    const float cen = sm / (float)n;
+    s_c[tid] = cen;
+    base[(size_t)kb * D + tid] = cen;
     base[(size_t)nk * D + (size_t)kb * D + tid] = l;
     base[(size_t)2 * nk * D + (size_t)kb * D + tid] = h;
   }
   __syncthreads();
-  // radius: one thread per key, squared distance to the centroid
-  float dist = 0.f;
-  if (tid < n) {
-    const __bf16* row = kp + (size_t)tid * D;
-    for (int e = 0; e < D; ++e) {
-      const float t = (float)row[e] - s_c[e];
+  // radius: the largest squared distance of a row to the centroid
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    float dist = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = x[i][e] - s_c[c * 8 + e];
       dist = __builtin_fmaf(t, t, dist);
     }
+#pragma unroll
+    for (int o = 1; o < CPR; o <<= 1) dist += __shfl_xor(dist, o);
+    if (tid / CPR + i * RPP < n) m = fmaxf(m, dist);
   }
-  const float m = wave_max(tid < n ? dist : 0.f);
-  if ((tid & 63) == 0) s_r[tid >> 6] = m;
+  m = wave_max(m);
+  if (lane == 0) s_r[wave] = m;
   __syncthreads();
   if (tid == 0) {
-    float r = fmaxf(fmaxf(s_r[0], s_r[1]), fmaxf(s_r[2], s_r[3]));
+    const float r = fmaxf(fmaxf(s_r[0], s_r[1]), fmaxf(s_r[2], s_r[3]));
     base[(size_t)3 * nk * D + kb] = sqrtf(r);
   }
 }
