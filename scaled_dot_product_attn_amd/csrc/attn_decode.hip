@@ -188,8 +188,6 @@ void attn_decode_split_kernel(
   __shared__ float s_l[4][GM];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int li = tid % LPK;  // which 8-wide d chunk
   const int gi = tid / LPK;  // key slot within a pass
 

@@ -69,7 +69,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kFwdWaves = 8;               // two groups of four
 constexpr int kFwdThreads = kFwdWaves * 64;
-constexpr int kGroupThreads = kFwdThreads / 2;
 constexpr int kFwdTileM = kFwdWaves * 32;  // query rows per workgroup
 constexpr int kFwdTileN = 64;              // keys per tile
 constexpr float kLazyRescale = 8.0f;       // log2 headroom before m is raised
