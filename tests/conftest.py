@@ -13,8 +13,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests fail loudly on a GPU machine whose library did not load; on a box
-    # without any GPU they are skipped rather than run.
+    # GPU tests fail loudly on a machine with a GPU whose library did not load;
+    # on a machine without any GPU they are skipped rather than run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
