@@ -645,6 +645,10 @@ BWD_CASES = [
     (1, 4, 4, 96, 96, 64, False, 0, 0, None),
     (1, 2, 1, 64, 256, 128, True, 16, 300, [200]),
     (1, 4, 2, 33, 700, 128, False, 0, 0, [650]),
+    # one partial key tile (Sk < 64) and fewer than 64 query rows at D = 128
+    (1, 2, 1, 45, 50, 128, True, 0, 5, None),
+    # eight query heads per KV head, a ragged tail on both sides
+    (1, 8, 1, 200, 333, 128, True, 0, 133, None),
 ]
 
 
