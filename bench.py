@@ -101,6 +101,34 @@ def traffic_for(kind: str):
     return t.get("bytes_per_launch")
 
 
+# hipDeviceAttribute_t values (hip/hip_runtime_api.h of this ROCm)
+_HIP_ATTR = {"clock_khz": 5, "memory_bus_bits": 59, "memory_clock_khz": 60, "cus": 63}
+FLOP_PER_CLK_PER_CU_BF16 = 4096  # dense bf16 MFMA on gfx950 (4 SIMDs x 1024)
+
+
+def device_info(torch) -> dict:
+    """The GPU's own figures (hipDeviceGetAttribute) and the dense bf16 MFMA
+    peak they imply (CUs x 4096 flop/clk x the peak engine clock).  The memory
+    clock and bus width are reported as the runtime gives them; the HBM peak
+    stays the published 8 TB/s."""
+    import ctypes
+    dev = torch.cuda.current_device()
+    props = torch.cuda.get_device_properties(dev)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None)}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return info
+    for key, attr in _HIP_ATTR.items():
+        v = ctypes.c_int(0)
+        rc = hip.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(attr), ctypes.c_int(dev))
+        info[key] = v.value if rc == 0 else None
+    if info.get("cus") and info.get("clock_khz"):
+        info["peak_bf16_tflops_at_clock"] = round(
+            info["cus"] * FLOP_PER_CLK_PER_CU_BF16 * info["clock_khz"] * 1e3 / 1e12, 1)
+    return info
+
+
 def cpu_baseline(w, seconds: float):
     """The fp64 oracle on whole (batch, head) pairs of the prefill workload."""
     import numpy as np
@@ -375,6 +403,7 @@ def main():
             "decode_bytes": db,
         },
         "roofline": roof("mfma", pre_tf, PEAK_BF16_TFLOPS, "TFLOP/s", traffic_for("prefill")),
+        "device": device_info(torch),
         "prefill_ms": round(ms["prefill"], 4),
         "decode": {
             "value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(ms["decode"], 4),
