@@ -233,6 +233,39 @@ def cpu_rows(pre, dec, dO, slopes, img, keep, seconds: float):
     return out
 
 
+def timing_stats(times_ms):
+    """Mean, median and min of per-launch times (ms)."""
+    t = sorted(times_ms)
+    n = len(t)
+    med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+    return {"mean": round(sum(t) / n, 4), "median": round(med, 4), "min": round(t[0], 4)}
+
+
+def profile_prefill(torch, attn, w, args):
+    """One prefill workload alone: warm-up, then timed launches on one stream."""
+    B, H, Sq, D = w.q.shape
+    O = torch.empty_like(w.q)
+    LSE = torch.empty(B, H, Sq, dtype=torch.float32, device=w.q.device)
+    stream = torch.cuda.current_stream()
+    run = lambda: attn.attn_fwd(O, w.q, w.k, w.v, LSE, w.causal, w.window, w.input_pos,
+                                w.k_lengths)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(args.steps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        run()
+        e.record(stream)
+        ev.append((s, e))
+    torch.cuda.synchronize()
+    t = timing_stats([s.elapsed_time(e) for s, e in ev])
+    f = prefill_flops(w)
+    print(json.dumps({"profile_prefill": args.profile_prefill, "flops": f, "ms": t,
+                      "TFLOP/s_median": round(f / (t["median"] * 1e-3) / 1e12, 2)}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +274,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--profile-prefill", choices=["gqa_causal", "window_offset", "image_clustered"],
+                    help="time only this prefill workload (for per-workload profiler passes) and "
+                         "print its timing line instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -253,6 +289,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_prefill:
+        profile_prefill(torch, attn, wl.make(args.profile_prefill, device=dev), args)
+        return
     log("generating inputs")
     pre = wl.make("gqa_causal", device=dev)
     dec = wl.make("decode_split", device=dev)
@@ -371,6 +410,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = {n: sum(s.elapsed_time(e) for s, e in ev[n]) / args.steps for n in names}
+    timing = {n: timing_stats([s.elapsed_time(e) for s, e in ev[n]]) for n in names}
     log("kernel ms: " + ", ".join(f"{n}={ms[n]:.4f}" for n in names))
 
     fl = prefill_flops(pre)
@@ -404,6 +444,7 @@ def main():
         },
         "roofline": roof("mfma", pre_tf, PEAK_BF16_TFLOPS, "TFLOP/s", traffic_for("prefill")),
         "device": device_info(torch),
+        "timing_ms": timing,
         "prefill_ms": round(ms["prefill"], 4),
         "decode": {
             "value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(ms["decode"], 4),

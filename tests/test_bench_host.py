@@ -34,3 +34,8 @@ def test_multi_gpu_request_exits_with_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_timing_stats_median_and_min():
+    assert bench.timing_stats([3.0, 1.0, 2.0]) == {"mean": 2.0, "median": 2.0, "min": 1.0}
+    assert bench.timing_stats([4.0, 1.0, 2.0, 3.0]) == {"mean": 2.5, "median": 2.5, "min": 1.0}
