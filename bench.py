@@ -34,6 +34,10 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+# The CPU baseline's BLAS threads: the CPUs this process may run on, unless the
+# environment already fixes them (set before NumPy is first imported).
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(len(os.sched_getaffinity(0))))
 
 METRIC = ("attn fwd bf16 TFLOP/s (prefill) + decode KV GB/s, % of roofline, 1 MI355X")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
