@@ -499,6 +499,13 @@ void attn_decode_paged_kernel(
 
 // One wave per (sequence, head): O = sum_s w_s O_s / sum_s w_s with
 // w_s = 2^(L_s - max L) (L_s in base-2 units); O = 0 when every slice is empty.
+// Every slice writes its partial row (zeros and L = -inf when it is empty),
+// so an empty slice enters with w_s = 2^-inf = 0.  The kernel is bound by
+// load latency, not bytes: the slice maxima come from one load per lane and
+// a butterfly, and the partial rows of kMergeBatch slices are all loaded
+// before the first of them is used.
+constexpr int kMergeBatch = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_merge_kernel(
     const float* __restrict__ Opart, const float* __restrict__ Lpart,
@@ -508,21 +515,32 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(
   const int lane = threadIdx.x & 63;
   if (bh >= BH) return;
   const float* lp = Lpart + (size_t)bh * n_splits;
+  const float* op = Opart + (size_t)bh * n_splits * D + lane;
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, lp[s]);
+  for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, lp[s]);
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
   float o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
   float wsum = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float ls = lp[s];
-      if (ls == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(ls - M);
-      wsum += w;
-      const float* op = Opart + ((size_t)bh * n_splits + s) * D;
+    for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
+      float ls[kMergeBatch], x[kMergeBatch][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, op[lane + 64 * e], o[e]);
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int s = min(s0 + u, n_splits - 1);  // past the end: weight 0
+        ls[u] = s0 + u < n_splits ? lp[s] : -INFINITY;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x[u][e] = op[(size_t)s * D + 64 * e];
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float w = __builtin_amdgcn_exp2f(ls[u] - M);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, x[u][e], o[e]);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

@@ -272,6 +272,7 @@ DEC_CASES = [
     (6, 32, 8, 128, 512, 4096, 8),
     (2, 4, 4, 64, 64, 64, 64),
     (3, 16, 1, 128, 200, 900, 8),   # 16 heads per KV head: four head chunks
+    (2, 4, 2, 128, 1, 3000, 100),   # more slices than a wave has lanes, most empty
 ]
 
 
