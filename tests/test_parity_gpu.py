@@ -277,6 +277,7 @@ DEC_CASES = [
     (2, 4, 4, 64, 64, 64, 64),
     (3, 16, 1, 128, 200, 900, 8),   # 16 heads per KV head: four head chunks
     (2, 4, 2, 128, 1, 3000, 100),   # more slices than a wave has lanes, most empty
+    (300, 2, 1, 64, 1, 200, 4),     # more sequences than the longest-first ranking covers
 ]
 
 
@@ -380,6 +381,7 @@ PAGED_CASES = [
     (3, 8, 2, 128, 1, 1000, 64, 8),
     (2, 16, 2, 128, 1, 700, 16, 8),      # eight query heads per KV head
     (2, 8, 2, 128, 1, 300, 2, 4),        # blocks smaller than a wave's keys
+    (300, 2, 1, 64, 1, 200, 16, 4),      # more sequences than the longest-first ranking covers
     (2, 8, 2, 64, 1, 300, 4, 4),
 ]
 
