@@ -311,6 +311,20 @@ def test_decode_edge_lengths_and_poison():
         _check_decode(w, O)
 
 
+def test_decode_lengths_clamped_to_cache():
+    # lengths outside [0, Smax] are clamped on the device: -5 attends to nothing,
+    # 10**6 to the whole cache
+    B, H, Hkv, D, Smax = 4, 8, 2, 128, 200
+    w = wl.decode_random(B, H, Hkv, D, 1, Smax, 8, seed=25)
+    w.lengths = torch.tensor([-5, 10**6, Smax, 0], dtype=torch.int32)
+    w.q, w.k, w.v, w.lengths = (t.to(DEV) for t in (w.q, w.k, w.v, w.lengths))
+    for ns in (1, 8):
+        O = attn.decode(w.q, w.k, w.v, w.lengths, ns)
+        torch.cuda.synchronize()
+        assert torch.all(O[0] == 0) and torch.all(O[3] == 0)
+        _check_decode(w, O)
+
+
 def test_decode_splits_invariant_and_ws():
     w = wl.decode_random(8, 16, 4, 128, 10, 3000, 8, seed=23)
     w.q, w.k, w.v, w.lengths = (t.to(DEV) for t in (w.q, w.k, w.v, w.lengths))
