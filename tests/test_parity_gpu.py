@@ -113,6 +113,7 @@ BF16_CASES = [
     (1, 2, 1, 96, 96, 128, True, 0, -40, None),           # leading rows see nothing
     (1, 2, 1, 64, 256, 128, True, 16, 300, [200]),         # window past k_len: empty rows
     (1, 8, 1, 512, 512, 128, True, 0, 0, None),           # MQA
+    (3, 4, 2, 150, 200, 128, True, 0, 60, [-7, 10**6, 120]),  # key lengths clamped to [0, Sk]
     # 516 work items: the persistent schedule (two or more items per CU on a
     # 256-CU GPU), with 4 items past the last multiple of 8
     (1, 172, 43, 600, 600, 64, True, 0, 0, None),
