@@ -172,7 +172,7 @@ def _cores():
         return len(os.sched_getaffinity(0))
 
 
-def cpu_rows(pre, dec, dO, slopes, img, keep, seconds: float):
+def cpu_rows(pre, dec, dO, slopes, img, keep, seconds: float, paged=None):
     """The fp64 oracle beside each row after the hot path, each on a bounded
     sample of the same inputs the GPU ran (whole (batch, head) pairs, whole
     sequences), as a rate in the row's own unit."""
@@ -205,6 +205,30 @@ def cpu_rows(pre, dec, dO, slopes, img, keep, seconds: float):
                      "kind": "oracle",
                      "sample": f"{len(done_b)} of {len(lens)} sequences (the longest), "
                                f"decode_ref, {dt:.1f} s"}
+    # paged decode: whole sequences, longest first, each gathered through its
+    # block table by the oracle (the caches handed over hold only its blocks)
+    if paged is not None:
+        lens = paged.lengths.cpu().long()
+        tables = paged.block_tables.cpu().long()
+        bs, Hkv_p = paged.k_cache.shape[1], paged.k_cache.shape[2]
+        order = sorted(range(len(lens)), key=lambda b: -int(lens[b]))
+        done, nbytes, dt = 0, 0, 0.0
+        for b in order:
+            L = int(lens[b])
+            nb = (L + bs - 1) // bs
+            blocks = tables[b, :nb].to(paged.k_cache.device)
+            kc, vc = f64(paged.k_cache[blocks]), f64(paged.v_cache[blocks])
+            q = f64(paged.q[b:b + 1])
+            table = np.arange(nb)[None, :]
+            dt += timed(lambda: ora.decode_paged_ref(q, kc, vc, table, np.array([L])))
+            nbytes += L * Hkv_p * D * 2 * 2 + paged.q.shape[1] * D * 2 * 2
+            done += 1
+            if dt >= seconds:
+                break
+        out["decode_paged"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": cores, "kind": "oracle",
+                               "sample": f"{done} of {len(lens)} sequences (the longest), "
+                                         f"decode_paged_ref, {dt:.1f} s"}
     # prefill-shaped rows: one (batch, head) pair each
     B, H, Sq, D = pre.q.shape
     pairs = allowed_pairs(Sq, pre.k.shape[2], pre.causal, pre.window, pre.input_pos,
@@ -502,7 +526,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
         if extra:
             log("fp64 oracle beside the other rows")
-            rows = cpu_rows(pre, dec, dO, flex_slopes, img, bs_keep, args.cpu_seconds / 5)
+            rows = cpu_rows(pre, dec, dO, flex_slopes, img, bs_keep, args.cpu_seconds / 5,
+                            paged)
             for n, r in rows.items():
                 if n in out:
                     out[n]["cpu_oracle"] = r
