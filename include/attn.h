@@ -42,8 +42,9 @@
  *   stated); the library keeps none after the call returns.  Work is enqueued
  *   asynchronously on `stream` (0 = the null stream); inputs and outputs must
  *   stay alive until the stream has passed it.  No entry point synchronises,
- *   and the host never reads device arrays (k_lengths, lengths).  The library
- *   holds no mutable global state; calls from several host threads are safe.
+ *   and the host never reads device arrays (k_lengths, lengths).  Calls from
+ *   several host threads are safe, except overlapping attn_decode_static
+ *   calls on one GPU (they share its static scratch).
  *
  * Errors: every int-returning entry point returns
  *   ATTN_OK (0), ATTN_EINVAL (1, a bad argument: shape, H % Hkv, window
@@ -275,6 +276,26 @@ int attn_decode_ws(void* O, const void* Q, const void* K, const void* V,
                    const int32_t* lengths, int n_splits, int B, int H, int Hkv,
                    int Smax, int D, void* workspace, size_t ws_bytes,
                    hipStream_t stream);
+
+/* Maximum scratch of attn_decode_static: 32 MiB per GPU, i.e.
+ * attn_decode_workspace_bytes(B, H, n_splits, D) must not exceed it
+ * (B * H * n_splits up to about 65,000 at D = 128). */
+#define ATTN_DECODE_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* attn_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, semantics and kernels as attn_decode, with the slice
+ * partials in a static device array of ATTN_DECODE_STATIC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends.  Calls no
+ * allocating routine.  Returns ATTN_EUNSUPPORTED, before anything is
+ * enqueued, when attn_decode_workspace_bytes(B, H, n_splits, D) exceeds that
+ * size (n_splits = 1 needs no scratch).  Every call on one GPU shares its
+ * array and leaves its partials there: calls that overlap on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller.  The
+ * array's device address is looked up on the first call on each device. */
+int attn_decode_static(void* O, const void* Q, const void* K, const void* V,
+                       const int32_t* lengths, int n_splits, int B, int H,
+                       int Hkv, int Smax, int D, hipStream_t stream);
 
 /* Split-KV decode over a paged KV cache, bf16 Q/K/V/O.
  *   O, Q          (B, H, D) bf16, as attn_decode

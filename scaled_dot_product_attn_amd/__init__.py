@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 TILE_M, TILE_N = 256, 64  # prefill tile sizes (ATTN_FWD_TILE_M / _N)
 BLOCK = 64                 # block-sparse block size (ATTN_BLOCK)
+DECODE_STATIC_SCRATCH_BYTES = 32 << 20  # ATTN_DECODE_STATIC_SCRATCH_BYTES
 BLOCK_SCORES_RBS, BLOCK_SCORES_MINMAX = 0, 1
 BLOCK_MASK_RELATIVE, BLOCK_MASK_TOPK, BLOCK_MASK_BAND = 0, 1, 2
 
@@ -47,6 +48,7 @@ _SIGS = {
                            ctypes.POINTER(AttnFlex), _P]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "attn_decode_ws": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
+    "attn_decode_static": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "attn_block_scores_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
@@ -289,6 +291,15 @@ def attn_decode_ws(O, Q, K, V, lengths, n_splits, workspace, stream=None) -> Non
                               int(n_splits), B, H, Hkv, Smax, D, ws, nbytes,
                               _stream(stream))
     _check(rc, "attn_decode_ws")
+
+
+def attn_decode_static(O, Q, K, V, lengths, n_splits=8, stream=None) -> None:
+    """Split-KV decode whose scratch is the library's static per-GPU array
+    (no allocation; overlapping calls on one GPU race)."""
+    B, H, Hkv, Smax, D = _dec_args(O, Q, K, V, lengths)
+    rc = lib().attn_decode_static(_ptr(O), _ptr(Q), _ptr(K), _ptr(V), _ptr(lengths),
+                                  int(n_splits), B, H, Hkv, Smax, D, _stream(stream))
+    _check(rc, "attn_decode_static")
 
 
 def attn_decode_paged(O, Q, K_cache, V_cache, block_tables, lengths, n_splits=8,

@@ -10,6 +10,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "attn_common.h"
 
@@ -139,6 +142,44 @@ static int check_decode_paged(const void* O, const void* Q, const void* Kc,
   return ATTN_OK;
 }
 
+// ---- scratch of attn_decode_static ----
+// The decode's slice partials (O_s and LSE_s of every (sequence, head,
+// slice)) live in this file-scope device array instead of an allocation, for
+// callers that cannot allocate.  Each GPU holds its own copy from the time
+// the library's code is loaded on it until the process ends.  In host code
+// `scratch` is only a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) char scratch[ATTN_DECODE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (set up on the first
+// call on each device, under a lock).
+static int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return ATTN_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_EUNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return ATTN_EHIP;
+      }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ATTN_OK;
+}
+
 }  // namespace attn
 
 using namespace attn;
@@ -240,6 +281,24 @@ int attn_decode(void* O, const void* Q, const void* K, const void* V,
     rc = ATTN_EHIP;
   }
   return rc;
+}
+
+int attn_decode_static(void* O, const void* Q, const void* K, const void* V,
+                       const int32_t* lengths, int n_splits, int B, int H,
+                       int Hkv, int Smax, int D, hipStream_t stream) {
+  int rc = check_decode(O, Q, K, V, lengths, n_splits, B, H, Hkv, Smax, D);
+  if (rc != ATTN_OK) return rc;
+  void* ws = nullptr;
+  if (n_splits > 1) {
+    // every slice writes its partial row (zeros and LSE = -inf when empty),
+    // so nothing in the scratch has to start at zero
+    if (decode_workspace_bytes(B, H, n_splits, D) > ATTN_DECODE_STATIC_SCRATCH_BYTES)
+      return ATTN_EUNSUPPORTED;
+    rc = static_scratch(&ws);
+    if (rc != ATTN_OK) return rc;
+  }
+  return hip_status(launch_decode(O, Q, K, V, lengths, n_splits, B, H, Hkv,
+                                  Smax, D, ws, stream));
 }
 
 int attn_fwd_block_sparse(void* O, const void* Q, const void* K, const void* V,

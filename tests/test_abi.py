@@ -40,7 +40,7 @@ def test_header_declares_expected_entry_points():
               "attn_decode_workspace_bytes", "attn_decode_paged", "attn_fwd_flex",
               "attn_bwd", "attn_bwd_workspace_bytes", "attn_block_scores",
               "attn_block_scores_workspace_bytes", "attn_block_mask", "attn_fwd_block_sparse",
-              "attn_mask_dump",
+              "attn_decode_static", "attn_mask_dump",
               "attn_tile_plan",
               "attn_status_string", "attn_version"):
         assert n in names
@@ -175,6 +175,26 @@ def test_decode_argument_errors(lib):
                               None) == attn.ATTN_EINVAL
     assert lib.attn_decode_workspace_bytes(0, 8, 8, 128) == 0
     assert lib.attn_decode_workspace_bytes(2, 8, 8, 96) == 0
+
+
+def test_decode_static_argument_errors(lib):
+    # the argument checks of attn_decode, and sizes past the static scratch
+    # refused before any HIP call (the array's address is not looked up)
+    def dec(O=1, Q=1, K=1, V=1, L=1, ns=8, B=2, H=8, Hkv=2, S=64, D=128):
+        return lib.attn_decode_static(O, Q, K, V, L, ns, B, H, Hkv, S, D, None)
+    assert dec(ns=0) == attn.ATTN_EINVAL
+    assert dec(H=6, Hkv=4) == attn.ATTN_EINVAL
+    assert dec(L=None) == attn.ATTN_EINVAL
+    assert dec(D=80) == attn.ATTN_EUNSUPPORTED
+    limit = attn.DECODE_STATIC_SCRATCH_BYTES
+    # the largest batch that fits at H = 32, n_splits = 8, D = 128, and one more
+    per_seq = lib.attn_decode_workspace_bytes(1, 32, 8, 128)
+    B = limit // per_seq
+    while lib.attn_decode_workspace_bytes(B, 32, 8, 128) > limit:
+        B -= 1
+    assert lib.attn_decode_workspace_bytes(B + 1, 32, 8, 128) > limit
+    assert dec(B=B + 1, H=32, Hkv=8) == attn.ATTN_EUNSUPPORTED
+    assert dec(B=4096, H=32, Hkv=8) == attn.ATTN_EUNSUPPORTED
 
 
 def test_decode_paged_argument_errors(lib):
