@@ -51,8 +51,14 @@
  *   without causal, n_splits < 1, a NULL required pointer, too small a
  *   workspace), ATTN_EUNSUPPORTED (2, D not in {64, 128}, or sizes beyond the
  *   32-bit index range), or ATTN_EHIP (3, a HIP launch or allocation error;
- *   the HIP error is cleared).  Nothing is printed and nothing is enqueued when
- *   an argument check fails.  attn_status_string() names a code.
+ *   the HIP error is cleared).  Nothing is enqueued when an argument check
+ *   fails.  attn_status_string() names a code.
+ *
+ * Logging: off by default, nothing is printed.  With ATTN_LOG=1 in the
+ *   environment (read once, at the first call) every entry point prints one
+ *   line to stderr with its sizes, flags and returned status, and each kernel
+ *   launch prints its grid, in the spirit of the debug logging the
+ *   vllm_mlx.attention backend does through its module logger.
  */
 #ifndef ATTN_MI355X_H
 #define ATTN_MI355X_H

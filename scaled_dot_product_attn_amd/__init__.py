@@ -5,8 +5,9 @@ The functions below carry the names of the C entry points declared in
 tensors, pass raw device pointers and the current HIP stream, and turn a
 non-zero status into ``RuntimeError`` (like vllm_mlx.attention's forward,
 which logs and re-raises).  Every step of the computation runs in the HIP
-kernels; there is no fallback.  ``sdpa`` and ``decode`` are allocating
-conveniences on top.
+kernels; there is no fallback.  Every tensor's shape is checked against the
+sizes passed to the library (it addresses them through raw pointers).  ``fwd``
+(also ``sdpa``) and ``decode`` are allocating conveniences on top.
 
 Layouts (row-major, contiguous): prefill Q/O (B, H, Sq, D), K/V (B, Hkv, Sk, D),
 LSE (B, H, Sq) float32; decode Q/O (B, H, D), K/V (B, Hkv, Smax, D).
@@ -115,9 +116,33 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
-def _fwd(name, dtype, O, Q, K, V, LSE, causal, window, input_pos, k_lengths, stream):
+def _expect(t, shape, name) -> None:
+    """Raise ValueError unless tensor t (if given) has exactly this shape.
+
+    The kernels read and write through raw pointers sized from the shape
+    arguments, so a tensor of another shape would be read or written past its
+    end; the C ABI cannot see tensor sizes, so the binding checks them."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _prefill_shapes(Q, K, V, O=None, LSE=None, k_lengths=None):
+    """(B, H, Hkv, Sq, Sk, D) from Q (B, H, Sq, D) and K (B, Hkv, Sk, D),
+    with V, O, LSE and k_lengths checked against them."""
+    if Q.dim() != 4 or K.dim() != 4:
+        raise ValueError("Q and K must be 4-d: (B, H, Sq, D) and (B, Hkv, Sk, D)")
     B, H, Sq, D = Q.shape
-    _, Hkv, Sk, _ = K.shape
+    Hkv, Sk = K.shape[1], K.shape[2]
+    _expect(K, (B, Hkv, Sk, D), "K")
+    _expect(V, (B, Hkv, Sk, D), "V")
+    _expect(O, (B, H, Sq, D), "O")
+    _expect(LSE, (B, H, Sq), "LSE")
+    _expect(k_lengths, (B,), "k_lengths")
+    return B, H, Hkv, Sq, Sk, D
+
+
+def _fwd(name, dtype, O, Q, K, V, LSE, causal, window, input_pos, k_lengths, stream):
+    B, H, Hkv, Sq, Sk, D = _prefill_shapes(Q, K, V, O, LSE, k_lengths)
     for t in (O, Q, K, V):
         if t.dtype != dtype:
             raise ValueError(f"{name} takes {dtype} tensors")
@@ -154,8 +179,11 @@ def attn_fwd_flex(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
     {1, H}; ``alibi_slopes`` float32 (H,); ``q_lengths`` int32 (B,);
     ``doc_q`` / ``doc_kv`` int32 (B, Sq) / (B, Sk).
     """
-    B, H, Sq, D = Q.shape
-    _, Hkv, Sk, _ = K.shape
+    B, H, Hkv, Sq, Sk, D = _prefill_shapes(Q, K, V, O, LSE, k_lengths)
+    _expect(q_lengths, (B,), "q_lengths")
+    _expect(alibi_slopes, (H,), "alibi_slopes")
+    _expect(doc_q, (B, Sq), "doc_q")
+    _expect(doc_kv, (B, Sk), "doc_kv")
     for t in (O, Q, K, V):
         if t.dtype != torch.bfloat16:
             raise ValueError("attn_fwd_flex takes bfloat16 tensors")
@@ -166,8 +194,10 @@ def attn_fwd_flex(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
                         (doc_kv, torch.int32, "doc_kv")):
         if t is not None and t.dtype != dt:
             raise ValueError(f"{name} must be {dt}")
-    if bias is not None and (bias.dim() != 4 or tuple(bias.shape[2:]) != (Sq, Sk)):
-        raise ValueError("bias must be (bias_B, bias_H, Sq, Sk)")
+    if bias is not None and (bias.dim() != 4 or tuple(bias.shape[2:]) != (Sq, Sk)
+                             or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H)):
+        raise ValueError("bias must be (bias_B, bias_H, Sq, Sk) with bias_B in {1, B}, "
+                         "bias_H in {1, H}")
     f = AttnFlex(_ptr(q_lengths), _ptr(alibi_slopes), _ptr(bias), _ptr(doc_q), _ptr(doc_kv),
                  bias.shape[0] if bias is not None else 0,
                  bias.shape[1] if bias is not None else 0,
@@ -185,8 +215,9 @@ def attn_block_scores_workspace_bytes(B: int, Hkv: int, Sk: int, D: int) -> int:
 def attn_block_scores(base, rescue, Q, K, kind=0, low=0.5, high=0.9, workspace=None,
                       stream=None) -> None:
     """Block scores (B, H, ceil(Sq/64), ceil(Sk/64)) float32 into base (and rescue)."""
-    B, H, Sq, D = Q.shape
-    _, Hkv, Sk, _ = K.shape
+    B, H, Hkv, Sq, Sk, D = _prefill_shapes(Q, K, K)
+    _expect(base, (B, H, -(-Sq // BLOCK), -(-Sk // BLOCK)), "base")
+    _expect(rescue, (B, H, -(-Sq // BLOCK), -(-Sk // BLOCK)), "rescue")
     for t in (Q, K):
         if t.dtype != torch.bfloat16:
             raise ValueError("attn_block_scores takes bfloat16 Q and K")
@@ -219,8 +250,7 @@ def attn_block_mask(keep, scores=None, mode=0, alpha=1.0, k=0, diagonal=0, accum
 def attn_fwd_block_sparse(O, Q, K, V, keep, LSE=None, causal=False, window=0, input_pos=0,
                           k_lengths=None, stream=None) -> None:
     """bf16 prefill on the kept 64 x 64 blocks of keep (B, H, nqb, nkb) uint8."""
-    B, H, Sq, D = Q.shape
-    _, Hkv, Sk, _ = K.shape
+    B, H, Hkv, Sq, Sk, D = _prefill_shapes(Q, K, V, O, LSE, k_lengths)
     for t in (O, Q, K, V):
         if t.dtype != torch.bfloat16:
             raise ValueError("attn_fwd_block_sparse takes bfloat16 tensors")
@@ -241,8 +271,13 @@ def attn_bwd_workspace_bytes(B: int, H: int, Sq: int, D: int) -> int:
 def attn_bwd(dQ, dK, dV, dO, Q, K, V, O, LSE, causal=False, window=0, input_pos=0,
              k_lengths=None, workspace=None, stream=None) -> None:
     """Backward of attn_fwd into dQ, dK, dV (bf16); see include/attn.h."""
-    B, H, Sq, D = Q.shape
-    _, Hkv, Sk, _ = K.shape
+    B, H, Hkv, Sq, Sk, D = _prefill_shapes(Q, K, V, O, LSE, k_lengths)
+    if LSE is None:
+        raise ValueError("attn_bwd needs the forward's LSE")
+    _expect(dQ, (B, H, Sq, D), "dQ")
+    _expect(dO, (B, H, Sq, D), "dO")
+    _expect(dK, (B, Hkv, Sk, D), "dK")
+    _expect(dV, (B, Hkv, Sk, D), "dV")
     for t in (dQ, dK, dV, dO, Q, K, V, O):
         if t.dtype != torch.bfloat16:
             raise ValueError("attn_bwd takes bfloat16 tensors")
@@ -264,8 +299,14 @@ def attn_decode_workspace_bytes(B: int, H: int, n_splits: int, D: int) -> int:
 
 
 def _dec_args(O, Q, K, V, lengths):
+    if Q.dim() != 3 or K.dim() != 4:
+        raise ValueError("decode Q must be (B, H, D) and K (B, Hkv, Smax, D)")
     B, H, D = Q.shape
-    _, Hkv, Smax, _ = K.shape
+    Hkv, Smax = K.shape[1], K.shape[2]
+    _expect(K, (B, Hkv, Smax, D), "K")
+    _expect(V, (B, Hkv, Smax, D), "V")
+    _expect(O, (B, H, D), "O")
+    _expect(lengths, (B,), "lengths")
     for t in (O, Q, K, V):
         if t.dtype != torch.bfloat16:
             raise ValueError("decode takes bfloat16 tensors")
@@ -309,10 +350,14 @@ def attn_decode_paged(O, Q, K_cache, V_cache, block_tables, lengths, n_splits=8,
     ``block_tables`` int32 (B, max_blocks), ``lengths`` int32 (B,); with
     ``workspace=None`` the library allocates its scratch stream-ordered.
     """
+    if Q.dim() != 3 or K_cache.dim() != 4:
+        raise ValueError("Q must be (B, H, D) and K_cache (num_blocks, block_size, Hkv, D)")
     B, H, D = Q.shape
     num_blocks, block_size, Hkv, Dk = K_cache.shape
     if Dk != D or tuple(V_cache.shape) != tuple(K_cache.shape):
         raise ValueError("K_cache / V_cache must be (num_blocks, block_size, Hkv, D)")
+    _expect(O, (B, H, D), "O")
+    _expect(lengths, (B,), "lengths")
     for t in (O, Q, K_cache, V_cache):
         if t.dtype != torch.bfloat16:
             raise ValueError("decode takes bfloat16 tensors")
@@ -333,6 +378,9 @@ def attn_decode_paged(O, Q, K_cache, V_cache, block_tables, lengths, n_splits=8,
 def attn_mask_dump(M, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
                    stream=None) -> None:
     """The kernels' own mask predicate into M (uint8 (Sq, Sk))."""
+    _expect(M, (Sq, Sk), "M")
+    if M.dtype != torch.uint8:
+        raise ValueError("M must be uint8")
     rc = lib().attn_mask_dump(_ptr(M), Sq, Sk, int(bool(causal)), int(window),
                               int(input_pos), Sk if k_len is None else int(k_len),
                               _stream(stream))
@@ -342,6 +390,9 @@ def attn_mask_dump(M, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
 def attn_tile_plan(P, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
                    stream=None) -> None:
     """The prefill kernel's tile plan into P (int8 (ceil(Sq/256), ceil(Sk/64)))."""
+    _expect(P, (-(-Sq // TILE_M), -(-Sk // TILE_N)), "P")
+    if P.dtype != torch.int8:
+        raise ValueError("P must be int8")
     rc = lib().attn_tile_plan(_ptr(P), Sq, Sk, int(bool(causal)), int(window),
                               int(input_pos), Sk if k_len is None else int(k_len),
                               _stream(stream))
@@ -352,15 +403,19 @@ def attn_tile_plan(P, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
 # allocating conveniences
 # ---------------------------------------------------------------------------
 
-def sdpa(q, k, v, causal=False, window=0, input_pos=0, k_lengths=None,
-         return_lse=True, stream=None):
-    """Allocate O (and LSE) and run the forward matching q's dtype."""
+def fwd(q, k, v, causal=False, window=0, input_pos=0, k_lengths=None,
+        return_lse=True, stream=None):
+    """Allocate O (and LSE) and run the forward matching q's dtype
+    (attn_fwd for bfloat16, attn_fwd_f32 for float32)."""
     B, H, Sq, D = q.shape
     O = torch.empty_like(q)
     LSE = torch.empty(B, H, Sq, dtype=torch.float32, device=q.device) if return_lse else None
     fn = attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_f32
     fn(O, q, k, v, LSE, causal, window, input_pos, k_lengths, stream)
     return (O, LSE) if return_lse else O
+
+
+sdpa = fwd  # the same allocating forward under the scaled-dot-product name
 
 
 def decode(q, k, v, lengths, n_splits=8, stream=None):

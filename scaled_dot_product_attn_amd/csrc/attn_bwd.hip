@@ -38,6 +38,7 @@
 #include <stdint.h>
 
 #include "attn_common.h"
+#include "attn_host.h"
 
 namespace attn {
 
@@ -728,6 +729,9 @@ static hipError_t launch_bwd_d(void* dQ, void* dK, void* dV, const void* dO,
   }
   if (Sk > 0) {
     const int nkt = (Sk + kKvTile - 1) / kKvTile;
+    if (log_enabled())
+      log_line("  attn_bwd_dkdv8_kernel<D=%d> grid=(%d, %d, %d) threads=%d", D, nkt, Hkv, B,
+               kThreads8);
     hipLaunchKernelGGL(attn_bwd_dkdv8_kernel<D>, dim3(nkt, Hkv, B), dim3(kThreads8), 0,
                        stream, (__bf16*)dK, (__bf16*)dV, (const __bf16*)dO,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V,
@@ -738,6 +742,8 @@ static hipError_t launch_bwd_d(void* dQ, void* dK, void* dV, const void* dO,
   }
   if (rows == 0) return hipSuccess;
   const int nqt = (Sq + kDqRows - 1) / kDqRows;
+  if (log_enabled())
+    log_line("  attn_bwd_dq_kernel<D=%d> grid=(%d, %d, %d) threads=%d", D, nqt, H, B, kThreads);
   hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(nqt, H, B), dim3(kThreads), 0,
                      stream, (__bf16*)dQ, (const __bf16*)dO, (const __bf16*)Q,
                      (const __bf16*)K, (const __bf16*)V, (const float*)delta,

@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_host.h"
+
 namespace attn {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -565,6 +567,9 @@ static hipError_t launch_split(const void* Q, const void* K, const void* V,
   const int n_hchunks = (G + GM - 1) / GM;
   const long long grid = (long long)B * Hkv * n_hchunks * n_splits;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  if (log_enabled())
+    log_line("  attn_decode_split_kernel<D=%d, GM=%d> grid=%lld threads=%d", D, GM, grid,
+             kDecThreads);
   hipLaunchKernelGGL((attn_decode_split_kernel<D, GM>), dim3((unsigned)grid),
                      dim3(kDecThreads), 0, stream, (const __bf16*)Q,
                      (const __bf16*)K, (const __bf16*)V, lengths, Opart, Lpart,
@@ -619,6 +624,9 @@ static hipError_t launch_paged_split(const void* Q, const void* Kc,
   const int n_hchunks = (G + GM - 1) / GM;
   const long long grid = (long long)B * Hkv * n_hchunks * n_splits;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  if (log_enabled())
+    log_line("  attn_decode_paged_kernel<D=%d, GM=%d, WAVE_BLOCK=%d> grid=%lld threads=%d", D,
+             GM, (int)WAVE_BLOCK, grid, kDecThreads);
   hipLaunchKernelGGL((attn_decode_paged_kernel<D, GM, WAVE_BLOCK>), dim3((unsigned)grid),
                      dim3(kDecThreads), 0, stream, (const __bf16*)Q,
                      (const __bf16*)Kc, (const __bf16*)Vc, tables, lengths,

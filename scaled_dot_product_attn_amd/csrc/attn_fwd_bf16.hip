@@ -53,6 +53,7 @@
 
 #include "../../include/attn.h"
 #include "attn_common.h"
+#include "attn_host.h"
 
 #ifndef KFWD_OP_DEPTH
 #define KFWD_OP_DEPTH 6
@@ -753,22 +754,20 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   }
 }
 
-// Number of persistent workgroups for `total` items (one per CU, a multiple
-// of 8), or 0 for a launch of one workgroup per item when there are too few
-// items to pair up.
+// Number of persistent workgroups for `total` items (per_cu per CU, a
+// multiple of 8), or 0 for a launch of one workgroup per item when there are
+// too few items to pair up.
 static int persistent_workgroups(long long total, int per_cu = 1) {
-  static int cu_count[64];  // per device; 0 = not queried yet
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cu_count[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      n = -1;
-    cu_count[dev] = n > 0 ? n : -1;
-  }
-  const int n_wg = (cu_count[dev] / 8) * 8 * per_cu;
+  const int n_wg = (device_cu_count() / 8) * 8 * per_cu;
   if (n_wg < 8 || total < 2LL * n_wg) return 0;
   return n_wg;
+}
+
+static void log_fwd_grid(const char* kernel, int D, unsigned grid, int threads,
+                         long long items, int n_wg) {
+  if (log_enabled())
+    log_line("  %s<D=%d> grid=%u threads=%d items=%lld %s", kernel, D, grid, threads,
+             items, n_wg > 0 ? "persistent" : "one workgroup per item");
 }
 
 template <int D>
@@ -782,6 +781,7 @@ hipError_t launch_fwd_bf16(void* O, const void* Q, const void* K,
   const int n_wg = persistent_workgroups(total);
   const unsigned grid = n_wg > 0 ? (unsigned)n_wg : (unsigned)total;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  log_fwd_grid("attn_fwd_bf16_kernel", D, grid, kFwdThreads, total, n_wg);
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, false>), dim3(grid),
                      dim3(kFwdThreads), 0, stream, (__bf16*)O,
                      (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
@@ -812,6 +812,8 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
   fx.prefix = f->prefix;
   fx.softcap = f->softcap;
   fx.qk_scale = f->qk_scale > 0.f ? f->qk_scale : 1.f / sqrtf((float)D);
+  log_fwd_grid(fx.bias ? "attn_fwd_bf16_kernel[flex+bias]" : "attn_fwd_bf16_kernel[flex]", D,
+               grid, kFwdThreads, total, n_wg);
   // the bias tile costs 32 registers per lane: a kernel of its own
   if (fx.bias)
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, false>), dim3(grid),
@@ -840,6 +842,7 @@ hipError_t launch_fwd_sparse(void* O, const void* Q, const void* K,
   const int n_wg = persistent_workgroups(total, 2);  // two workgroups per CU
   const unsigned grid = n_wg > 0 ? (unsigned)n_wg : (unsigned)total;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  log_fwd_grid("attn_fwd_bf16_kernel[block-sparse]", D, grid, NT, total, n_wg);
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, true>), dim3(grid),
                      dim3(NT), 0, stream, (__bf16*)O,
                      (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
