@@ -61,7 +61,10 @@ repository's design notes):
   each; the slice merge weighs each slice by exp(LSE_s - max LSE);
 * flex: score mods act on the scaled score, bias and ALiBi are added first
   and soft-capping comes last; ALiBi adds slope * (q - kv) literally, with
-  absolute positions; the bias and doc_q are indexed by the local query row;
+  absolute positions; the bias is indexed by the local query row; doc_q
+  holds the document ids of the Sq query rows (row i at absolute position
+  input_pos + i, so a single id vector doc of a whole sequence gives
+  doc_q[i] = doc[input_pos + i] and doc_kv[j] = doc[j]);
   a prefix ORs keys j < prefix into the causal / window set; rows at or past
   q_lengths[b] attend to nothing;
 * block scores: radius quantiles per KV head with linear interpolation; a
@@ -84,9 +87,9 @@ import numpy as np
 
 NEG_INF = -np.inf
 
-# Tile classes of the block plan (Tylo.jl "Primitives", ``BlockMask``: per
-# query block, the KV blocks holding any unmasked element, and which of those
-# are fully unmasked).
+# Tile classes of the block plan (Tylo.jl "Primitives", ``BlockMask``): a
+# (query tile, key tile) pair is empty (no allowed pair), full (every pair
+# allowed) or partial.
 TILE_EMPTY = 0
 TILE_PARTIAL = 1
 TILE_FULL = 2
@@ -603,11 +606,16 @@ def minmax_block_scores_ref(Q, K, block_size: int = 64):
     return out
 
 
-def relative_block_mask_ref(scores, alpha: float) -> np.ndarray:
+def relative_block_mask_ref(scores, alpha: float, dtype=np.float64) -> np.ndarray:
     """Keep the blocks whose exp(score) is at least alpha times the row maximum
-    (mlx-arsenal ``relative_block_mask``), i.e. score >= max + ln(alpha)."""
-    s = np.asarray(scores, dtype=np.float64)
-    return s >= s.max(axis=-1, keepdims=True) + math.log(alpha)
+    (mlx-arsenal ``relative_block_mask``), i.e. score >= max + ln(alpha).
+
+    ``dtype`` is the precision the threshold is formed and compared in (the
+    page fixes none): float64 by default; float32 takes the keep/drop decision
+    exactly as a float32 implementation does (max and ln(alpha) rounded to
+    float32, their sum rounded once)."""
+    s = np.asarray(scores, dtype=dtype)
+    return s >= s.max(axis=-1, keepdims=True) + dtype(math.log(alpha))
 
 
 def top_k_block_mask_ref(scores, k: int) -> np.ndarray:

@@ -1,7 +1,8 @@
 // Block-score estimators and block masks for block-sparse prefill on gfx950.
 //
-// mlx-arsenal "Radius-bounded block scores (RBS)": block-sparse attention
-// scores each (query block, key block) pair from a summary of the key block.
+// mlx-arsenal "Radius-bounded block scores (RBS)": a block score estimates how
+// much a query block attends to a key block from a few statistics of the
+// key block, without the token-level scores.
 //   base    per query token q.c_b / sqrt(D)   (c_b the block's centroid)
 //   rescue  (q.c_b + ||q|| r_b beta_b) / sqrt(D), r_b = max ||k - c_b||,
 //           beta_b = clip((r_b - r_low) / (r_high - r_low), 0, 1) from the

@@ -982,6 +982,20 @@ def test_relative_and_topk_masks_hand_worked():
                                   [[1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 1, 0]])
 
 
+def test_relative_mask_decision_precision():
+    # ln 0.18 = -1.71479842809..., which float32 rounds down to
+    # -1.71479845047; a score at exactly that float32 value sits below the
+    # exact threshold (dropped in float64) and on the float32 threshold (kept
+    # when the decision is taken in float32, as a float32 kernel takes it)
+    t32 = np.float32(math.log(0.18))
+    assert float(t32) < math.log(0.18)
+    s = np.array([[0.0, t32, np.float32(-1.8), np.float32(-1.7)]], dtype=np.float32)
+    np.testing.assert_array_equal(ora.relative_block_mask_ref(s, 0.18),
+                                  [[True, False, False, True]])
+    np.testing.assert_array_equal(ora.relative_block_mask_ref(s, 0.18, np.float32),
+                                  [[True, True, False, True]])
+
+
 def test_block_sparse_attention_vs_torch_and_special_cases():
     rng = np.random.default_rng(93)
     B, H, Hkv, S, D, bs = 1, 4, 2, 20, 8, 4
