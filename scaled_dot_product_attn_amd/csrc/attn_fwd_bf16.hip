@@ -13,17 +13,21 @@
 //
 // Ping-pong between two wave groups.  Waves 0-3 (group A) and 4-7 (group B)
 // sit one per SIMD each, so every SIMD holds one wave of each group.  Each
-// wave alternates two phases, separated by workgroup barriers:
+// wave alternates two phases:
 //   M-phase k: O += P(k-1) V(k-1) and S(k) = K(k) Q^T   (32 MFMAs)
-//   V-phase k: mask and online softmax of S(k) -> P(k), plus staging
-// and group B runs one phase behind group A, so while one wave of a SIMD
-// feeds the matrix core the other works on the vector ALU.
+//   V-phase k: mask and online softmax of S(k) -> P(k)
+// with one workgroup barrier per tile: window k is M(k) then V(k) for group
+// A and V(k-1) then M(k) for group B, so at the start of a window one wave of
+// each SIMD feeds the matrix core while the other runs the softmax, and they
+// swap halfway (the M-phase runs at raised wave priority).
 //
-// Staging: K and V^T each have a two-tile LDS ring.  In V-phase k group A
-// stores K(k+1) and group B stores V(k+1) (transposed), from registers loaded
-// by buffer loads issued one V-phase earlier.  Reads of K(k) happen in the
-// M-phases k of both groups, reads of V(k) in the M-phases k+1, so no buffer
-// is rewritten while a group may still read it.
+// Staging: K and V tiles go from HBM straight into LDS (buffer loads with the
+// LDS bit, issued by all eight waves two windows ahead of their use, at the
+// start of a V-phase), K into a three-slot ring of padded rows, V into a
+// four-slot ring of row-major rows read as V^T by transposing LDS reads.  K(k)
+// is read in window k, V(k) in window k+1, so a slot is rewritten only after
+// the barrier that ends its last reader's window; each wave waits for its own
+// loads of the next window's tiles just before the barrier.
 //
 // Contractions on the matrix cores (v_mfma_f32_32x32x16_bf16), transposed so
 // that one lane owns one query row:
@@ -32,8 +36,8 @@
 //        row sum are in-lane reductions plus one exchange with lane l^32.
 //   O^T (32 d x 32 queries) += V^T (32 d x 16 keys) * P^T (16 keys x 32 q)
 //     -> P^T is the S^T accumulator itself, rounded to bf16: no shuffle.
-//   The key order inside V^T's LDS rows is permuted to match the order in
-//   which the S^T accumulator registers hold the keys.
+//   The transposing reads (ds_read_b64_tr_b16) deliver V^T's keys in the
+//   order in which the S^T accumulator registers hold them.
 //
 // Flex variants (FLEX = true; Tylo.jl "Primitives", flex_attention! and its
 // mods): the same kernel with the score rewritten before the softmax, in this
@@ -42,7 +46,10 @@
 // and the mask extended by a prefix (prefix_lm = CausalMask | PrefixMask),
 // per-batch query lengths (q_lengths) and document ids (DocumentMask).  The
 // bias tile of a lane's row is loaded at the start of the M-phase that computes
-// the tile's scores, document ids of the keys are staged in LDS with K.
+// the tile's scores, document ids of the keys are loaded into LDS with K.
+//
+// The block-sparse instantiation (SPARSE) keeps register staging: four waves
+// without groups, K and V^T written to two-tile rings by the threads.
 //
 // Online softmax in base 2: t = s * log2(e) / sqrt(D), p = exp2(t - m).  The
 // running max m is only raised when a tile's max exceeds it by more than
@@ -119,7 +126,67 @@ struct FwdLds {
   static constexpr int kBytesOWave = 32 * kRowO;
   static constexpr int kOffO = kTotalFlex;
   static constexpr int kTotalAll = kOffO + (kFwdThreads / 64) * kBytesOWave;
+  // Direct-to-LDS staging (the ping-pong kernels): K in a ring of kRingK
+  // padded tiles as above; V in a ring of kRingV unpadded row-major tiles
+  // whose 16-byte chunks are XOR-swizzled (v_swizzle) for the transposing
+  // reads that deliver V^T operands; document ids beside K.  The output
+  // staging reuses the rings once every wave is past its last product.
+  static constexpr int kRingK = 3, kRingV = 4;
+  static constexpr int kRowVd = D * 2;
+  static constexpr int kBytesVd = kFwdTileN * kRowVd;
+  static constexpr int kOffVd = kRingK * kBytesK;
+  static constexpr int kOffDocD = kOffVd + kRingV * kBytesVd;
+  // (document ids are read in V-phases, which group B runs a window after
+  // group A: their ring is as deep as V's)
+  static constexpr int kTotalDma = kOffDocD + kRingV * kBytesDoc;
+  static_assert(kTotalDma >= (kFwdThreads / 64) * kBytesOWave, "O staging fits the rings");
+  // DMA instructions per tile: 64 lanes x 16 bytes each
+  static constexpr int kChunksK = kRowK / 16;                 // incl. the pad chunk
+  static constexpr int kInstrK = kFwdTileN * kChunksK / 64;
+  static constexpr int kInstrV = kFwdTileN * (D / 8) / 64;
+  static_assert(kFwdTileN * kChunksK % 64 == 0, "whole K instructions");
 };
+
+// One 16-byte-per-lane load from a buffer straight into LDS: lane l's chunk
+// lands at lds_addr + 16 l.  Written as inline assembly so that the compiler
+// does not treat the loads still in flight as pending LDS writes (it would
+// wait for them before every LDS read and barrier); the kernel waits for them
+// itself (s_waitcnt vmcnt) before the barrier that precedes their readers.
+// The instruction writes no vector register.
+__device__ inline void lds_load16(u32x4_t rsrc, uint32_t lds_addr, int voffset) {
+  asm volatile(
+      "s_nop 0\n\t"  // M0 written just before: one wait state
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr)
+      : "memory");
+}
+
+// A raw buffer descriptor (as for __builtin_amdgcn_make_buffer_rsrc: no
+// stride, num_records bytes, out-of-range reads return zero) in four scalar
+// registers, for the inline-assembly loads above.
+__device__ inline u32x4_t buffer_desc_s(const void* base, int num_records) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4_t d;
+  d[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+  d[2] = __builtin_amdgcn_readfirstlane((uint32_t)num_records);
+  d[3] = (uint32_t)kBufferRsrcWord3;
+  return d;
+}
+
+__device__ inline uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Chunk swizzle of the row-major V tiles: chunk c of row r is stored at
+// c ^ v_swizzle(r).  A transposing read covers 4 consecutive rows (from a
+// multiple of 4) x 4 aligned chunks with 32 lanes; the swizzle spreads those
+// 16 (row, chunk) pairs over distinct 16-byte bank groups.
+template <int D>
+__device__ inline int v_swizzle(int r) {
+  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   f32x2_t v = {a, b};
@@ -180,7 +247,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   static_assert(TM % kSparseBlock == 0, "row blocks per workgroup");
 
   // (the block-sparse kernel stages O in the K/V rings, after a barrier)
-  __shared__ __attribute__((aligned(16))) char smem[SPARSE ? L::kTotal : L::kTotalAll];
+  __shared__ __attribute__((aligned(16))) char smem[SPARSE ? L::kTotal : L::kTotalDma];
   // block-sparse: the key tiles some row block of this workgroup keeps, and
   // per listed tile the keep bits of its 64-row blocks
   __shared__ int16_t s_list[SPARSE ? kSparseMaxTiles : 1];
@@ -340,6 +407,46 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(V + valid_base), (short)0, nvalid * D * 2, kBufferRsrcWord3);
 
+  // ---- direct-to-LDS staging (ping-pong kernels) ----
+  // A tile's K rows are kInstrK instructions, its V rows kInstrV; wave w
+  // issues instructions w, w + 8, ...  Lane l of instruction n fills the 16
+  // bytes at the instruction's LDS address + 16 l, so each lane fetches the
+  // chunk the layout puts in that slot: for K, slot s holds row s / kChunksK,
+  // chunk s % kChunksK (the pad chunk re-reads the row's last chunk); for V,
+  // row s / (D / 8) and the chunk the swizzle stores there.
+  constexpr int NDMA = L::kInstrK + L::kInstrV;
+  constexpr int DMA_PER_WAVE = (NDMA + kFwdWaves - 1) / kFwdWaves;
+  int dma_voff[DMA_PER_WAVE];
+#pragma unroll
+  for (int t = 0; t < DMA_PER_WAVE; ++t) {
+    const int n = wave + kFwdWaves * t;
+    int off = 0;
+    if (n < L::kInstrK) {
+      const int sl = n * 64 + lane;
+      const int r = sl / L::kChunksK;
+      const int c = min(sl % L::kChunksK, L::kChunksK - 2);
+      off = (r * D + c * 8) * 2;
+    } else if (n < NDMA) {
+      const int sl = (n - L::kInstrK) * 64 + lane;
+      const int r = sl / (D / 8);
+      const int c = (sl % (D / 8)) ^ v_swizzle<D>(r);
+      off = (r * D + c * 8) * 2;
+    }
+    dma_voff[t] = off;
+  }
+  // V^T operand reads: lane l of a transposing read points at 4 d-values of
+  // one row; per 32-wide d block db its offset inside a 16-row slice
+  int vt_off[DBLK];
+  {
+    const int g4 = lane >> 4, j = lane & 15;
+    const int rr = (g4 >> 1) * 4 + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int d = db * 32 + (g4 & 1) * 16 + (j & 3) * 4;
+      vt_off[db] = rr * L::kRowVd + (((d >> 3) ^ v_swizzle<D>(rr)) << 4) + (d & 7) * 2;
+    }
+  }
+
   // ---- flex per-lane state ----
   const bool has_bias = FLEX && BIAS;
   const bool has_alibi = FLEX && fx.alibi != nullptr;
@@ -450,6 +557,46 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     }
   };
 
+  // Direct-to-LDS loads of the idx-th walked tile into ring slots idx % kRingK
+  // (K, document ids) and idx % kRingV (V).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const u32x4_t kdesc = buffer_desc_s(K + valid_base, nvalid * D * 2);
+  const u32x4_t vdesc = buffer_desc_s(V + valid_base, nvalid * D * 2);
+  const u32x4_t ddesc = buffer_desc_s(has_doc ? (const void*)(fx.doc_kv + (size_t)b * Sk + geo.union_lo)
+                                              : nullptr,
+                                      has_doc ? nvalid * 4 : 0);
+  auto dma_tile = [&](int idx) {
+    const int kt = tile_at(idx);
+    const int rel = (kt * kFwdTileN - geo.union_lo) * D * 2;  // in the valid range
+    const uint32_t kdst = lds_addr_of(smem + (idx % L::kRingK) * L::kBytesK);
+    const uint32_t vdst = lds_addr_of(smem + L::kOffVd + (idx % L::kRingV) * L::kBytesVd);
+#pragma unroll
+    for (int t = 0; t < DMA_PER_WAVE; ++t) {
+      const int n = wave_u + kFwdWaves * t;
+      if (n < L::kInstrK)
+        lds_load16(kdesc, kdst + n * 1024, dma_voff[t] + rel);
+      else if (n < NDMA)
+        lds_load16(vdesc, vdst + (n - L::kInstrK) * 1024, dma_voff[t] + rel);
+    }
+    if (FLEX && has_doc && wave_u == kFwdWaves - 1 && lane < kFwdTileN / 4)
+      lds_load16(ddesc,
+                 lds_addr_of(smem + L::kOffDocD + (idx % L::kRingV) * L::kBytesDoc),
+                 (kt * kFwdTileN - geo.union_lo + lane * 4) * 4);
+  };
+  // Wait until this wave's loads of the tile after the current one have
+  // landed, leaving those of the tile after that in flight (loads complete in
+  // order; every wave issues at least NDMA / 8 loads per tile; the flex
+  // kernel's later bias loads only make the wait longer).
+  auto dma_wait = [&](bool more_in_flight) {
+    static_assert(NDMA / kFwdWaves == 4 || NDMA / kFwdWaves == 2, "wait counts");
+    if (more_in_flight) {
+      if constexpr (NDMA / kFwdWaves == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
+
   f32x16_t s[2];           // S^T of the current tile (two 32-key blocks)
   u32x4_t pb[2][2];        // P^T of the previous tile, packed bf16 (MFMA B operands)
 
@@ -475,7 +622,68 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       do_pv = do_pv && wave_keeps(idx - 1);
       do_s = do_s && wave_keeps(idx);
     }
-    if (!FLEX && do_pv && do_s) {
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    // V^T operand i (< NPV) of the previous tile: two transposing reads, rows
+    // kb2 * 32 + st * 16 + 8 h8 + the lane's row of its 16-row slice
+    auto vt_operand = [&](const char* vb, int i) -> bf16x8_t {
+      const int pr = i / DBLK, db = i % DBLK;
+      i16x4_t part[2];
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8)
+        part[h8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vb + vt_off[db] +
+                                                        (pr * 16 + h8 * 8) * L::kRowVd));
+      return __builtin_bit_cast(bf16x8_t,
+                                __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    if (PP && !FLEX && do_pv && do_s) {
+      const char* vb = smem + L::kOffVd + ((idx - 1) % L::kRingV) * L::kBytesVd;
+      const char* kb = smem + (idx % L::kRingK) * L::kBytesK;
+      constexpr int NPV = DBLK * 4;
+      constexpr int NOP = NPV + 2 * KSTEPS;
+      auto load_op = [&](int i) -> bf16x8_t {
+        if (i < NPV) return vt_operand(vb, i);
+        const int j = i - NPV, ks = j >> 1, kb2 = j & 1;
+        return *(const bf16x8_t*)(kb + (kb2 * 32 + lrow) * L::kRowK + half * 16 + ks * 32);
+      };
+      bf16x8_t ring[kFwdOpDepth];
+#pragma unroll
+      for (int i = 0; i < kFwdOpDepth; ++i) ring[i] = load_op(i);
+      s[0] = s[1] = f32x16_t{};
+#pragma unroll
+      for (int i = 0; i < NOP; ++i) {
+        const bf16x8_t a = ring[i % kFwdOpDepth];
+        if (i + kFwdOpDepth < NOP) ring[i % kFwdOpDepth] = load_op(i + kFwdOpDepth);
+        if (i < NPV) {
+          const int pr = i / DBLK, db = i % DBLK;
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a, __builtin_bit_cast(bf16x8_t, pb[pr >> 1][pr & 1]), oacc[db], 0, 0, 0);
+        } else {
+          const int j = i - NPV, ks = j >> 1, kb2 = j & 1;
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[kb2], 0, 0, 0);
+        }
+      }
+      // the LDS reads of the first operands, then one MFMA and the reads of
+      // the operand kFwdOpDepth ahead alternately (two transposing reads per
+      // V^T operand), then the last MFMAs (0x100 = LDS read, 0x008 = MFMA)
+      {
+        constexpr int first = (kFwdOpDepth < NPV ? kFwdOpDepth : NPV) * 2 +
+                              (kFwdOpDepth > NPV ? kFwdOpDepth - NPV : 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NOP - kFwdOpDepth; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + kFwdOpDepth < NPV)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kFwdOpDepth, 0);
+      asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+      return;
+    }
+    if (!PP && !FLEX && do_pv && do_s) {
       // Steady state: the 32 products of the phase with their LDS operand
       // reads kept kFwdOpDepth ahead (left to itself the compiler keeps only
       // one or two in flight and each MFMA waits for its read).  Consecutive
@@ -526,23 +734,35 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       return;
     }
     if (do_pv) {
-      const char* vb = smem + L::kOffV + ((idx - 1) & 1) * L::kBytesV;
+      if constexpr (PP) {
+        const char* vb = smem + L::kOffVd + ((idx - 1) % L::kRingV) * L::kBytesVd;
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const char* arow = vb + (db * 32 + lrow) * L::kRowV + half * 16;
+        for (int pr = 0; pr < 4; ++pr)
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            bf16x8_t a = *(const bf16x8_t*)(arow + (kb2 * 2 + st) * 32);
+          for (int db = 0; db < DBLK; ++db) {
+            const bf16x8_t a = vt_operand(vb, pr * DBLK + db);
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                a, __builtin_bit_cast(bf16x8_t, pb[kb2][st]), oacc[db], 0, 0, 0);
+                a, __builtin_bit_cast(bf16x8_t, pb[pr >> 1][pr & 1]), oacc[db], 0, 0, 0);
           }
+      } else {
+        const char* vb = smem + L::kOffV + ((idx - 1) & 1) * L::kBytesV;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          const char* arow = vb + (db * 32 + lrow) * L::kRowV + half * 16;
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+              bf16x8_t a = *(const bf16x8_t*)(arow + (kb2 * 2 + st) * 32);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  a, __builtin_bit_cast(bf16x8_t, pb[kb2][st]), oacc[db], 0, 0, 0);
+            }
+        }
       }
     }
     if (FLEX && do_s && has_bias) bias_loads(idx);
     if (do_s) {
-      const char* kb = smem + (idx & 1) * L::kBytesK;
+      const char* kb = smem + (PP ? idx % L::kRingK : idx & 1) * L::kBytesK;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         s[kb2] = f32x16_t{};
@@ -607,7 +827,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   };
   // flex: a key whose document differs from the row's is blocked
   auto doc_mask = [&](int idx) {
-    const char* db = smem + L::kOffDoc + (idx & 1) * L::kBytesDoc + half * 16;
+    const char* db = smem + (PP ? L::kOffDocD + (idx % L::kRingV) * L::kBytesDoc
+                                : L::kOffDoc + (idx & 1) * L::kBytesDoc) + half * 16;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -623,6 +844,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const float sl2 = FLEX ? (transform ? 1.f : fx.qk_scale * kLog2e) : scale_log2;
 
   auto v_phase = [&](int idx) {
+    if constexpr (PP) {
+      // group A's V(idx) runs in window idx, group B's in window idx + 1:
+      // both load the tile two windows ahead, first thing in the phase
+      const int ahead = idx + 2 + grp;
+      if (ahead < n_tiles) dma_tile(ahead);
+    }
     const int kt = tile_at(idx);
     const int j0 = kt * kFwdTileN;
     if constexpr (FLEX) {
@@ -651,11 +878,20 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
           if ((unsigned)(c - t_lo) >= width) s[kb2][r] = -INFINITY;
         }
     }
-    float mx = s[0][0];
+    // row max as a tree of three-input maxima (v_max3_f32)
+    float m16[11];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    for (int t = 0; t < 10; ++t) {
+      const int a = 3 * t, b = a + 1, c = a + 2;
+      m16[t] = __builtin_fmaxf(__builtin_fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]),
+                               s[c >> 4][c & 15]);
+    }
+    m16[10] = __builtin_fmaxf(s[1][14], s[1][15]);
+    float mx = __builtin_fmaxf(__builtin_fmaxf(m16[0], m16[1]), m16[2]);
+    mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[3]), m16[4]);
+    mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[5]), m16[6]);
+    mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[7]), m16[8]);
+    mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[9]), m16[10]);
     const float mt = pair_max(mx) * sl2;
     const bool need = mt > m_run + kLazyRescale;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -669,18 +905,31 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
     const float mref = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
+    // Wide schedule: only this wave of its SIMD runs vector work now, so the
+    // latency of each dependent step must be covered by independent work:
+    // all 32 exponents' arguments, then the 32 exponentials, then packing and
+    // a tree of partial sums.
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 =
-            __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], sl2, -mref));
-        const float p1 = __builtin_amdgcn_exp2f(
-            __builtin_fmaf(s[kb2][r + 1], sl2, -mref));
-        psum += p0 + p1;
-        pb[kb2][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
-      }
+      for (int r = 0; r < 16; ++r) s[kb2][r] = __builtin_fmaf(s[kb2][r], sl2, -mref);
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb2][r] = __builtin_amdgcn_exp2f(s[kb2][r]);
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        pb[kb2][r >> 3][(r & 7) >> 1] = pack_bf16x2(s[kb2][r], s[kb2][r + 1]);
+    float q16[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) q16[r] = s[0][r] + s[1][r];
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) q16[r] = q16[r] + q16[r + w];
+    const float psum = q16[0];
     l_run += psum;
     // Pin P here: left alone, the compiler sinks the exponentials past the
     // barrier into the next MFMA phase (their only user), which serialises
@@ -688,25 +937,64 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     // other group's.
     asm volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]),
                  "+v"(l_run));
-    if (idx + 1 < n_tiles) stash((idx + 1) & 1);
-    if (idx + 2 < n_tiles) fetch(tile_at(idx + 2));
+    if constexpr (PP) {
+    } else {
+      if (idx + 1 < n_tiles) stash((idx + 1) & 1);
+      if (idx + 2 < n_tiles) fetch(tile_at(idx + 2));
+    }
   };
 
   if (n_tiles > 0) {
-    // prologue: the first tile in LDS, the second in flight
-    fetch(tile_at(0));
-    stash(0);
-    if (n_tiles > 1) fetch(tile_at(1));
-    __syncthreads();
-    if (PP && grp == 1) __syncthreads();  // group B runs one phase behind
-    for (int idx = 0; idx < n_tiles; ++idx) {
-      m_phase(idx, idx > 0, true);
+    if constexpr (PP) {
+      // prologue: the first two tiles (group B also the third) in LDS
+      const bool gb = __builtin_amdgcn_readfirstlane(tid >> 8) != 0;
+      dma_tile(0);
+      if (n_tiles > 1) dma_tile(1);
+      if (gb && n_tiles > 2) dma_tile(2);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      v_phase(idx);
+    } else {
+      // prologue: the first tile in LDS, the second in flight
+      fetch(tile_at(0));
+      stash(0);
+      if (n_tiles > 1) fetch(tile_at(1));
       __syncthreads();
     }
-    m_phase(n_tiles, true, false);
-    if (PP && grp == 0) __syncthreads();  // matches group B's extra barrier
+    if constexpr (PP) {
+      // One barrier per tile.  Both groups run M(0) V(0) M(1) V(1) ...;
+      // group A ends window k with V(k), group B with M(k), so in window k
+      // group A runs M(k) then V(k) while group B runs V(k-1) then M(k): at
+      // the start of a window one wave of each SIMD feeds the matrix core
+      // while the other runs the softmax, and they swap halfway.  Every LDS
+      // buffer written in window k (K(k+1) by A, V(k) by B) was last read in
+      // window k-1.
+      const bool group_b = __builtin_amdgcn_readfirstlane(tid >> 8) != 0;
+      for (int idx = 0; idx < n_tiles; ++idx) {
+        __builtin_amdgcn_s_setprio(3);
+        m_phase(idx, idx > 0, true);
+        __builtin_amdgcn_s_setprio(0);
+        // before a barrier, this wave's loads of the tile read in the next
+        // window have landed
+        if (group_b) {
+          dma_wait(idx + 2 < n_tiles);
+          __syncthreads();
+        }
+        v_phase(idx);
+        if (!group_b) {
+          dma_wait(idx + 2 < n_tiles);
+          __syncthreads();
+        }
+      }
+      m_phase(n_tiles, true, false);
+    } else {
+      for (int idx = 0; idx < n_tiles; ++idx) {
+        m_phase(idx, idx > 0, true);
+        __syncthreads();
+        v_phase(idx);
+        __syncthreads();
+      }
+      m_phase(n_tiles, true, false);
+    }
   }
 
   // ---- epilogue ----
@@ -720,8 +1008,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     // (without groups the staging area is the K/V rings, free once every
     // wave is past its last products)
-    if constexpr (!PP) __syncthreads();
-    char* ost = smem + (PP ? L::kOffO : 0) + wave * L::kBytesOWave;
+    __syncthreads();
+    char* ost = smem + wave * L::kBytesOWave;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
