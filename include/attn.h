@@ -76,8 +76,9 @@ extern "C" {
 #define ATTN_EUNSUPPORTED 2
 #define ATTN_EHIP 3
 
-/* Prefill tile sizes used by attn_fwd (rows of Q per workgroup, keys per
- * K/V tile); attn_tile_plan reports the plan at these sizes. */
+/* Prefill tile sizes used by attn_fwd (query rows per workgroup, counted
+ * over the query heads it serves, and keys per K/V tile); attn_tile_plan
+ * reports the plan at these sizes. */
 #define ATTN_FWD_TILE_M 256
 #define ATTN_FWD_TILE_N 64
 
@@ -342,12 +343,15 @@ int attn_decode_paged(void* O, const void* Q, const void* K_cache,
 int attn_mask_dump(uint8_t* M, int Sq, int Sk, int causal, int window,
                    int input_pos, int k_len, hipStream_t stream);
 
-/* Debug export: the tile plan attn_fwd uses, int8 (ceil(Sq/ATTN_FWD_TILE_M),
- * ceil(Sk/ATTN_FWD_TILE_N)) in P (device): 0 = empty (skipped), 1 = partial
- * (masked per element), 2 = full (no per-element mask).  Tylo.jl
- * "Primitives", BlockMask / build_block_mask. */
+/* Debug export: the tile plan attn_fwd uses for group = H / Hkv query heads
+ * per KV head.  A workgroup serves hp query heads of one KV head, hp the
+ * largest power of two up to 8 dividing group, at TP = ATTN_FWD_TILE_M / hp
+ * query positions; P (device) is int8 (ceil(Sq/TP), ceil(Sk/ATTN_FWD_TILE_N)):
+ * 0 = empty (skipped), 1 = partial (masked per element), 2 = full (no
+ * per-element mask).  ATTN_EINVAL for group < 1.  Tylo.jl "Primitives",
+ * BlockMask / build_block_mask. */
 int attn_tile_plan(int8_t* P, int Sq, int Sk, int causal, int window,
-                   int input_pos, int k_len, hipStream_t stream);
+                   int input_pos, int k_len, int group, hipStream_t stream);
 
 /* Static string naming a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -63,7 +63,7 @@ _SIGS = {
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
                                ctypes.c_size_t, _P]),
     "attn_mask_dump": (_I, [_P, _I, _I, _I, _I, _I, _I, _P]),
-    "attn_tile_plan": (_I, [_P, _I, _I, _I, _I, _I, _I, _P]),
+    "attn_tile_plan": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_version": (_I, []),
 }
@@ -387,15 +387,26 @@ def attn_mask_dump(M, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
     _check(rc, "attn_mask_dump")
 
 
-def attn_tile_plan(P, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
+def fwd_tile_positions(group: int = 1) -> int:
+    """Query positions per prefill workgroup for group = H / Hkv: TILE_M
+    divided by the query heads it serves (the largest power of two up to 8
+    dividing group)."""
+    hp = 1
+    while hp < 8 and group % (2 * hp) == 0:
+        hp *= 2
+    return TILE_M // hp
+
+
+def attn_tile_plan(P, Sq, Sk, causal=False, window=0, input_pos=0, k_len=None, group=1,
                    stream=None) -> None:
-    """The prefill kernel's tile plan into P (int8 (ceil(Sq/256), ceil(Sk/64)))."""
-    _expect(P, (-(-Sq // TILE_M), -(-Sk // TILE_N)), "P")
+    """The prefill kernel's tile plan into P (int8 (ceil(Sq/TP), ceil(Sk/64)),
+    TP = fwd_tile_positions(group))."""
+    _expect(P, (-(-Sq // fwd_tile_positions(group)), -(-Sk // TILE_N)), "P")
     if P.dtype != torch.int8:
         raise ValueError("P must be int8")
     rc = lib().attn_tile_plan(_ptr(P), Sq, Sk, int(bool(causal)), int(window),
                               int(input_pos), Sk if k_len is None else int(k_len),
-                              _stream(stream))
+                              int(group), _stream(stream))
     _check(rc, "attn_tile_plan")
 
 

@@ -71,12 +71,12 @@ __global__ void mask_dump_kernel(uint8_t* __restrict__ M, int Sq, int Sk,
 
 __global__ void tile_plan_kernel(int8_t* __restrict__ P, int Sq, int Sk,
                                  int causal, int window, int input_pos,
-                                 int kl, int nqt, int nkt) {
+                                 int kl, int nqt, int nkt, int tp) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)nqt * nkt) return;
   const int qt = (int)(idx / nkt), kt = (int)(idx % nkt);
-  const int i0 = qt * ATTN_FWD_TILE_M;
-  const int i1 = min(i0 + ATTN_FWD_TILE_M, Sq);
+  const int i0 = qt * tp;
+  const int i1 = min(i0 + tp, Sq);
   const KvGeometry g = kv_geometry(i0, i1, kl, causal, window, input_pos);
   P[idx] = (int8_t)tile_class(g, kt * ATTN_FWD_TILE_N, ATTN_FWD_TILE_N);
 }
@@ -585,11 +585,12 @@ int attn_mask_dump(uint8_t* M, int Sq, int Sk, int causal, int window,
 }
 
 int attn_tile_plan(int8_t* P, int Sq, int Sk, int causal, int window,
-                   int input_pos, int k_len, hipStream_t stream) {
-  if (Sq < 0 || Sk < 0 || (causal != 0 && causal != 1)) return ATTN_EINVAL;
+                   int input_pos, int k_len, int group, hipStream_t stream) {
+  if (Sq < 0 || Sk < 0 || (causal != 0 && causal != 1) || group < 1) return ATTN_EINVAL;
   if (window > 0 && !causal) return ATTN_EINVAL;
   if (Sq > INT_MAX - 256 || Sk > INT_MAX - 256) return ATTN_EUNSUPPORTED;
-  const int nqt = (Sq + ATTN_FWD_TILE_M - 1) / ATTN_FWD_TILE_M;
+  const int tp = ATTN_FWD_TILE_M >> fwd_heads_log2(group);
+  const int nqt = (Sq + tp - 1) / tp;
   const int nkt = (Sk + ATTN_FWD_TILE_N - 1) / ATTN_FWD_TILE_N;
   const long long n = (long long)nqt * nkt;
   if (n == 0) return ATTN_OK;
@@ -597,7 +598,7 @@ int attn_tile_plan(int8_t* P, int Sq, int Sk, int causal, int window,
   const int kl = k_len < 0 ? 0 : (k_len > Sk ? Sk : k_len);
   hipLaunchKernelGGL(tile_plan_kernel, dim3((unsigned)((n + 255) / 256)),
                      dim3(256), 0, stream, P, Sq, Sk, causal, window,
-                     input_pos, kl, nqt, nkt);
+                     input_pos, kl, nqt, nkt, tp);
   return hip_status(hipGetLastError());
 }
 

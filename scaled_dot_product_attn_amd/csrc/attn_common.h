@@ -91,6 +91,16 @@ __host__ __device__ inline KvGeometry kv_geometry(int i0, int i1, int kl,
   return g;
 }
 
+// Query heads a prefill workgroup serves, as log2: the largest power of two
+// up to 8 that divides the group size G = H / Hkv.  The workgroup's 256 rows
+// are then 256 >> log2 query positions of that many heads of one KV head,
+// which read the same K/V tiles.
+__host__ __device__ inline int fwd_heads_log2(int G) {
+  int l = 0;
+  while (l < 3 && G % (2 << l) == 0) ++l;
+  return l;
+}
+
 // Class of the key tile [j0, j0 + tile_n) for the rows described by g.
 __host__ __device__ inline int tile_class(const KvGeometry& g, int j0,
                                           int tile_n) {

@@ -227,7 +227,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     float* __restrict__ LSE, int B, int H, int Hkv, int Sq, int Sk, int causal,
     int window, int input_pos, const int32_t* __restrict__ k_lengths,
     float scale_log2, FlexArgs fx, const uint8_t* __restrict__ keep,
-    int n_wg) {
+    int n_wg, int hp_log2) {
   using L = FwdLds<D>;
   constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int DBLK = D / 32;     // 32-wide blocks of the head dimension
@@ -263,9 +263,16 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const int half = lane >> 5;  // which half of each MFMA k-slice this lane feeds
 
   // ---- work items: heaviest query tiles first, XCD-grouped by KV head ----
+  // A workgroup serves hp = 2^hp_log2 query heads of one KV head (they read
+  // the same K/V tiles) at TP = TM / hp query positions: with grouped-query
+  // attention the causal diagonal and window edges cut TP x TP blocks instead
+  // of TM x TM, so fewer tile elements are masked away.
   const int G = H / Hkv;
-  const int nqt = (Sq + TM - 1) / TM;
-  const int total = nqt * H * B;
+  const int hp = 1 << hp_log2;
+  const int TP = TM >> hp_log2;           // query positions per workgroup
+  const int nch = G >> hp_log2;           // head chunks per KV head
+  const int nqt = (Sq + TP - 1) / TP;
+  const int total = nqt * nch * Hkv * B;
   // Persistent launch (n_wg > 0 workgroups, a multiple of 8, one per CU): the
   // workgroup on XCD x (= blockIdx % 8) walks that XCD's item positions in a
   // snake order (c, 2C-1-c, 2C+c, ...), which pairs heavy and light causal
@@ -296,18 +303,19 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     const int per = total >> 3;
     if (lid < (per << 3)) wid = (lid & 7) * per + (lid >> 3);
   }
-  const int per_pair = nqt * G;
+  const int per_pair = nqt * nch;
   const int pair = wid / per_pair;
   const int rem = wid - pair * per_pair;
-  const int qt_rank = rem / G;
-  const int hg = rem - qt_rank * G;
+  const int qt_rank = rem / nch;
+  const int ch = rem - qt_rank * nch;
   const int b = pair / Hkv;
   const int g = pair - b * Hkv;
-  const int h = g * G + hg;
+  const int rb = wave >> hp_log2;         // this wave's 32-row block of the positions
+  const int h = g * G + ch * hp + (wave & (hp - 1));   // and its query head
   const int qt = causal ? (nqt - 1 - qt_rank) : qt_rank;
 
-  const int i0 = qt * TM;
-  const int i1 = min(i0 + TM, Sq);
+  const int i0 = qt * TP;
+  const int i1 = min(i0 + TP, Sq);
   const int kl = k_lengths ? min(max(k_lengths[b], 0), Sk) : Sk;
   // flex: rows at or past q_lengths[b] attend to nothing; the geometry covers
   // the live rows, and a workgroup with dead rows (or a document mask) masks
@@ -327,7 +335,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const size_t kv_base = ((size_t)(b * Hkv + g) * Sk) * D;
 
   // ---- my query row ----
-  const int qi = i0 + wave * 32 + lrow;  // global query row of this lane
+  const int qi = i0 + rb * 32 + lrow;  // global query row of this lane
   RowRange rr = row_range(qi, kl, causal, window, input_pos, prefix);
   if (FLEX && qi >= ql) rr.lo = rr.hi = 0;
 
@@ -1028,7 +1036,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       const int c = i * 64 + lane;
       const int row = c / CHUNKS, ch = c - row * CHUNKS;
       const u32x4_t v = *(const u32x4_t*)(ost + row * L::kRowO + ch * 16);
-      const int qrow = i0 + wave * 32 + row;
+      const int qrow = i0 + rb * 32 + row;
       if (qrow < Sq) *(u32x4_t*)(O + q_base + (size_t)qrow * D + ch * 8) = v;
     }
   }
@@ -1064,8 +1072,9 @@ hipError_t launch_fwd_bf16(void* O, const void* Q, const void* K,
                            int Sq, int Sk, int causal, int window,
                            int input_pos, const int32_t* k_lengths,
                            hipStream_t stream) {
-  const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
-  const long long total = (long long)nqt * H * B;
+  const int hl = fwd_heads_log2(H / Hkv);
+  const int nqt = (Sq + (kFwdTileM >> hl) - 1) / (kFwdTileM >> hl);
+  const long long total = (long long)nqt * (H >> hl) * B;
   const int n_wg = persistent_workgroups(total);
   const unsigned grid = n_wg > 0 ? (unsigned)n_wg : (unsigned)total;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
@@ -1074,7 +1083,7 @@ hipError_t launch_fwd_bf16(void* O, const void* Q, const void* K,
                      dim3(kFwdThreads), 0, stream, (__bf16*)O,
                      (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                      B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                     scale_log2, FlexArgs{}, (const uint8_t*)nullptr, n_wg);
+                     scale_log2, FlexArgs{}, (const uint8_t*)nullptr, n_wg, hl);
   return hipGetLastError();
 }
 
@@ -1084,8 +1093,9 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
                            int Sq, int Sk, int causal, int window,
                            int input_pos, const int32_t* k_lengths,
                            const attn_flex_t* f, hipStream_t stream) {
-  const int nqt = (Sq + kFwdTileM - 1) / kFwdTileM;
-  const long long total = (long long)nqt * H * B;
+  const int hl = fwd_heads_log2(H / Hkv);
+  const int nqt = (Sq + (kFwdTileM >> hl) - 1) / (kFwdTileM >> hl);
+  const long long total = (long long)nqt * (H >> hl) * B;
   const int n_wg = persistent_workgroups(total);
   const unsigned grid = n_wg > 0 ? (unsigned)n_wg : (unsigned)total;
   FlexArgs fx{};
@@ -1108,13 +1118,13 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
                        dim3(kFwdThreads), 0, stream, (__bf16*)O,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                        B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                       0.f, fx, (const uint8_t*)nullptr, n_wg);
+                       0.f, fx, (const uint8_t*)nullptr, n_wg, hl);
   else
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false, false>), dim3(grid),
                        dim3(kFwdThreads), 0, stream, (__bf16*)O,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                        B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                       0.f, fx, (const uint8_t*)nullptr, n_wg);
+                       0.f, fx, (const uint8_t*)nullptr, n_wg, hl);
   return hipGetLastError();
 }
 
@@ -1135,7 +1145,7 @@ hipError_t launch_fwd_sparse(void* O, const void* Q, const void* K,
                      dim3(NT), 0, stream, (__bf16*)O,
                      (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                      B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                     scale_log2, FlexArgs{}, keep, n_wg);
+                     scale_log2, FlexArgs{}, keep, n_wg, 0);
   return hipGetLastError();
 }
 

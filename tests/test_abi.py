@@ -222,8 +222,9 @@ def test_debug_export_argument_errors(lib):
     assert lib.attn_mask_dump(None, 4, 4, 0, 2, 0, 4, None) == attn.ATTN_EINVAL
     assert lib.attn_mask_dump(None, 4, 4, 1, 0, 0, 4, None) == attn.ATTN_EINVAL
     assert lib.attn_mask_dump(None, 0, 4, 1, 0, 0, 4, None) == attn.ATTN_OK
-    assert lib.attn_tile_plan(None, 4, 4, 1, 0, 0, 4, None) == attn.ATTN_EINVAL
-    assert lib.attn_tile_plan(None, 0, 0, 1, 0, 0, 0, None) == attn.ATTN_OK
+    assert lib.attn_tile_plan(None, 4, 4, 1, 0, 0, 4, 1, None) == attn.ATTN_EINVAL
+    assert lib.attn_tile_plan(None, 0, 0, 1, 0, 0, 0, 1, None) == attn.ATTN_OK
+    assert lib.attn_tile_plan(1, 4, 4, 1, 0, 0, 4, 0, None) == attn.ATTN_EINVAL
 
 
 @pytest.fixture(scope="module")

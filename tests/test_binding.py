@@ -179,3 +179,11 @@ def test_launch_log_only_when_asked():
     for value in (None, "0"):
         off = _run_logged(value)
         assert off.returncode == 0 and "[attn]" not in off.stderr
+
+
+@pytest.mark.parametrize("group,tp", [(1, 256), (2, 128), (3, 256), (4, 64), (6, 128),
+                                      (8, 32), (16, 32)])
+def test_tile_positions_per_group(group, tp):
+    # query positions per prefill workgroup: its 256 rows over the largest
+    # power of two up to 8 dividing the group
+    assert attn.fwd_tile_positions(group) == tp

@@ -117,13 +117,15 @@ def test_mask_dump_bitexact(Sq, Sk, causal, window, ip, kl):
     np.testing.assert_array_equal(M.cpu().numpy().astype(bool), want)
 
 
+@pytest.mark.parametrize("group", [1, 4, 8])
 @pytest.mark.parametrize("Sq,Sk,causal,window,ip,kl", MASK_CASES + [
     (4096, 4096, 1, 0, 0, 4096), (2048, 16384, 1, 4096, 14336, 16384), (4096, 4096, 0, 0, 0, 4096)])
-def test_tile_plan_bitexact(Sq, Sk, causal, window, ip, kl):
-    nqt, nkt = -(-Sq // attn.TILE_M), -(-Sk // attn.TILE_N)
+def test_tile_plan_bitexact(Sq, Sk, causal, window, ip, kl, group):
+    tp = attn.fwd_tile_positions(group)
+    nqt, nkt = -(-Sq // tp), -(-Sk // attn.TILE_N)
     P = torch.empty(nqt, nkt, dtype=torch.int8, device=DEV)
-    attn.attn_tile_plan(P, Sq, Sk, causal, window, ip, kl)
-    want = ora.tile_plan_ref(Sq, Sk, bool(causal), window, ip, kl, attn.TILE_M, attn.TILE_N)
+    attn.attn_tile_plan(P, Sq, Sk, causal, window, ip, kl, group)
+    want = ora.tile_plan_ref(Sq, Sk, bool(causal), window, ip, kl, tp, attn.TILE_N)
     np.testing.assert_array_equal(P.cpu().numpy(), want)
 
 
