@@ -124,13 +124,11 @@ struct FwdLds {
   // output staging: per wave its 32 rows of D bf16, padded like K
   static constexpr int kRowO = D * 2 + 16;
   static constexpr int kBytesOWave = 32 * kRowO;
-  static constexpr int kOffO = kTotalFlex;
-  static constexpr int kTotalAll = kOffO + (kFwdThreads / 64) * kBytesOWave;
+  static_assert((kFwdThreads / 64) * kBytesOWave <= kTotal, "O staging fits the buffers");
   // Direct-to-LDS staging (the ping-pong kernels): K in a ring of kRingK
   // padded tiles as above; V in a ring of kRingV unpadded row-major tiles
   // whose 16-byte chunks are XOR-swizzled (v_swizzle) for the transposing
-  // reads that deliver V^T operands; document ids beside K.  The output
-  // staging reuses the rings once every wave is past its last product.
+  // reads that deliver V^T operands; document ids beside K.
   static constexpr int kRingK = 3, kRingV = 4;
   static constexpr int kRowVd = D * 2;
   static constexpr int kBytesVd = kFwdTileN * kRowVd;
@@ -139,7 +137,12 @@ struct FwdLds {
   // (document ids are read in V-phases, which group B runs a window after
   // group A: their ring is as deep as V's)
   static constexpr int kTotalDma = kOffDocD + kRingV * kBytesDoc;
-  static_assert(kTotalDma >= (kFwdThreads / 64) * kBytesOWave, "O staging fits the rings");
+  // ping-pong kernels: O staged in an area of its own, half the head
+  // dimension at a time (the rings may already hold the next item's tiles)
+  static constexpr int kRowOh = D + 16;
+  static constexpr int kBytesOWaveH = 32 * kRowOh;
+  static constexpr int kOffOs = kTotalDma;
+  static constexpr int kTotalPP = kOffOs + (kFwdThreads / 64) * kBytesOWaveH;
   // DMA instructions per tile: 64 lanes x 16 bytes each
   static constexpr int kChunksK = kRowK / 16;                 // incl. the pad chunk
   static constexpr int kInstrK = kFwdTileN * kChunksK / 64;
@@ -247,7 +250,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   static_assert(TM % kSparseBlock == 0, "row blocks per workgroup");
 
   // (the block-sparse kernel stages O in the K/V rings, after a barrier)
-  __shared__ __attribute__((aligned(16))) char smem[SPARSE ? L::kTotal : L::kTotalDma];
+  __shared__ __attribute__((aligned(16))) char smem[SPARSE ? L::kTotal : L::kTotalPP];
   // block-sparse: the key tiles some row block of this workgroup keeps, and
   // per listed tile the keep bits of its 64-row blocks
   __shared__ int16_t s_list[SPARSE ? kSparseMaxTiles : 1];
@@ -282,54 +285,93 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const int per_xcd = total >> 3;
   const int wg_x = n_wg >> 3;
   const int rounds = persistent ? (per_xcd + wg_x - 1) / wg_x + 1 : 1;
-  for (int round = 0; round < rounds; ++round) {
-  int lid = blockIdx.x;
-  if (persistent) {
-    const int c = (int)blockIdx.x >> 3;
-    if (round < rounds - 1) {
-      const int pos = (round & 1) ? (round + 1) * wg_x - 1 - c : round * wg_x + c;
-      if (pos >= per_xcd) continue;
-      lid = (pos << 3) | ((int)blockIdx.x & 7);
-    } else {
-      lid = (per_xcd << 3) + (int)blockIdx.x;
-      if (lid >= total) continue;
+  // the item (workgroup-level work unit) of a round, or -1 for none
+  auto lid_of = [&](int rd) -> int {
+    int lid = blockIdx.x;
+    if (persistent) {
+      const int c = (int)blockIdx.x >> 3;
+      if (rd < rounds - 1) {
+        const int pos = (rd & 1) ? (rd + 1) * wg_x - 1 - c : rd * wg_x + c;
+        if (pos >= per_xcd) return -1;
+        lid = (pos << 3) | ((int)blockIdx.x & 7);
+      } else {
+        lid = (per_xcd << 3) + (int)blockIdx.x;
+        if (lid >= total) return -1;
+      }
+    } else if (rd > 0) {
+      return -1;
     }
-  }
-  int wid = lid;
-  {
-    // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-    // contiguous range of work so the query heads sharing a KV head (and
-    // their K/V tiles) stay in one L2.
-    const int per = total >> 3;
-    if (lid < (per << 3)) wid = (lid & 7) * per + (lid >> 3);
-  }
-  const int per_pair = nqt * nch;
-  const int pair = wid / per_pair;
-  const int rem = wid - pair * per_pair;
-  const int qt_rank = rem / nch;
-  const int ch = rem - qt_rank * nch;
-  const int b = pair / Hkv;
-  const int g = pair - b * Hkv;
+    return lid;
+  };
+  struct ItemGeo {
+    int b, g, ch, i0, i1, kl, ql, prefix;
+    bool force_partial;
+    KvGeometry geo;
+  };
+  auto item_geo = [&](int lid) -> ItemGeo {
+    ItemGeo it;
+    int wid = lid;
+    {
+      // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
+      // contiguous range of work so the query heads sharing a KV head (and
+      // their K/V tiles) stay in one L2.
+      const int per = total >> 3;
+      if (lid < (per << 3)) wid = (lid & 7) * per + (lid >> 3);
+    }
+    const int per_pair = nqt * nch;
+    const int pair = wid / per_pair;
+    const int rem = wid - pair * per_pair;
+    const int qt_rank = rem / nch;
+    it.ch = rem - qt_rank * nch;
+    it.b = pair / Hkv;
+    it.g = pair - it.b * Hkv;
+    const int qt = causal ? (nqt - 1 - qt_rank) : qt_rank;
+    it.i0 = qt * TP;
+    it.i1 = min(it.i0 + TP, Sq);
+    it.kl = k_lengths ? min(max(k_lengths[it.b], 0), Sk) : Sk;
+    // flex: rows at or past q_lengths[b] attend to nothing; the geometry
+    // covers the live rows, and a workgroup with dead rows (or a document
+    // mask) masks every tile element by element
+    it.prefix = 0;
+    it.ql = Sq;
+    it.force_partial = false;
+    if constexpr (FLEX) {
+      it.prefix = fx.prefix;
+      if (fx.q_lengths) it.ql = min(max(fx.q_lengths[it.b], 0), Sq);
+      it.force_partial = fx.doc_q != nullptr || it.ql < it.i1;
+    }
+    const int i1g = FLEX ? max(min(it.i1, it.ql), it.i0) : it.i1;
+    it.geo = KvGeometry{0, 0, 0, 0, 0};
+    if (i1g > it.i0)
+      it.geo = kv_geometry(it.i0, i1g, it.kl, causal, window, input_pos, it.prefix);
+    return it;
+  };
   const int rb = wave >> hp_log2;         // this wave's 32-row block of the positions
-  const int h = g * G + ch * hp + (wave & (hp - 1));   // and its query head
-  const int qt = causal ? (nqt - 1 - qt_rank) : qt_rank;
-
-  const int i0 = qt * TP;
-  const int i1 = min(i0 + TP, Sq);
-  const int kl = k_lengths ? min(max(k_lengths[b], 0), Sk) : Sk;
-  // flex: rows at or past q_lengths[b] attend to nothing; the geometry covers
-  // the live rows, and a workgroup with dead rows (or a document mask) masks
-  // every tile element by element
-  int prefix = 0, ql = Sq;
-  bool force_partial = false;
-  if constexpr (FLEX) {
-    prefix = fx.prefix;
-    if (fx.q_lengths) ql = min(max(fx.q_lengths[b], 0), Sq);
-    force_partial = fx.doc_q != nullptr || ql < i1;
-  }
-  const int i1g = FLEX ? max(min(i1, ql), i0) : i1;
-  KvGeometry geo = {0, 0, 0, 0, 0};
-  if (i1g > i0) geo = kv_geometry(i0, i1g, kl, causal, window, input_pos, prefix);
+  auto head_of = [&](const ItemGeo& it) { return it.g * G + it.ch * hp + (wave & (hp - 1)); };
+  auto load_q = [&](bf16x8_t (&qr)[KSTEPS], const ItemGeo& it) {
+    const int qrow = it.i0 + rb * 32 + lrow;
+    const bool ok = qrow < Sq;
+    const __bf16* qp = Q + ((size_t)(it.b * H + head_of(it)) * Sq + (ok ? qrow : 0)) * D +
+                       half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4_t v = ok ? *(const u32x4_t*)(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
+      qr[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  };
+  bf16x8_t qreg[KSTEPS];
+  int pf_round = -1;  // the round whose Q and first tiles are already loaded
+  int t0 = 0;         // tiles walked so far: ring slot of tile idx is t0 + idx
+  for (int round = 0; round < rounds; ++round) {
+  const int lid = lid_of(round);
+  if (lid < 0) continue;
+  const ItemGeo itg = item_geo(lid);
+  const int b = itg.b, g = itg.g;
+  const int h = head_of(itg);
+  const int i0 = itg.i0, i1 = itg.i1, kl = itg.kl;
+  const int prefix = itg.prefix, ql = itg.ql;
+  const bool force_partial = itg.force_partial;
+  const KvGeometry geo = itg.geo;
 
   const size_t q_base = ((size_t)(b * H + h) * Sq) * D;
   const size_t kv_base = ((size_t)(b * Hkv + g) * Sk) * D;
@@ -339,16 +381,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   RowRange rr = row_range(qi, kl, causal, window, input_pos, prefix);
   if (FLEX && qi >= ql) rr.lo = rr.hi = 0;
 
-  bf16x8_t qreg[KSTEPS];
-  {
-    const bool ok = qi < Sq;
-    const __bf16* qp = Q + q_base + (size_t)(ok ? qi : 0) * D + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4_t v = ok ? *(const u32x4_t*)(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
-      qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
+  const bool prefetched = PP && round == pf_round;
+  if (!prefetched) load_q(qreg, itg);
 
   f32x16_t oacc[DBLK];
 #pragma unroll
@@ -573,23 +607,27 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const u32x4_t ddesc = buffer_desc_s(has_doc ? (const void*)(fx.doc_kv + (size_t)b * Sk + geo.union_lo)
                                               : nullptr,
                                       has_doc ? nvalid * 4 : 0);
-  auto dma_tile = [&](int idx) {
-    const int kt = tile_at(idx);
-    const int rel = (kt * kFwdTileN - geo.union_lo) * D * 2;  // in the valid range
-    const uint32_t kdst = lds_addr_of(smem + (idx % L::kRingK) * L::kBytesK);
-    const uint32_t vdst = lds_addr_of(smem + L::kOffVd + (idx % L::kRingV) * L::kBytesVd);
+  // (kt: the key tile; slot: its place in the rings; ulo: the first key of
+  // the range the descriptors cover)
+  auto dma_issue = [&](const u32x4_t& kd, const u32x4_t& vd, const u32x4_t& dd, bool doc,
+                       int ulo, int kt, int slot) {
+    const int rel = (kt * kFwdTileN - ulo) * D * 2;  // in the valid range
+    const uint32_t kdst = lds_addr_of(smem + (slot % L::kRingK) * L::kBytesK);
+    const uint32_t vdst = lds_addr_of(smem + L::kOffVd + (slot % L::kRingV) * L::kBytesVd);
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
       const int n = wave_u + kFwdWaves * t;
       if (n < L::kInstrK)
-        lds_load16(kdesc, kdst + n * 1024, dma_voff[t] + rel);
+        lds_load16(kd, kdst + n * 1024, dma_voff[t] + rel);
       else if (n < NDMA)
-        lds_load16(vdesc, vdst + (n - L::kInstrK) * 1024, dma_voff[t] + rel);
+        lds_load16(vd, vdst + (n - L::kInstrK) * 1024, dma_voff[t] + rel);
     }
-    if (FLEX && has_doc && wave_u == kFwdWaves - 1 && lane < kFwdTileN / 4)
-      lds_load16(ddesc,
-                 lds_addr_of(smem + L::kOffDocD + (idx % L::kRingV) * L::kBytesDoc),
-                 (kt * kFwdTileN - geo.union_lo + lane * 4) * 4);
+    if (FLEX && doc && wave_u == kFwdWaves - 1 && lane < kFwdTileN / 4)
+      lds_load16(dd, lds_addr_of(smem + L::kOffDocD + (slot % L::kRingV) * L::kBytesDoc),
+                 (kt * kFwdTileN - ulo + lane * 4) * 4);
+  };
+  auto dma_tile = [&](int idx) {
+    dma_issue(kdesc, vdesc, ddesc, has_doc, geo.union_lo, tile_at(idx), t0 + idx);
   };
   // Wait until this wave's loads of the tile after the current one have
   // landed, leaving those of the tile after that in flight (loads complete in
@@ -645,8 +683,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
                                 __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
     };
     if (PP && !FLEX && do_pv && do_s) {
-      const char* vb = smem + L::kOffVd + ((idx - 1) % L::kRingV) * L::kBytesVd;
-      const char* kb = smem + (idx % L::kRingK) * L::kBytesK;
+      const char* vb = smem + L::kOffVd + ((t0 + idx - 1) % L::kRingV) * L::kBytesVd;
+      const char* kb = smem + ((t0 + idx) % L::kRingK) * L::kBytesK;
       constexpr int NPV = DBLK * 4;
       constexpr int NOP = NPV + 2 * KSTEPS;
       auto load_op = [&](int i) -> bf16x8_t {
@@ -743,7 +781,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     }
     if (do_pv) {
       if constexpr (PP) {
-        const char* vb = smem + L::kOffVd + ((idx - 1) % L::kRingV) * L::kBytesVd;
+        const char* vb = smem + L::kOffVd + ((t0 + idx - 1) % L::kRingV) * L::kBytesVd;
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr)
 #pragma unroll
@@ -770,7 +808,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     }
     if (FLEX && do_s && has_bias) bias_loads(idx);
     if (do_s) {
-      const char* kb = smem + (PP ? idx % L::kRingK : idx & 1) * L::kBytesK;
+      const char* kb = smem + (PP ? (t0 + idx) % L::kRingK : idx & 1) * L::kBytesK;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         s[kb2] = f32x16_t{};
@@ -835,7 +873,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   };
   // flex: a key whose document differs from the row's is blocked
   auto doc_mask = [&](int idx) {
-    const char* db = smem + (PP ? L::kOffDocD + (idx % L::kRingV) * L::kBytesDoc
+    const char* db = smem + (PP ? L::kOffDocD + ((t0 + idx) % L::kRingV) * L::kBytesDoc
                                 : L::kOffDoc + (idx & 1) * L::kBytesDoc) + half * 16;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -954,11 +992,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
 
   if (n_tiles > 0) {
     if constexpr (PP) {
-      // prologue: the first two tiles (group B also the third) in LDS
+      // prologue: the first two tiles (group B also the third) in LDS,
+      // unless the previous item already loaded them
       const bool gb = __builtin_amdgcn_readfirstlane(tid >> 8) != 0;
-      dma_tile(0);
-      if (n_tiles > 1) dma_tile(1);
-      if (gb && n_tiles > 2) dma_tile(2);
+      if (!prefetched) {
+        dma_tile(0);
+        if (n_tiles > 1) dma_tile(1);
+        if (gb && n_tiles > 2) dma_tile(2);
+      }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     } else {
@@ -993,7 +1034,35 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
           __syncthreads();
         }
       }
+      // Start the next item: its queries into registers and its first tiles
+      // into the ring slots after this item's.  Past the last barrier no wave
+      // reads those slots again (the last product below reads only the slot
+      // of this item's last V tile), and the next item's prologue barrier
+      // orders them before the slots come round again.
+      int nr = round + 1;
+      while (nr < rounds && lid_of(nr) < 0) ++nr;
+      ItemGeo nx;
+      if (nr < rounds) {
+        nx = item_geo(lid_of(nr));
+        if (nx.geo.any) {
+          const int nfirst = nx.geo.union_lo / kFwdTileN;
+          const int nn = (nx.geo.union_hi - 1) / kFwdTileN - nfirst + 1;
+          const int nval = nx.geo.union_hi - nx.geo.union_lo;
+          const size_t nbase = ((size_t)(nx.b * Hkv + nx.g) * Sk + nx.geo.union_lo) * D;
+          const u32x4_t kd = buffer_desc_s(K + nbase, nval * D * 2);
+          const u32x4_t vd = buffer_desc_s(V + nbase, nval * D * 2);
+          const u32x4_t dd = buffer_desc_s(
+              has_doc ? (const void*)(fx.doc_kv + (size_t)nx.b * Sk + nx.geo.union_lo) : nullptr,
+              has_doc ? nval * 4 : 0);
+          const int cnt = min(group_b ? 3 : 2, nn);
+          for (int t = 0; t < cnt; ++t)
+            dma_issue(kd, vd, dd, has_doc, nx.geo.union_lo, nfirst + t, t0 + n_tiles + t);
+        }
+        pf_round = nr;
+      }
       m_phase(n_tiles, true, false);
+      // (the queries only once the last product has freed their registers)
+      if (nr < rounds) load_q(qreg, nx);
     } else {
       for (int idx = 0; idx < n_tiles; ++idx) {
         m_phase(idx, idx > 0, true);
@@ -1014,6 +1083,39 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     // chunks, each 16 lanes write one whole row.  The wave only reads what it
     // wrote, so no barrier is needed.
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if constexpr (PP) {
+      // The ping-pong kernels stage in an area of their own, half the head
+      // dimension per pass, so neither the staging nor the next item's loads
+      // into the rings wait for the other waves.
+      char* ost = smem + L::kOffOs + wave * L::kBytesOWaveH;
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+        if (hd) __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int dbh = 0; dbh < DBLK / 2; ++dbh)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int db = hd * (DBLK / 2) + dbh;
+            const int d = dbh * 32 + r4 * 8 + half * 4;  // within the half
+            u32x2_t w = {pack_bf16x2(oacc[db][r4 * 4 + 0] * inv,
+                                     oacc[db][r4 * 4 + 1] * inv),
+                         pack_bf16x2(oacc[db][r4 * 4 + 2] * inv,
+                                     oacc[db][r4 * 4 + 3] * inv)};
+            *(u32x2_t*)(ost + lrow * L::kRowOh + d * 2) = w;
+          }
+        __builtin_amdgcn_wave_barrier();
+        constexpr int CHUNKS = D / 16;  // 16-byte chunks per half row
+#pragma unroll
+        for (int i = 0; i < 32 * CHUNKS / 64; ++i) {
+          const int c = i * 64 + lane;
+          const int row = c / CHUNKS, ch = c - row * CHUNKS;
+          const u32x4_t v = *(const u32x4_t*)(ost + row * L::kRowOh + ch * 16);
+          const int qrow = i0 + rb * 32 + row;
+          if (qrow < Sq)
+            *(u32x4_t*)(O + q_base + (size_t)qrow * D + hd * (D / 2) + ch * 8) = v;
+        }
+      }
+    } else {
     // (without groups the staging area is the K/V rings, free once every
     // wave is past its last products)
     __syncthreads();
@@ -1039,6 +1141,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       const int qrow = i0 + rb * 32 + row;
       if (qrow < Sq) *(u32x4_t*)(O + q_base + (size_t)qrow * D + ch * 8) = v;
     }
+    }
   }
   if (LSE && qi < Sq && half == 0) {
     const float lse = l_tot > 0.f
@@ -1046,7 +1149,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
                           : -INFINITY;
     LSE[(size_t)(b * H + h) * Sq + qi] = lse;
   }
-  __syncthreads();  // LDS is reused by the next item
+  if constexpr (PP) {
+    t0 += n_tiles;
+  } else {
+    __syncthreads();  // LDS is reused by the next item
+  }
   }
 }
 
