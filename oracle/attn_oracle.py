@@ -37,7 +37,9 @@ plainly, in float64 NumPy:
   "Primitives", ``∇attention!``);
 * the flex variants: ``SoftCapScore``, ``AliBiScore``, ``BiasScore``,
   ``PrefixMask`` / ``prefix_lm``, ``DocumentMask`` and ``q_lengths``
-  (Tylo.jl "Primitives", ``flex_attention!`` and its mods);
+  (Tylo.jl "Primitives", ``flex_attention!`` and its mods), and the coarse
+  block classes of a mask (Tylo.jl "Primitives", ``BlockMask`` /
+  ``build_block_mask``);
 * block-sparse prefill: centroid / radius-bounded (RBS) and min/max block
   scores, relative and top-k block masks, attention on the kept blocks
   (mlx-arsenal "Radius-bounded block scores (RBS)");
@@ -65,8 +67,11 @@ repository's design notes):
   holds the document ids of the Sq query rows (row i at absolute position
   input_pos + i, so a single id vector doc of a whole sequence gives
   doc_q[i] = doc[input_pos + i] and doc_kv[j] = doc[j]);
-  a prefix ORs keys j < prefix into the causal / window set; rows at or past
-  q_lengths[b] attend to nothing;
+  a prefix ORs keys j < prefix into the causal / window set (with a window
+  a row may then see two key intervals); rows at or past q_lengths[b] attend
+  to nothing;
+* block classes: a block counts only the rows and keys that exist (a ragged
+  last block is classed on its existing pairs);
 * block scores: radius quantiles per KV head with linear interpolation; a
   ragged last block summarises its existing keys; top-k ties go to the lower
   block index;
@@ -506,6 +511,31 @@ def flex_ref(Q, K, V, causal: bool = False, window: int = 0, input_pos: int = 0,
             O[b, h, r] = combine(P, V[b, g])
             LSE[b, h, r] = lse_from_stats(M, L)
     return O, LSE
+
+
+def block_mask_ref(ok, tile_m: int = 64, tile_n: int = 64) -> np.ndarray:
+    """Coarse block classes of a boolean (..., Sq, Sk) pair mask (Tylo.jl
+    "Primitives", ``BlockMask`` / ``build_block_mask``: per query block, the key
+    blocks holding any unmasked element, and which of those are fully unmasked).
+
+    Query block qb covers the rows [qb * tile_m, (qb + 1) * tile_m) that exist
+    (< Sq), key block kb the keys [kb * tile_n, (kb + 1) * tile_n) that exist
+    (< Sk).  The class is 0 when no pair of the block attends, 2 when every
+    pair does and 1 otherwise.  Returns uint8 (..., ceil(Sq / tile_m),
+    ceil(Sk / tile_n)).  ``ok`` is the predicate evaluated at every pair, e.g.
+    ``flex_mask`` (which already shifts the queries by ``input_pos``).
+    """
+    ok = np.asarray(ok, dtype=bool)
+    Sq, Sk = ok.shape[-2:]
+    nqb, nkb = -(-Sq // tile_m), -(-Sk // tile_n)
+    out = np.zeros(ok.shape[:-2] + (nqb, nkb), dtype=np.uint8)
+    for qb in range(nqb):
+        for kb in range(nkb):
+            blk = ok[..., qb * tile_m:(qb + 1) * tile_m, kb * tile_n:(kb + 1) * tile_n]
+            some = blk.any(axis=(-2, -1))
+            every = blk.all(axis=(-2, -1))
+            out[..., qb, kb] = np.where(every, 2, np.where(some, 1, 0))
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -714,6 +714,86 @@ def test_q_lengths_rows_attend_to_nothing():
     np.testing.assert_array_equal(O[1], Or[1])
 
 
+def test_prefix_or_window_rows_hand_worked():
+    # PrefixMask(2) | sliding window of 3 keys (causal): row i sees keys
+    # {0, 1} and {i-2 .. i}; from row 5 on these are two separate intervals
+    ok = ora.flex_mask(10, 10, True, 3, 0, prefix=2)
+    want = [{0, 1}, {0, 1}, {0, 1, 2}, {0, 1, 2, 3}, {0, 1, 2, 3, 4}, {0, 1, 3, 4, 5},
+            {0, 1, 4, 5, 6}, {0, 1, 5, 6, 7}, {0, 1, 6, 7, 8}, {0, 1, 7, 8, 9}]
+    for i, keys in enumerate(want):
+        assert set(np.flatnonzero(ok[i])) == keys, i
+    # with input_pos = -3 the window part of rows 0..2 is empty, the prefix stays
+    ok = ora.flex_mask(6, 6, True, 3, -3, prefix=2)
+    assert [set(np.flatnonzero(r)) for r in ok] == [{0, 1}, {0, 1}, {0, 1}, {0, 1},
+                                                   {0, 1}, {0, 1, 2}]
+
+
+def test_prefix_or_window_attention_is_attention_over_the_two_intervals():
+    _, Q, K, V = _flex_case(58, Sq=12, Sk=12)
+    O, L = ora.flex_ref(Q, K, V, True, 3, prefix=2)
+    keys = [0, 1, 7, 8, 9]  # row 9: the prefix and the window's three keys
+    Og, Lg = ora.attn_ref(Q[:, :, 9:10], K[:, :, keys], V[:, :, keys], False)
+    np.testing.assert_allclose(O[:, :, 9:10], Og, atol=1e-14)
+    np.testing.assert_allclose(L[:, :, 9:10], Lg, atol=1e-14)
+
+
+def _block_mask_pins_pass():
+    try:
+        # two documents of 128 under a causal mask, 64 x 64 blocks
+        doc = np.repeat([0, 1], 128)
+        got = ora.block_mask_ref(ora.flex_mask(256, 256, True, doc_q=doc, doc_kv=doc))
+        assert got.tolist() == [[1, 0, 0, 0], [2, 1, 0, 0], [0, 0, 1, 0], [0, 0, 2, 1]]
+        # ragged last blocks are classed on the pairs that exist
+        got = ora.block_mask_ref(ora.flex_mask(100, 100, True))
+        assert got.tolist() == [[1, 0], [2, 1]]
+        # key lengths and shifted queries
+        got = ora.block_mask_ref(ora.flex_mask(64, 128, False, k_len=100))
+        assert got.tolist() == [[2, 1]]
+        got = ora.block_mask_ref(ora.flex_mask(64, 192, True, input_pos=128))
+        assert got.tolist() == [[2, 2, 1]]
+        # unequal tile sizes, worked by hand: rows {0,1},{2,3}; keys {0,1,2},{3,4}
+        got = ora.block_mask_ref(ora.flex_mask(4, 5, True), tile_m=2, tile_n=3)
+        assert got.shape == (2, 2) and got.tolist() == [[1, 0], [2, 1]]
+        # a batch axis is carried through
+        ok = np.stack([ora.flex_mask(4, 5, True), np.ones((4, 5), bool)])
+        assert ora.block_mask_ref(ok, 2, 3).tolist() == [[[1, 0], [2, 1]], [[2, 2], [2, 2]]]
+    except AssertionError:
+        return False
+    return True
+
+
+def test_block_mask_closed_forms():
+    assert _block_mask_pins_pass()
+
+
+ORIG_BLOCK_MASK = ora.block_mask_ref
+
+
+def _mut_bm_classes_swapped(ok, tile_m=64, tile_n=64):
+    c = ORIG_BLOCK_MASK(ok, tile_m, tile_n)
+    return np.where(c == 1, 2, np.where(c == 2, 1, 0)).astype(np.uint8)
+
+
+def _mut_bm_tiles_swapped(ok, tile_m=64, tile_n=64):
+    return ORIG_BLOCK_MASK(ok, tile_n, tile_m)
+
+
+def _mut_bm_padded(ok, tile_m=64, tile_n=64):
+    ok = np.asarray(ok, bool)
+    Sq, Sk = ok.shape[-2:]
+    pad = np.zeros(ok.shape[:-2] + (-(-Sq // tile_m) * tile_m, -(-Sk // tile_n) * tile_n), bool)
+    pad[..., :Sq, :Sk] = ok
+    return ORIG_BLOCK_MASK(pad, tile_m, tile_n)
+
+
+@pytest.mark.parametrize("mutant", [_mut_bm_classes_swapped, _mut_bm_tiles_swapped,
+                                    _mut_bm_padded])
+def test_planted_block_mask_mistakes(monkeypatch, mutant):
+    assert _block_mask_pins_pass()
+    monkeypatch.setattr(ora, "block_mask_ref", mutant)
+    assert not _block_mask_pins_pass()
+
+
 def _flex_pins_pass():
     checks = [
         lambda: test_flex_bias_alibi_document_prefix_vs_torch_sdpa((2, 4)),
@@ -722,6 +802,8 @@ def _flex_pins_pass():
         test_prefix_lm_decomposes,
         test_document_mask_block_diagonal_equals_separate_sequences,
         test_q_lengths_rows_attend_to_nothing,
+        test_prefix_or_window_rows_hand_worked,
+        test_prefix_or_window_attention_is_attention_over_the_two_intervals,
     ]
     for c in checks:
         try:
@@ -778,7 +860,14 @@ def _mut_doc_shifted(Sq, Sk, causal=False, window=0, input_pos=0, k_len=None, q_
     return ORIG_FLEX_MASK(Sq, Sk, causal, window, input_pos, k_len, q_len, prefix, doc_q, doc_kv)
 
 
+def _mut_prefix_dropped_with_window(Sq, Sk, causal=False, window=0, input_pos=0, k_len=None,
+                                    q_len=None, prefix=0, doc_q=None, doc_kv=None):
+    return ORIG_FLEX_MASK(Sq, Sk, causal, window, input_pos, k_len, q_len,
+                          0 if window > 0 else prefix, doc_q, doc_kv)
+
+
 @pytest.mark.parametrize("target,mutant", [
+    ("flex_mask", _mut_prefix_dropped_with_window),
     ("score_mods", _mut_alibi_sign),
     ("score_mods", _mut_alibi_local_positions),
     ("score_mods", _mut_softcap_first),
