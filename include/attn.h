@@ -126,11 +126,23 @@ int attn_fwd_f32(void* O, const void* Q, const void* K, const void* V,
  *                 doc_q[b][i] == doc_kv[b][j] (DocumentMask(doc_q, doc_kv));
  *                 both or neither
  *   prefix        >= 0: keys j < prefix are visible to every query in addition
- *                 to the causal set (PrefixMask; causal + prefix is
- *                 prefix_lm); > 0 with a window is ATTN_EUNSUPPORTED
+ *                 to the causal / window set (PrefixMask; causal + prefix is
+ *                 prefix_lm; with a window a row sees the prefix and its
+ *                 window, two key intervals: PrefixMask | SlidingWindowMask)
  *   softcap       0: off; > 0: score -> softcap * tanh(score / softcap),
  *                 applied after bias and ALiBi (SoftCapScore)
  *   qk_scale      0: 1/sqrt(D); > 0: the scale applied to q.k (qk_scale)
+ *   block_mask    uint8 (block_mask_B, ceil(Sq / ATTN_BLOCK), ceil(Sk /
+ *                 ATTN_BLOCK)) row-major, block_mask_B in {1, B}: the coarse
+ *                 class of each (query block, key block) under the whole mask
+ *                 (BlockMask): ATTN_BLOCK_EMPTY blocks are skipped,
+ *                 ATTN_BLOCK_FULL blocks take no document mask, other values
+ *                 are masked element by element.  Query block qb is the local
+ *                 rows [qb * ATTN_BLOCK, (qb + 1) * ATTN_BLOCK).  The classes
+ *                 must agree with the mask (an EMPTY block with an attending
+ *                 pair, or a FULL one with a blocked document pair, gives
+ *                 wrong results); attn_build_block_mask writes them.  Needs
+ *                 ceil(Sk / ATTN_BLOCK) <= ATTN_SPARSE_MAX_KEY_BLOCKS.
  * The score is qk_scale * q.k, plus bias, plus ALiBi, then soft-capped; blocked
  * pairs (causal / window / k_lengths / q_lengths / documents, OR the prefix)
  * contribute nothing. */
@@ -144,12 +156,23 @@ typedef struct attn_flex {
   int prefix;
   float softcap;
   float qk_scale;
+  const uint8_t* block_mask;
+  int block_mask_B;
 } attn_flex_t;
+
+/* Classes of a BlockMask entry (Tylo.jl "Primitives", BlockMask: the key
+ * blocks holding any unmasked element, and which of those are fully
+ * unmasked). */
+#define ATTN_BLOCK_EMPTY 0
+#define ATTN_BLOCK_PARTIAL 1
+#define ATTN_BLOCK_FULL 2
 
 /* attn_fwd with the flex mods of *flex (NULL = none), bf16 only.  Same
  * arguments, layouts and errors as attn_fwd, plus ATTN_EINVAL for a bad
  * flex field (softcap or qk_scale < 0, prefix < 0, bias_B / bias_H not 1 or
- * B / H, doc_q without doc_kv or the reverse).  Defined by: Tylo.jl
+ * B / H, doc_q without doc_kv or the reverse, block_mask_B not 1 or B) and
+ * ATTN_EUNSUPPORTED for a block mask past ATTN_SPARSE_MAX_KEY_BLOCKS key
+ * blocks.  Defined by: Tylo.jl
  * "Primitives", flex_attention! (score_mod, mask_mod, qk_scale, q_lengths),
  * SoftCapScore, AliBiScore, BiasScore, PrefixMask, prefix_lm, DocumentMask. */
 int attn_fwd_flex(void* O, const void* Q, const void* K, const void* V,
@@ -157,6 +180,26 @@ int attn_fwd_flex(void* O, const void* Q, const void* K, const void* V,
                   int causal, int window, int input_pos,
                   const int32_t* k_lengths, const attn_flex_t* flex,
                   hipStream_t stream);
+
+/* BlockMask of the flex mask of these arguments, on the device (the
+ * predicate build_block_mask takes, evaluated at every pair): writes
+ * block_mask, uint8 (B, ceil(Sq / ATTN_BLOCK), ceil(Sk / ATTN_BLOCK)), with
+ * ATTN_BLOCK_EMPTY where no pair of the block attends, ATTN_BLOCK_FULL where
+ * every existing pair does (rows < Sq, keys < Sk) and ATTN_BLOCK_PARTIAL
+ * otherwise.  The pair mask is that of attn_fwd_flex: causal / window at
+ * absolute query positions input_pos + i, OR keys j < prefix, AND j <
+ * k_lengths[b], AND i < q_lengths[b], AND doc_q[b][i] == doc_kv[b][j]; the
+ * score fields and block_mask of *flex are ignored.  The output can be
+ * passed as flex->block_mask (block_mask_B = B) with the same arguments.
+ * Errors: ATTN_EINVAL for a NULL block_mask with Sq, Sk > 0 or a bad
+ * argument (as attn_fwd_flex), ATTN_EUNSUPPORTED past
+ * ATTN_SPARSE_MAX_KEY_BLOCKS key blocks.  Defined by: Tylo.jl "Primitives",
+ * BlockMask and build_block_mask (block classes from a keep predicate that
+ * agrees with the device mask_mod; TILE_M = TILE_N = 64). */
+int attn_build_block_mask(uint8_t* block_mask, int B, int Sq, int Sk,
+                          int causal, int window, int input_pos,
+                          const int32_t* k_lengths, const attn_flex_t* flex,
+                          hipStream_t stream);
 
 /* Bytes of scratch attn_bwd needs (two float32 values per query row),
  * host-only; 0 for invalid sizes. */

@@ -40,13 +40,18 @@ class AttnFlex(ctypes.Structure):
     """attn_flex_t of include/attn.h (device pointers, NULL = mod off)."""
     _fields_ = [("q_lengths", _P), ("alibi_slopes", _P), ("bias", _P), ("doc_q", _P),
                 ("doc_kv", _P), ("bias_B", _I), ("bias_H", _I), ("prefix", _I),
-                ("softcap", ctypes.c_float), ("qk_scale", ctypes.c_float)]
+                ("softcap", ctypes.c_float), ("qk_scale", ctypes.c_float),
+                ("block_mask", _P), ("block_mask_B", _I)]
+
+BLOCK_EMPTY, BLOCK_PARTIAL, BLOCK_FULL = 0, 1, 2
 
 _SIGS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "attn_fwd_flex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P,
                            ctypes.POINTER(AttnFlex), _P]),
+    "attn_build_block_mask": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, ctypes.POINTER(AttnFlex),
+                                   _P]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "attn_decode_ws": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
     "attn_decode_static": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
@@ -172,18 +177,25 @@ def attn_fwd_f32(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
 
 def attn_fwd_flex(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
                   k_lengths=None, q_lengths=None, prefix=0, softcap=0.0, alibi_slopes=None,
-                  bias=None, doc_q=None, doc_kv=None, qk_scale=0.0, stream=None) -> None:
+                  bias=None, doc_q=None, doc_kv=None, qk_scale=0.0, block_mask=None,
+                  stream=None) -> None:
     """bf16 prefill with the flex mods (see attn_flex_t in include/attn.h).
 
     ``bias`` float32 (bias_B, bias_H, Sq, Sk) with bias_B in {1, B}, bias_H in
     {1, H}; ``alibi_slopes`` float32 (H,); ``q_lengths`` int32 (B,);
-    ``doc_q`` / ``doc_kv`` int32 (B, Sq) / (B, Sk).
+    ``doc_q`` / ``doc_kv`` int32 (B, Sq) / (B, Sk); ``block_mask`` uint8
+    (1 or B, ceil(Sq/64), ceil(Sk/64)) of BLOCK_* classes (``build_block_mask``).
     """
     B, H, Hkv, Sq, Sk, D = _prefill_shapes(Q, K, V, O, LSE, k_lengths)
     _expect(q_lengths, (B,), "q_lengths")
     _expect(alibi_slopes, (H,), "alibi_slopes")
     _expect(doc_q, (B, Sq), "doc_q")
     _expect(doc_kv, (B, Sk), "doc_kv")
+    if block_mask is not None and (
+            block_mask.dtype != torch.uint8 or block_mask.dim() != 3
+            or tuple(block_mask.shape[1:]) != (-(-Sq // BLOCK), -(-Sk // BLOCK))
+            or block_mask.shape[0] not in (1, B)):
+        raise ValueError("block_mask must be uint8 (1 or B, ceil(Sq/64), ceil(Sk/64))")
     for t in (O, Q, K, V):
         if t.dtype != torch.bfloat16:
             raise ValueError("attn_fwd_flex takes bfloat16 tensors")
@@ -201,11 +213,50 @@ def attn_fwd_flex(O, Q, K, V, LSE=None, causal=False, window=0, input_pos=0,
     f = AttnFlex(_ptr(q_lengths), _ptr(alibi_slopes), _ptr(bias), _ptr(doc_q), _ptr(doc_kv),
                  bias.shape[0] if bias is not None else 0,
                  bias.shape[1] if bias is not None else 0,
-                 int(prefix), float(softcap), float(qk_scale))
+                 int(prefix), float(softcap), float(qk_scale), _ptr(block_mask),
+                 block_mask.shape[0] if block_mask is not None else 0)
     rc = lib().attn_fwd_flex(_ptr(O), _ptr(Q), _ptr(K), _ptr(V), _ptr(LSE), B, H, Hkv, Sq,
                              Sk, D, int(bool(causal)), int(window), int(input_pos),
                              _ptr(k_lengths), ctypes.byref(f), _stream(stream))
     _check(rc, "attn_fwd_flex")
+
+
+def attn_build_block_mask(block_mask, Sq, Sk, causal=False, window=0, input_pos=0,
+                          k_lengths=None, q_lengths=None, prefix=0, doc_q=None, doc_kv=None,
+                          stream=None) -> None:
+    """BlockMask classes (B, ceil(Sq/64), ceil(Sk/64)) uint8 of the flex mask of
+    these arguments into block_mask (see attn_build_block_mask in include/attn.h)."""
+    if block_mask.dtype != torch.uint8 or block_mask.dim() != 3:
+        raise ValueError("block_mask must be uint8 (B, ceil(Sq/64), ceil(Sk/64))")
+    B = block_mask.shape[0]
+    _expect(block_mask, (B, -(-Sq // BLOCK), -(-Sk // BLOCK)), "block_mask")
+    _expect(k_lengths, (B,), "k_lengths")
+    _expect(q_lengths, (B,), "q_lengths")
+    _expect(doc_q, (B, Sq), "doc_q")
+    _expect(doc_kv, (B, Sk), "doc_kv")
+    for t, name in ((k_lengths, "k_lengths"), (q_lengths, "q_lengths"), (doc_q, "doc_q"),
+                    (doc_kv, "doc_kv")):
+        if t is not None and t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    f = AttnFlex(_ptr(q_lengths), None, None, _ptr(doc_q), _ptr(doc_kv), 0, 0, int(prefix),
+                 0.0, 0.0, None, 0)
+    rc = lib().attn_build_block_mask(_ptr(block_mask), B, int(Sq), int(Sk), int(bool(causal)),
+                                     int(window), int(input_pos), _ptr(k_lengths),
+                                     ctypes.byref(f), _stream(stream))
+    _check(rc, "attn_build_block_mask")
+
+
+def build_block_mask(Sq, Sk, B=1, causal=False, window=0, input_pos=0, k_lengths=None,
+                     q_lengths=None, prefix=0, doc_q=None, doc_kv=None, device=None):
+    """Allocating form of attn_build_block_mask: returns the uint8 BlockMask."""
+    if doc_q is not None:
+        B = doc_q.shape[0]
+        device = device or doc_q.device
+    out = torch.empty(B, -(-Sq // BLOCK), -(-Sk // BLOCK), dtype=torch.uint8,
+                      device=device or "cuda")
+    attn_build_block_mask(out, Sq, Sk, causal, window, input_pos, k_lengths, q_lengths,
+                          prefix, doc_q, doc_kv)
+    return out
 
 
 def attn_block_scores_workspace_bytes(B: int, Hkv: int, Sk: int, D: int) -> int:

@@ -32,6 +32,8 @@ template <int D>
 hipError_t launch_fwd_flex(void*, const void*, const void*, const void*,
                            float*, int, int, int, int, int, int, int, int,
                            const int32_t*, const attn_flex_t*, hipStream_t);
+hipError_t launch_build_block_mask(uint8_t*, int, int, int, int, int, int,
+                                   const int32_t*, const attn_flex_t*, hipStream_t);
 template <int D>
 hipError_t launch_fwd_f32(void*, const void*, const void*, const void*,
                           float*, int, int, int, int, int, int, int, int,
@@ -285,7 +287,11 @@ int attn_fwd_flex(void* O, const void* Q, const void* K, const void* V,
         return ATTN_EINVAL;
       if (((long long)Sq * Sk + Sk) * 4 + 256 > INT_MAX) return ATTN_EUNSUPPORTED;
     }
-    if (f->prefix > 0 && window > 0) return ATTN_EUNSUPPORTED;
+    if (f->block_mask) {
+      if (f->block_mask_B != 1 && f->block_mask_B != B) return ATTN_EINVAL;
+      if (((long long)Sk + ATTN_BLOCK - 1) / ATTN_BLOCK > ATTN_SPARSE_MAX_KEY_BLOCKS)
+        return ATTN_EUNSUPPORTED;
+    }
     if (Sq == 0) return ATTN_OK;
     hipError_t e =
         D == 64 ? launch_fwd_flex<64>(O, Q, K, V, LSE, B, H, Hkv, Sq, Sk, causal,
@@ -295,8 +301,33 @@ int attn_fwd_flex(void* O, const void* Q, const void* K, const void* V,
     return hip_status(e);
   }();
   return logged(rc_, "attn_fwd_flex", B, H, Hkv, Sq, Sk, D,
-                "causal=%d window=%d input_pos=%d",
-                causal, window, input_pos);
+                "causal=%d window=%d input_pos=%d block_mask=%s",
+                causal, window, input_pos, flex && flex->block_mask ? "yes" : "no");
+}
+
+int attn_build_block_mask(uint8_t* block_mask, int B, int Sq, int Sk, int causal,
+                          int window, int input_pos, const int32_t* k_lengths,
+                          const attn_flex_t* flex, hipStream_t stream) {
+  const int rc_ = [&]() -> int {
+    if (B < 1 || Sq < 0 || Sk < 0) return ATTN_EINVAL;
+    if (causal != 0 && causal != 1) return ATTN_EINVAL;
+    if (window < 0 || (window > 0 && !causal)) return ATTN_EINVAL;
+    attn_flex_t none = {};
+    const attn_flex_t* f = flex ? flex : &none;
+    if (f->prefix < 0) return ATTN_EINVAL;
+    if ((f->doc_q == nullptr) != (f->doc_kv == nullptr)) return ATTN_EINVAL;
+    if (((long long)Sk + ATTN_BLOCK - 1) / ATTN_BLOCK > ATTN_SPARSE_MAX_KEY_BLOCKS)
+      return ATTN_EUNSUPPORTED;
+    if ((long long)B * ((Sq + ATTN_BLOCK - 1) / ATTN_BLOCK) *
+            ((Sk + ATTN_BLOCK - 1) / ATTN_BLOCK) > INT_MAX)
+      return ATTN_EUNSUPPORTED;
+    if (Sq == 0 || Sk == 0) return ATTN_OK;
+    if (!block_mask) return ATTN_EINVAL;
+    return hip_status(launch_build_block_mask(block_mask, B, Sq, Sk, causal, window,
+                                              input_pos, k_lengths, f, stream));
+  }();
+  return logged(rc_, "attn_build_block_mask", B, 0, 0, Sq, Sk, 0,
+                "causal=%d window=%d input_pos=%d", causal, window, input_pos);
 }
 
 int attn_fwd_f32(void* O, const void* Q, const void* K, const void* V,

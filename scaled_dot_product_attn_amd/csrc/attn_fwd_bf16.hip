@@ -100,6 +100,8 @@ struct FlexArgs {
   const int32_t* doc_q;
   const int32_t* doc_kv;
   long long bias_bstride, bias_hstride;
+  const uint8_t* bmask;   // block classes (ATTN_BLOCK_*), or null
+  long long bm_bstride;   // elements between batches of bmask (0: shared)
   int prefix;
   float softcap;
   float qk_scale;
@@ -157,8 +159,13 @@ struct FwdLds {
 // itself (s_waitcnt vmcnt) before the barrier that precedes their readers.
 // The instruction writes no vector register.
 __device__ inline void lds_load16(u32x4_t rsrc, uint32_t lds_addr, int voffset) {
+  // Five wait states first: the descriptor registers may have just been
+  // written by a vector instruction (v_readlane / v_readfirstlane), which a
+  // memory instruction may read only five wait states later, and the
+  // compiler inserts no such wait for an instruction inside inline assembly
+  // (M0, written just before, needs one).
   asm volatile(
-      "s_nop 0\n\t"  // M0 written just before: one wait state
+      "s_nop 4\n\t"
       "buffer_load_dwordx4 %0, %1, 0 offen lds"
       :
       : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr)
@@ -255,6 +262,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // per listed tile the keep bits of its 64-row blocks
   __shared__ int16_t s_list[SPARSE ? kSparseMaxTiles : 1];
   __shared__ uint8_t s_kbits[SPARSE ? kSparseMaxTiles : 1];
+  // flex with a block mask: the key tiles of the item whose class is not
+  // empty, bit 15 set for FULL
+  __shared__ int16_t s_blist[FLEX ? kSparseMaxTiles : 1];
   __shared__ int s_ntiles;
 
   const int tid = threadIdx.x;
@@ -303,10 +313,16 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     }
     return lid;
   };
+  // An item's keys: the interval geometry `geo` of its live rows and, with a
+  // prefix beside a window, the keys [0, pe) every live row sees as well.
+  // The tiles walked are kt0, kt0 + 1, ... for the first n1, then the rest
+  // after a jump of `gap` tiles (over the keys between the prefix and the
+  // window); K/V are read from the key range [vlo, vhi).
   struct ItemGeo {
-    int b, g, ch, i0, i1, kl, ql, prefix;
+    int b, g, ch, i0, i1, kl, ql, prefix, pe;
     bool force_partial;
     KvGeometry geo;
+    int kt0, n1, gap, nwalk, vlo, vhi;
   };
   auto item_geo = [&](int lid) -> ItemGeo {
     ItemGeo it;
@@ -330,21 +346,60 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     it.i1 = min(it.i0 + TP, Sq);
     it.kl = k_lengths ? min(max(k_lengths[it.b], 0), Sk) : Sk;
     // flex: rows at or past q_lengths[b] attend to nothing; the geometry
-    // covers the live rows, and a workgroup with dead rows (or a document
-    // mask) masks every tile element by element
+    // covers the live rows, and a workgroup with dead rows masks every tile
+    // element by element
     it.prefix = 0;
+    it.pe = 0;
     it.ql = Sq;
     it.force_partial = false;
     if constexpr (FLEX) {
-      it.prefix = fx.prefix;
       if (fx.q_lengths) it.ql = min(max(fx.q_lengths[it.b], 0), Sq);
-      it.force_partial = fx.doc_q != nullptr || it.ql < it.i1;
+      it.force_partial = it.ql < it.i1;
+      // without a window the prefix widens each row's one interval; beside a
+      // window it is a second interval
+      if (window > 0) it.pe = min(fx.prefix, it.kl);
+      else it.prefix = fx.prefix;
     }
     const int i1g = FLEX ? max(min(it.i1, it.ql), it.i0) : it.i1;
     it.geo = KvGeometry{0, 0, 0, 0, 0};
     if (i1g > it.i0)
       it.geo = kv_geometry(it.i0, i1g, it.kl, causal, window, input_pos, it.prefix);
+    else
+      it.pe = 0;
+    it.kt0 = 0;
+    it.gap = 0;
+    it.nwalk = 0;
+    it.vlo = it.vhi = 0;
+    if (it.geo.any) {
+      it.kt0 = it.geo.union_lo / kFwdTileN;
+      it.nwalk = (it.geo.union_hi - 1) / kFwdTileN - it.kt0 + 1;
+      it.vlo = it.geo.union_lo;
+      it.vhi = it.geo.union_hi;
+    }
+    if (it.pe > 0) {
+      const int pt = (it.pe + kFwdTileN - 1) / kFwdTileN;  // tiles of [0, pe)
+      if (!it.geo.any) {
+        it.nwalk = pt;
+        it.vhi = it.pe;
+      } else if (it.kt0 <= pt) {
+        it.nwalk = max(pt, it.kt0 + it.nwalk);
+        it.vhi = max(it.pe, it.vhi);
+      } else {
+        it.gap = it.kt0 - pt;
+        it.nwalk += pt;
+        it.n1 = pt;
+      }
+      if (!it.geo.any || it.kt0 <= pt) it.n1 = it.nwalk;
+      it.kt0 = 0;
+      it.vlo = 0;
+    } else {
+      it.n1 = it.nwalk;
+    }
     return it;
+  };
+  // the t-th tile of an item's walk
+  auto walk_tile = [&](const ItemGeo& it, int t) {
+    return it.kt0 + t + (t >= it.n1 ? it.gap : 0);
   };
   const int rb = wave >> hp_log2;         // this wave's 32-row block of the positions
   auto head_of = [&](const ItemGeo& it) { return it.g * G + it.ch * hp + (wave & (hp - 1)); };
@@ -372,6 +427,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const int prefix = itg.prefix, ql = itg.ql;
   const bool force_partial = itg.force_partial;
   const KvGeometry geo = itg.geo;
+  const int pe = itg.pe;
 
   const size_t q_base = ((size_t)(b * H + h) * Sq) * D;
   const size_t kv_base = ((size_t)(b * Hkv + g) * Sk) * D;
@@ -379,8 +435,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // ---- my query row ----
   const int qi = i0 + rb * 32 + lrow;  // global query row of this lane
   RowRange rr = row_range(qi, kl, causal, window, input_pos, prefix);
-  if (FLEX && qi >= ql) rr.lo = rr.hi = 0;
+  int pe_row = pe;  // the row also sees the keys [0, pe_row)
+  if (FLEX && qi >= ql) rr.lo = rr.hi = pe_row = 0;
 
+  // the queries (and, without a block mask, the first tiles) are loaded
   const bool prefetched = PP && round == pf_round;
   if (!prefetched) load_q(qreg, itg);
 
@@ -390,14 +448,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   float m_run = -INFINITY;  // running max (base-2 scaled domain)
   float l_run = 0.f;        // this lane's half of the running row sum
 
-  int kt_first = 0, kt_last = -1;
-  if (geo.any) {
-    kt_first = geo.union_lo / kFwdTileN;
-    kt_last = (geo.union_hi - 1) / kFwdTileN;
-  }
-  // The tiles walked, in order: every tile of the union, or (block-sparse)
-  // those that some row block of the workgroup keeps, listed by wave 0.
-  int n_tiles = kt_last - kt_first + 1;
+  // The tiles walked, in order: the item's walk, or (block-sparse) those
+  // that some row block of the workgroup keeps, listed by wave 0, or (flex
+  // with a block mask) those whose class is not empty for some row block of
+  // the workgroup, listed by wave 0.
+  int n_tiles = itg.nwalk;
   if constexpr (SPARSE) {
     const int nqb = (Sq + kSparseBlock - 1) / kSparseBlock;
     const int nkb = (Sk + kSparseBlock - 1) / kSparseBlock;
@@ -405,10 +460,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     const uint8_t* krow = keep + ((size_t)(b * H + h) * nqb + qb0) * nkb;
     if (wave == 0) {
       int base = 0;
-      for (int c0 = kt_first; c0 <= kt_last; c0 += 64) {
-        const int kt = c0 + lane;
+      for (int c0 = 0; c0 < n_tiles; c0 += 64) {
+        const int t = c0 + lane;
+        const int kt = itg.kt0 + t;
         unsigned bits = 0;
-        if (kt <= kt_last) {
+        if (t < n_tiles) {
 #pragma unroll
           for (int q = 0; q < TM / kSparseBlock; ++q)
             if (qb0 + q < nqb && krow[(size_t)q * nkb + kt]) bits |= 1u << q;
@@ -426,7 +482,49 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     __syncthreads();
     n_tiles = s_ntiles;
   }
-  auto tile_at = [&](int idx) { return SPARSE ? (int)s_list[idx] : kt_first + idx; };
+  const bool use_bm = FLEX && fx.bmask != nullptr;
+  if (FLEX && use_bm) {
+    // (the first barrier: every wave is past its reads of the last list)
+    __syncthreads();
+    if (wave == 0) {
+      const int nkb = (Sk + kFwdTileN - 1) / kFwdTileN;
+      const int qb0 = i0 / kFwdTileN;
+      const int nq = n_tiles > 0 ? (max(min(i1, ql), i0 + 1) - 1) / kFwdTileN - qb0 + 1 : 0;
+      const uint8_t* brow = fx.bmask + b * fx.bm_bstride + (size_t)qb0 * nkb;
+      int base = 0;
+      for (int c0 = 0; c0 < n_tiles; c0 += 64) {
+        const int t = c0 + lane;
+        const int kt = walk_tile(itg, t);
+        bool some = false, every = true;
+        if (t < n_tiles) {
+          for (int q = 0; q < nq; ++q) {
+            const int c = brow[(size_t)q * nkb + kt];
+            some |= c != ATTN_BLOCK_EMPTY;
+            every &= c == ATTN_BLOCK_FULL;
+          }
+        }
+        const uint64_t m = __builtin_amdgcn_ballot_w64(some);
+        if (some) {
+          const int at = base + __builtin_popcountll(m & ((1ull << lane) - 1));
+          s_blist[at] = (int16_t)(kt | (every ? 0x8000 : 0));
+        }
+        base += __builtin_popcountll(m);
+      }
+      if (lane == 0) s_ntiles = base;
+    }
+    __syncthreads();
+    n_tiles = s_ntiles;
+  }
+  auto tile_at = [&](int idx) -> int {
+    if constexpr (SPARSE) return s_list[idx];
+    if (FLEX && use_bm) return __builtin_amdgcn_readfirstlane((int)s_blist[idx]) & 0x7fff;
+    return walk_tile(itg, idx);
+  };
+  // flex with a block mask: every pair of the idx-th walked tile is in the
+  // same document
+  auto bm_full = [&](int idx) {
+    return FLEX && use_bm && __builtin_amdgcn_readfirstlane((int)s_blist[idx]) < 0;
+  };
   // block-sparse: does this wave's 64-row block keep the idx-th walked tile?
   // (uniform per wave; a wave skips the products and softmax of a tile it
   // drops, and still takes part in the staging and the barriers)
@@ -440,8 +538,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // range check returns zeros for any other key, so keys that no row may see
   // (past k_lengths, past the causal frontier, before the window) are never
   // read and the loads need no branches.  Group A stages K, group B stages V.
-  const int nvalid = geo.union_hi - geo.union_lo;
-  const size_t valid_base = kv_base + (size_t)geo.union_lo * D;
+  const int nvalid = itg.vhi - itg.vlo;
+  const size_t valid_base = kv_base + (size_t)itg.vlo * D;
   // one resource per tensor, both uniform: selecting between them per group
   // would make the resource divergent
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -505,7 +603,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   }
   // document ids of the workgroup's key union; the (batch, head) bias plane
   const __amdgpu_buffer_rsrc_t doc_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      has_doc ? (void*)(fx.doc_kv + (size_t)b * Sk + geo.union_lo) : nullptr,
+      has_doc ? (void*)(fx.doc_kv + (size_t)b * Sk + itg.vlo) : nullptr,
       (short)0, has_doc ? nvalid * 4 : 0, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t bias_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       has_bias ? (void*)(fx.bias + b * fx.bias_bstride + h * fx.bias_hstride)
@@ -521,7 +619,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const bool v_stager = VTHREADS == GT || gtid < VTHREADS;
 
   auto fetch = [&](int kt) {
-    const int rel0 = kt * kFwdTileN - geo.union_lo;  // tile start, in valid keys
+    const int rel0 = kt * kFwdTileN - itg.vlo;  // tile start, in valid keys
     auto fetch_v = [&](u32x4_t (&dst)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -604,7 +702,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const u32x4_t kdesc = buffer_desc_s(K + valid_base, nvalid * D * 2);
   const u32x4_t vdesc = buffer_desc_s(V + valid_base, nvalid * D * 2);
-  const u32x4_t ddesc = buffer_desc_s(has_doc ? (const void*)(fx.doc_kv + (size_t)b * Sk + geo.union_lo)
+  const u32x4_t ddesc = buffer_desc_s(has_doc ? (const void*)(fx.doc_kv + (size_t)b * Sk + itg.vlo)
                                               : nullptr,
                                       has_doc ? nvalid * 4 : 0);
   // (kt: the key tile; slot: its place in the rings; ulo: the first key of
@@ -627,7 +725,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
                  (kt * kFwdTileN - ulo + lane * 4) * 4);
   };
   auto dma_tile = [&](int idx) {
-    dma_issue(kdesc, vdesc, ddesc, has_doc, geo.union_lo, tile_at(idx), t0 + idx);
+    dma_issue(kdesc, vdesc, ddesc, has_doc, itg.vlo, tile_at(idx), t0 + idx);
   };
   // Wait until this wave's loads of the tile after the current one have
   // landed, leaving those of the tile after that in flight (loads complete in
@@ -900,7 +998,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     const int j0 = kt * kFwdTileN;
     if constexpr (FLEX) {
       if (transform) flex_scores(j0);
-      if (has_doc) doc_mask(idx);
+      if (has_doc && !bm_full(idx)) doc_mask(idx);
     }
     if constexpr (SPARSE) {
       // this wave's 64-row block drops the tile: no score, only the staging
@@ -910,19 +1008,35 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         return;
       }
     }
-    if (tile_class(geo, j0, kFwdTileN) == kTilePartial || (FLEX && force_partial)) {
+    int cls = tile_class(geo, j0, kFwdTileN);
+    // beside a window, a tile inside the prefix is seen whole by every row
+    if (FLEX && pe > 0)
+      cls = j0 + kFwdTileN <= pe || cls == kTileFull ? kTileFull : kTilePartial;
+    if (cls == kTilePartial || (FLEX && force_partial)) {
       // key j0 + half*4 + c is allowed iff c lies in [t_lo, t_lo + width);
       // c is a compile-time constant per register, so one subtract, one
       // unsigned compare and one select per score
       const int t_lo = rr.lo - (j0 + half * 4);
       const unsigned width = (unsigned)max(rr.hi - rr.lo, 0);
+      if (FLEX && pe > 0) {
+        // ... or c < t_pe (the prefix)
+        const int t_pe = pe_row - (j0 + half * 4);
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = kb2 * 32 + (r >> 2) * 8 + (r & 3);
-          if ((unsigned)(c - t_lo) >= width) s[kb2][r] = -INFINITY;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int c = kb2 * 32 + (r >> 2) * 8 + (r & 3);
+            if ((unsigned)(c - t_lo) >= width && c >= t_pe) s[kb2][r] = -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = kb2 * 32 + (r >> 2) * 8 + (r & 3);
+            if ((unsigned)(c - t_lo) >= width) s[kb2][r] = -INFINITY;
+          }
+      }
     }
     // row max as a tree of three-input maxima (v_max3_f32)
     float m16[11];
@@ -995,7 +1109,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       // prologue: the first two tiles (group B also the third) in LDS,
       // unless the previous item already loaded them
       const bool gb = __builtin_amdgcn_readfirstlane(tid >> 8) != 0;
-      if (!prefetched) {
+      if (!prefetched || use_bm) {
         dma_tile(0);
         if (n_tiles > 1) dma_tile(1);
         if (gb && n_tiles > 2) dma_tile(2);
@@ -1044,19 +1158,19 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       ItemGeo nx;
       if (nr < rounds) {
         nx = item_geo(lid_of(nr));
-        if (nx.geo.any) {
-          const int nfirst = nx.geo.union_lo / kFwdTileN;
-          const int nn = (nx.geo.union_hi - 1) / kFwdTileN - nfirst + 1;
-          const int nval = nx.geo.union_hi - nx.geo.union_lo;
-          const size_t nbase = ((size_t)(nx.b * Hkv + nx.g) * Sk + nx.geo.union_lo) * D;
+        // (with a block mask the next item's tiles are known only once its
+        // list is built)
+        if (nx.nwalk > 0 && !use_bm) {
+          const int nval = nx.vhi - nx.vlo;
+          const size_t nbase = ((size_t)(nx.b * Hkv + nx.g) * Sk + nx.vlo) * D;
           const u32x4_t kd = buffer_desc_s(K + nbase, nval * D * 2);
           const u32x4_t vd = buffer_desc_s(V + nbase, nval * D * 2);
           const u32x4_t dd = buffer_desc_s(
-              has_doc ? (const void*)(fx.doc_kv + (size_t)nx.b * Sk + nx.geo.union_lo) : nullptr,
+              has_doc ? (const void*)(fx.doc_kv + (size_t)nx.b * Sk + nx.vlo) : nullptr,
               has_doc ? nval * 4 : 0);
-          const int cnt = min(group_b ? 3 : 2, nn);
+          const int cnt = min(group_b ? 3 : 2, nx.nwalk);
           for (int t = 0; t < cnt; ++t)
-            dma_issue(kd, vd, dd, has_doc, nx.geo.union_lo, nfirst + t, t0 + n_tiles + t);
+            dma_issue(kd, vd, dd, has_doc, nx.vlo, walk_tile(nx, t), t0 + n_tiles + t);
         }
         pf_round = nr;
       }
@@ -1215,6 +1329,11 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
   fx.bias_hstride = f->bias && f->bias_H > 1 ? plane : 0;
   fx.bias_bstride = f->bias && f->bias_B > 1 ? plane * f->bias_H : 0;
   fx.prefix = f->prefix;
+  fx.bmask = f->block_mask;
+  fx.bm_bstride = f->block_mask && f->block_mask_B > 1
+                      ? (long long)((Sq + kFwdTileN - 1) / kFwdTileN) *
+                            ((Sk + kFwdTileN - 1) / kFwdTileN)
+                      : 0;
   fx.softcap = f->softcap;
   fx.qk_scale = f->qk_scale > 0.f ? f->qk_scale : 1.f / sqrtf((float)D);
   log_fwd_grid(fx.bias ? "attn_fwd_bf16_kernel[flex+bias]" : "attn_fwd_bf16_kernel[flex]", D,
@@ -1232,6 +1351,63 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
                        B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
                        0.f, fx, (const uint8_t*)nullptr, n_wg, hl);
+  return hipGetLastError();
+}
+
+// ---- BlockMask of a flex mask (Tylo.jl "Primitives", BlockMask /
+// build_block_mask) ----
+// One wave per (batch, query block, key block): lane l holds key kb * 64 + l
+// and the wave walks the block's rows, testing every pair with the flex
+// mask's own predicate (causal / window at absolute positions, OR the
+// prefix, AND the key and query lengths, AND equal document ids).
+__global__ __launch_bounds__(256) void attn_build_block_mask_kernel(
+    uint8_t* __restrict__ out, int B, int Sq, int Sk, int causal, int window,
+    int input_pos, const int32_t* __restrict__ k_lengths,
+    const int32_t* __restrict__ q_lengths, const int32_t* __restrict__ doc_q,
+    const int32_t* __restrict__ doc_kv, int prefix) {
+  const int nqb = (Sq + kFwdTileN - 1) / kFwdTileN;
+  const int nkb = (Sk + kFwdTileN - 1) / kFwdTileN;
+  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long long)B * nqb * nkb) return;
+  const int lane = threadIdx.x & 63;
+  const int kb = (int)(w % nkb);
+  const int qb = (int)((w / nkb) % nqb);
+  const int b = (int)(w / ((long long)nkb * nqb));
+  const int kl = k_lengths ? min(max(k_lengths[b], 0), Sk) : Sk;
+  const int ql = q_lengths ? min(max(q_lengths[b], 0), Sq) : Sq;
+  const int j = kb * kFwdTileN + lane;
+  const bool key_exists = j < Sk;
+  const uint64_t exists = __builtin_amdgcn_ballot_w64(key_exists);
+  const int dkv = doc_kv && key_exists ? doc_kv[(size_t)b * Sk + j] : 0;
+  const int r_end = min(kFwdTileN, Sq - qb * kFwdTileN);
+  bool some = false, every = true;
+  for (int r = 0; r < r_end; ++r) {
+    const int i = qb * kFwdTileN + r;
+    const long long p = (long long)input_pos + i;
+    bool ok = (!causal || j <= p) && (window <= 0 || j >= p - window + 1);
+    ok = (ok || j < prefix) && j < kl && i < ql;
+    if (doc_q) ok = ok && doc_q[(size_t)b * Sq + i] == dkv;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(ok && key_exists);
+    some |= m != 0;
+    every &= m == exists;
+    if (some && !every) break;
+  }
+  if (lane == 0)
+    out[w] = some ? (every ? ATTN_BLOCK_FULL : ATTN_BLOCK_PARTIAL) : ATTN_BLOCK_EMPTY;
+}
+
+hipError_t launch_build_block_mask(uint8_t* out, int B, int Sq, int Sk, int causal,
+                                   int window, int input_pos, const int32_t* k_lengths,
+                                   const attn_flex_t* f, hipStream_t stream) {
+  const long long n = (long long)B * ((Sq + kFwdTileN - 1) / kFwdTileN) *
+                      ((Sk + kFwdTileN - 1) / kFwdTileN);
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n + 3) / 4);
+  if (log_enabled())
+    log_line("  attn_build_block_mask_kernel grid=%u threads=256 blocks=%lld", grid, n);
+  hipLaunchKernelGGL(attn_build_block_mask_kernel, dim3(grid), dim3(256), 0, stream, out, B,
+                     Sq, Sk, causal, window, input_pos, k_lengths, f->q_lengths, f->doc_q,
+                     f->doc_kv, f->prefix);
   return hipGetLastError();
 }
 

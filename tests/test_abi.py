@@ -40,7 +40,7 @@ def test_header_declares_expected_entry_points():
               "attn_decode_workspace_bytes", "attn_decode_paged", "attn_fwd_flex",
               "attn_bwd", "attn_bwd_workspace_bytes", "attn_block_scores",
               "attn_block_scores_workspace_bytes", "attn_block_mask", "attn_fwd_block_sparse",
-              "attn_decode_static", "attn_mask_dump",
+              "attn_decode_static", "attn_mask_dump", "attn_build_block_mask",
               "attn_tile_plan",
               "attn_status_string", "attn_version"):
         assert n in names
@@ -97,7 +97,13 @@ def test_fwd_flex_argument_errors(lib):
     assert flex(attn.AttnFlex(softcap=-1.0)) == attn.ATTN_EINVAL
     assert flex(attn.AttnFlex(qk_scale=-0.5)) == attn.ATTN_EINVAL
     assert flex(attn.AttnFlex(prefix=-1)) == attn.ATTN_EINVAL
-    assert flex(attn.AttnFlex(prefix=4), window=2) == attn.ATTN_EUNSUPPORTED
+    # a prefix beside a window is accepted (a row then sees two key intervals):
+    # with Sq = 0 the call returns before touching the device
+    assert flex(attn.AttnFlex(prefix=4), window=2, Sq=0) == attn.ATTN_OK
+    assert flex(attn.AttnFlex(block_mask=8, block_mask_B=3), B=2) == attn.ATTN_EINVAL
+    assert flex(attn.AttnFlex(block_mask=8, block_mask_B=0)) == attn.ATTN_EINVAL
+    assert flex(attn.AttnFlex(block_mask=8, block_mask_B=1), Sk=64 * 2048 + 1) == \
+        attn.ATTN_EUNSUPPORTED
     assert flex(attn.AttnFlex(bias=8, bias_B=3, bias_H=1), B=2) == attn.ATTN_EINVAL
     assert flex(attn.AttnFlex(bias=8, bias_B=1, bias_H=2)) == attn.ATTN_EINVAL
     assert flex(attn.AttnFlex(bias=8, bias_B=1, bias_H=1), Sq=40000, Sk=40000) == \
@@ -105,6 +111,24 @@ def test_fwd_flex_argument_errors(lib):
     assert flex(attn.AttnFlex(doc_q=8)) == attn.ATTN_EINVAL
     assert flex(attn.AttnFlex(doc_kv=8)) == attn.ATTN_EINVAL
     assert flex(Sq=0) == attn.ATTN_OK
+
+
+def test_build_block_mask_argument_errors(lib):
+    def bm(out=8, B=1, Sq=8, Sk=8, causal=1, window=0, f=None):
+        return lib.attn_build_block_mask(out, B, Sq, Sk, causal, window, 0, None,
+                                         None if f is None else ctypes.byref(f), None)
+    assert bm(B=0) == attn.ATTN_EINVAL
+    assert bm(Sq=-1) == attn.ATTN_EINVAL
+    assert bm(causal=2) == attn.ATTN_EINVAL
+    assert bm(causal=0, window=3) == attn.ATTN_EINVAL
+    assert bm(window=-1) == attn.ATTN_EINVAL
+    assert bm(f=attn.AttnFlex(prefix=-1)) == attn.ATTN_EINVAL
+    assert bm(f=attn.AttnFlex(doc_q=8)) == attn.ATTN_EINVAL
+    assert bm(Sk=64 * 2048 + 1) == attn.ATTN_EUNSUPPORTED
+    assert bm(out=None) == attn.ATTN_EINVAL
+    # nothing to do: returns before touching the device
+    assert bm(out=None, Sq=0) == attn.ATTN_OK
+    assert bm(out=None, Sk=0) == attn.ATTN_OK
 
 
 def test_bwd_argument_errors(lib):

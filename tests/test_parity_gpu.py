@@ -597,6 +597,15 @@ FLEX_CASES = {
     "prefix_long": dict(shape=(1, 4, 1, 520, 520, 128), mods=dict(prefix=400)),
     "q_lengths": dict(shape=(2, 4, 2, 600, 600, 128), mods=dict(q_lengths=[517, 37])),
     "qk_scale": dict(shape=(1, 4, 2, 200, 200, 128), mods=dict(qk_scale=0.05)),
+    # PrefixMask | sliding window: rows past the prefix see two key intervals
+    "prefix_window_gap": dict(shape=(2, 8, 2, 600, 600, 128), window=128,
+                              mods=dict(prefix=100)),
+    "prefix_window_merged": dict(shape=(1, 4, 1, 300, 300, 64), window=200,
+                                 mods=dict(prefix=150)),
+    "prefix_window_g8": dict(shape=(1, 16, 2, 333, 333, 128), window=64,
+                             mods=dict(prefix=70, q_lengths=[300])),
+    "prefix_window_offset": dict(shape=(2, 4, 2, 200, 500, 128), window=96, input_pos=300,
+                                 k_lengths=[500, 420], mods=dict(prefix=70, docs=3)),
     "everything": dict(shape=(2, 8, 2, 300, 330, 128), input_pos=30, k_lengths=[330, 250],
                        qscale=2.0,
                        mods=dict(softcap=15.0, alibi=True, bias=(2, 1), docs=4, prefix=40,
@@ -630,11 +639,108 @@ def test_flex_parity(name):
     _say(f"flex {name} {case['shape']}")
     w = _flex_inputs(*case["shape"], seed=60, qscale=case.get("qscale", 1.0))
     mods = _build_mods(case, w, 61)
-    kw = dict(causal=case.get("causal", True), input_pos=case.get("input_pos", 0),
-              k_lengths=case.get("k_lengths"))
+    kw = dict(causal=case.get("causal", True), window=case.get("window", 0),
+              input_pos=case.get("input_pos", 0), k_lengths=case.get("k_lengths"))
     O, L = _run_flex(w, **kw, **mods)
     assert torch.isfinite(O.float()).all()
     _check_flex(w, O, L, **kw, **mods)
+
+
+# BlockMask cases: (B, H, Hkv, Sq, Sk, D, causal, window, input_pos, k_lengths,
+# q_lengths, prefix, documents per sequence, one mask for every batch)
+BLOCK_MASK_CASES = {
+    "docs_g4": (2, 8, 2, 700, 700, 128, True, 0, 0, None, None, 0, 9, False),
+    "docs_g8": (1, 16, 2, 520, 520, 128, True, 0, 0, None, None, 0, 6, False),
+    "docs_g1_lengths_d64": (2, 4, 4, 600, 600, 64, True, 0, 0, [600, 455], [590, 600], 0, 5,
+                            False),
+    "docs_noncausal_g2": (1, 4, 2, 300, 300, 128, False, 0, 0, None, None, 0, 4, False),
+    "docs_window_prefix": (1, 8, 2, 640, 640, 128, True, 160, 0, None, None, 64, 4, False),
+    "docs_offset": (2, 8, 2, 256, 512, 128, True, 0, 256, [512, 400], None, 0, 5, False),
+    "docs_shared": (2, 8, 2, 400, 400, 128, True, 0, 0, None, None, 0, 7, True),
+}
+
+
+def _block_mask_case(name):
+    (B, H, Hkv, Sq, Sk, D, causal, window, ip, kl, ql, prefix, nd, shared) = \
+        BLOCK_MASK_CASES[name]
+    w = _flex_inputs(B, H, Hkv, Sq, Sk, D, seed=64)
+    docs = _docs(1 if shared else B, ip + Sq if ip + Sq > Sk else Sk, nd, 65)
+    if shared:
+        docs = docs.expand(B, -1).contiguous()
+    # one id vector per sequence: queries take the ids at their absolute positions
+    mods = dict(doc_q=docs[:, ip:ip + Sq].contiguous(), doc_kv=docs[:, :Sk].contiguous())
+    if prefix:
+        mods["prefix"] = prefix
+    if ql is not None:
+        mods["q_lengths"] = torch.tensor(ql, dtype=torch.int32)
+    kw = dict(causal=causal, window=window, input_pos=ip, k_lengths=kl)
+    return w, mods, kw, shared
+
+
+def _oracle_block_mask(B, Sq, Sk, mods, kw):
+    out = []
+    for b in range(B):
+        ok = ora.flex_mask(Sq, Sk, kw["causal"], kw["window"], kw["input_pos"],
+                           None if kw["k_lengths"] is None else kw["k_lengths"][b],
+                           None if "q_lengths" not in mods else int(mods["q_lengths"][b]),
+                           mods.get("prefix", 0), mods["doc_q"][b].numpy(),
+                           mods["doc_kv"][b].numpy())
+        out.append(ora.block_mask_ref(ok))
+    return np.stack(out)
+
+
+def _gpu_block_mask(B, Sq, Sk, mods, kw):
+    kl = None if kw["k_lengths"] is None else torch.tensor(kw["k_lengths"], dtype=torch.int32,
+                                                          device=DEV)
+    ql = mods["q_lengths"].to(DEV) if "q_lengths" in mods else None
+    bm = torch.full((B, -(-Sq // 64), -(-Sk // 64)), 255, dtype=torch.uint8, device=DEV)
+    attn.attn_build_block_mask(bm, Sq, Sk, kw["causal"], kw["window"], kw["input_pos"], kl, ql,
+                               mods.get("prefix", 0), mods["doc_q"].to(DEV),
+                               mods["doc_kv"].to(DEV))
+    torch.cuda.synchronize()
+    return bm
+
+
+@pytest.mark.parametrize("name", list(BLOCK_MASK_CASES))
+def test_build_block_mask_bitexact(name):
+    _say(f"build_block_mask {name}")
+    w, mods, kw, _ = _block_mask_case(name)
+    shape = (w.q.shape[0], w.q.shape[2], w.k.shape[2])
+    bm = _gpu_block_mask(*shape, mods, kw)
+    ref = _oracle_block_mask(*shape, mods, kw)
+    np.testing.assert_array_equal(bm.cpu().numpy(), ref)
+    assert (ref == 0).any() and (ref == 2).any()
+
+
+@pytest.mark.parametrize("name", list(BLOCK_MASK_CASES))
+def test_flex_block_mask_parity(name):
+    _say(f"flex block_mask {name}")
+    w, mods, kw, shared = _block_mask_case(name)
+    bm = _gpu_block_mask(w.q.shape[0], w.q.shape[2], w.k.shape[2], mods, kw)
+    if shared:
+        assert torch.equal(bm[0], bm[1])
+        bm = bm[:1].contiguous()
+    O, L = _run_flex(w, **kw, **mods, block_mask=bm)
+    assert torch.isfinite(O.float()).all()
+    _check_flex(w, O, L, **kw, **mods)
+    # the skipped tiles are those every row of the tile masks away: the
+    # result is the one without the block mask, bit for bit
+    O0, L0 = _run_flex(w, **kw, **mods)
+    assert torch.equal(O, O0) and torch.equal(L, L0)
+    # a coarser mask (FULL taken as PARTIAL) gives the same result
+    O1, L1 = _run_flex(w, **kw, **mods, block_mask=torch.clamp(bm, max=1))
+    assert torch.equal(O, O1) and torch.equal(L, L1)
+
+
+def test_build_block_mask_full_size():
+    # the causal GQA shape cut into documents: every block of both sequences
+    _say("build_block_mask gqa_causal-size, 16 documents")
+    B, S = 2, 4096
+    docs = _docs(B, S, 16, 66)
+    mods = dict(doc_q=docs, doc_kv=docs)
+    kw = dict(causal=True, window=0, input_pos=0, k_lengths=None)
+    bm = _gpu_block_mask(B, S, S, mods, kw)
+    np.testing.assert_array_equal(bm.cpu().numpy(), _oracle_block_mask(B, S, S, mods, kw))
 
 
 def test_flex_without_mods_matches_plain():
