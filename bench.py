@@ -172,7 +172,7 @@ def _cores():
         return len(os.sched_getaffinity(0))
 
 
-def cpu_rows(pre, dec, dO, slopes, img, keep, seconds: float, paged=None):
+def cpu_rows(pre, dec, dO, slopes, img, keep, seconds: float, paged=None, doc=None):
     """The fp64 oracle beside each row after the hot path, each on a bounded
     sample of the same inputs the GPU ran (whole (batch, head) pairs, whole
     sequences), as a rate in the row's own unit."""
@@ -239,6 +239,13 @@ def cpu_rows(pre, dec, dO, slopes, img, keep, seconds: float, paged=None):
     out["flex_softcap_alibi"] = {
         "value": round(4 * D * pairs / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
         "kind": "oracle", "sample": f"1 of {B * H} (batch, head) pairs, flex_ref, {dt:.1f} s"}
+    if doc is not None:
+        d0 = doc[:1].cpu().numpy()
+        dt = timed(lambda: ora.flex_ref(q, k, v, True, doc_q=d0, doc_kv=d0, heads=[(0, 0)]))
+        out["flex_documents"] = {
+            "value": round(document_flops(doc[:1], 1, D) / dt / 1e12, 5), "unit": "TFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"1 of {B * H} (batch, head) pairs, flex_ref with documents, {dt:.1f} s"}
     g = f64(dO[:1])
     dt = timed(lambda: ora.attn_bwd_ref(q, k, v, g, True, heads=[(0, 0)]))
     out["backward"] = {
@@ -259,6 +266,18 @@ def cpu_rows(pre, dec, dO, slopes, img, keep, seconds: float, paged=None):
         "extrapolated)", "cores": cores, "kind": "oracle",
         "sample": f"1 of {img.q.shape[1]} heads, rbs_block_scores_ref, {dt:.1f} s"}
     return out
+
+
+def document_flops(doc, H: int, D: int) -> int:
+    """4 D flops per allowed pair of causal attention inside each document of
+    the (B, S) id rows (ids constant on contiguous runs), over H heads."""
+    total = 0
+    for row in doc.cpu().tolist():
+        run = 0
+        for i, d in enumerate(row):
+            run = run + 1 if i > 0 and d == row[i - 1] else 1
+            total += run  # row i sees the `run` keys of its document up to itself
+    return 4 * D * H * total
 
 
 def timing_stats(times_ms):
@@ -393,9 +412,25 @@ def main():
         attn.attn_fwd_flex(Of, pre.q, pre.k, pre.v, Lf, True, softcap=30.0,
                            alibi_slopes=flex_slopes)
 
+    # documents: the gqa_causal tensors packed as 16 documents per sequence,
+    # causal inside each document (DocumentMask); the BlockMask is built once,
+    # as a caller would per batch layout, and timed on its own
+    if not args.no_extra:
+        doc = wl.documents_of(pre)
+        doc_bm = attn.build_block_mask(Sq, pre.k.shape[2], B, causal=True, doc_q=doc,
+                                       doc_kv=doc, device=dev)
+
+    def run_doc_build():
+        attn.attn_build_block_mask(doc_bm, Sq, pre.k.shape[2], True, doc_q=doc, doc_kv=doc)
+
+    def run_doc(block_mask):
+        attn.attn_fwd_flex(Of, pre.q, pre.k, pre.v, Lf, True, doc_q=doc, doc_kv=doc,
+                           block_mask=block_mask)
+
     names = ["prefill", "decode"] + list(extra) + (["decode_paged"] if paged is not None else [])
     if not args.no_extra:
-        names += ["flex_softcap_alibi", "backward", "block_estimate", "block_sparse"]
+        names += ["flex_softcap_alibi", "backward", "block_estimate", "block_sparse",
+                  "flex_documents", "flex_documents_dense", "block_mask_build"]
     ev = {n: [] for n in names}
 
     def step(record):
@@ -418,6 +453,12 @@ def main():
                 run_block_estimate()
             elif n == "block_sparse":
                 run_block_sparse()
+            elif n == "flex_documents":
+                run_doc(doc_bm)
+            elif n == "flex_documents_dense":
+                run_doc(None)
+            elif n == "block_mask_build":
+                run_doc_build()
             else:
                 run_prefill(extra[n], *ext_out[n])
             if record:
@@ -512,6 +553,24 @@ def main():
             "config": "image_clustered, RBS-base block scores, top-10% key blocks per row "
                       "block (attn_block_scores + attn_block_mask, then attn_fwd_block_sparse); "
                       "flops = 4 D per pair of the kept blocks"}
+    if "flex_documents" in ms:
+        dfl = document_flops(doc, H, D)
+        tf = dfl / (ms["flex_documents"] * 1e-3) / 1e12
+        tfd = dfl / (ms["flex_documents_dense"] * 1e-3) / 1e12
+        bmc = doc_bm.cpu()
+        out["flex_documents"] = {
+            "ms": round(ms["flex_documents"], 4), "TFLOP/s": round(tf, 2),
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": dfl,
+            "dense_ms": round(ms["flex_documents_dense"], 4),
+            "dense_TFLOP/s": round(tfd, 2),
+            "speedup_vs_dense": round(ms["flex_documents_dense"] / ms["flex_documents"], 3),
+            "block_mask_build_ms": round(ms["block_mask_build"], 4),
+            "blocks_empty_partial_full": [int((bmc == c).sum()) for c in (0, 1, 2)],
+            "config": "gqa_documents: the gqa_causal tensors, 16 documents per 4096-token "
+                      "sequence, causal within each (attn_fwd_flex with doc_q/doc_kv and the "
+                      "BlockMask of attn_build_block_mask; dense = the same call without it, "
+                      "masking every tile of the causal union element by element); "
+                      "flops = 4 D per allowed pair"}
     if paged is not None:
         pb = decode_bytes(paged)
         gbs = pb / (ms["decode_paged"] * 1e-3) / 1e9
@@ -527,7 +586,7 @@ def main():
         if extra:
             log("fp64 oracle beside the other rows")
             rows = cpu_rows(pre, dec, dO, flex_slopes, img, bs_keep, args.cpu_seconds / 5,
-                            paged)
+                            paged, doc)
             for n, r in rows.items():
                 if n in out:
                     out[n]["cpu_oracle"] = r

@@ -229,7 +229,10 @@ __device__ inline int vt_group_pos(int quad_in_group) {
 template <bool SPARSE>
 constexpr int fwd_threads() { return SPARSE ? 256 : kFwdThreads; }
 
-template <int D, bool FLEX, bool BIAS, bool SPARSE>
+// XM (flex only): the mask extensions — a BlockMask, or a prefix beside a
+// window (two key intervals per row) — in an instantiation of their own, so
+// the other flex launches carry none of their registers.
+template <int D, bool FLEX, bool BIAS, bool SPARSE, bool XM = false>
 __global__ __launch_bounds__(fwd_threads<SPARSE>())
 __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     __bf16* __restrict__ O, const __bf16* __restrict__ Q,
@@ -264,7 +267,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   __shared__ uint8_t s_kbits[SPARSE ? kSparseMaxTiles : 1];
   // flex with a block mask: the key tiles of the item whose class is not
   // empty, bit 15 set for FULL
-  __shared__ int16_t s_blist[FLEX ? kSparseMaxTiles : 1];
+  __shared__ int16_t s_blist[XM ? kSparseMaxTiles : 1];
   __shared__ int s_ntiles;
 
   const int tid = threadIdx.x;
@@ -357,7 +360,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       it.force_partial = it.ql < it.i1;
       // without a window the prefix widens each row's one interval; beside a
       // window it is a second interval
-      if (window > 0) it.pe = min(fx.prefix, it.kl);
+      if (XM && window > 0) it.pe = min(fx.prefix, it.kl);
       else it.prefix = fx.prefix;
     }
     const int i1g = FLEX ? max(min(it.i1, it.ql), it.i0) : it.i1;
@@ -399,6 +402,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   };
   // the t-th tile of an item's walk
   auto walk_tile = [&](const ItemGeo& it, int t) {
+    if constexpr (!XM) return it.kt0 + t;
     return it.kt0 + t + (t >= it.n1 ? it.gap : 0);
   };
   const int rb = wave >> hp_log2;         // this wave's 32-row block of the positions
@@ -482,8 +486,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     __syncthreads();
     n_tiles = s_ntiles;
   }
-  const bool use_bm = FLEX && fx.bmask != nullptr;
-  if (FLEX && use_bm) {
+  const bool use_bm = XM && fx.bmask != nullptr;
+  if (XM && use_bm) {
     // (the first barrier: every wave is past its reads of the last list)
     __syncthreads();
     if (wave == 0) {
@@ -517,13 +521,13 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   }
   auto tile_at = [&](int idx) -> int {
     if constexpr (SPARSE) return s_list[idx];
-    if (FLEX && use_bm) return __builtin_amdgcn_readfirstlane((int)s_blist[idx]) & 0x7fff;
+    if (XM && use_bm) return __builtin_amdgcn_readfirstlane((int)s_blist[idx]) & 0x7fff;
     return walk_tile(itg, idx);
   };
   // flex with a block mask: every pair of the idx-th walked tile is in the
   // same document
   auto bm_full = [&](int idx) {
-    return FLEX && use_bm && __builtin_amdgcn_readfirstlane((int)s_blist[idx]) < 0;
+    return XM && use_bm && __builtin_amdgcn_readfirstlane((int)s_blist[idx]) < 0;
   };
   // block-sparse: does this wave's 64-row block keep the idx-th walked tile?
   // (uniform per wave; a wave skips the products and softmax of a tile it
@@ -1010,7 +1014,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     }
     int cls = tile_class(geo, j0, kFwdTileN);
     // beside a window, a tile inside the prefix is seen whole by every row
-    if (FLEX && pe > 0)
+    if (XM && pe > 0)
       cls = j0 + kFwdTileN <= pe || cls == kTileFull ? kTileFull : kTilePartial;
     if (cls == kTilePartial || (FLEX && force_partial)) {
       // key j0 + half*4 + c is allowed iff c lies in [t_lo, t_lo + width);
@@ -1018,7 +1022,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       // unsigned compare and one select per score
       const int t_lo = rr.lo - (j0 + half * 4);
       const unsigned width = (unsigned)max(rr.hi - rr.lo, 0);
-      if (FLEX && pe > 0) {
+      if (XM && pe > 0) {
         // ... or c < t_pe (the prefix)
         const int t_pe = pe_row - (j0 + half * 4);
 #pragma unroll
@@ -1338,19 +1342,23 @@ hipError_t launch_fwd_flex(void* O, const void* Q, const void* K,
   fx.qk_scale = f->qk_scale > 0.f ? f->qk_scale : 1.f / sqrtf((float)D);
   log_fwd_grid(fx.bias ? "attn_fwd_bf16_kernel[flex+bias]" : "attn_fwd_bf16_kernel[flex]", D,
                grid, kFwdThreads, total, n_wg);
-  // the bias tile costs 32 registers per lane: a kernel of its own
+  if (log_enabled() && (fx.bmask || (fx.prefix > 0 && window > 0)))
+    log_line("  (mask extensions: %s)", fx.bmask ? "block mask" : "prefix beside a window");
+  // the bias tile costs 32 registers per lane, the mask extensions some
+  // more: kernels of their own
+  const bool xm = fx.bmask != nullptr || (fx.prefix > 0 && window > 0);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kFwdThreads), 0, stream, (__bf16*)O,
+                       (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
+                       B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
+                       0.f, fx, (const uint8_t*)nullptr, n_wg, hl);
+  };
   if (fx.bias)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, false>), dim3(grid),
-                       dim3(kFwdThreads), 0, stream, (__bf16*)O,
-                       (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
-                       B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                       0.f, fx, (const uint8_t*)nullptr, n_wg, hl);
+    xm ? go(attn_fwd_bf16_kernel<D, true, true, false, true>)
+       : go(attn_fwd_bf16_kernel<D, true, true, false, false>);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false, false>), dim3(grid),
-                       dim3(kFwdThreads), 0, stream, (__bf16*)O,
-                       (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, LSE,
-                       B, H, Hkv, Sq, Sk, causal, window, input_pos, k_lengths,
-                       0.f, fx, (const uint8_t*)nullptr, n_wg, hl);
+    xm ? go(attn_fwd_bf16_kernel<D, true, false, false, true>)
+       : go(attn_fwd_bf16_kernel<D, true, false, false, false>);
   return hipGetLastError();
 }
 

@@ -18,6 +18,12 @@ Workloads (the shapes of the pages' use cases; no dataset is involved):
                       N(0,1) mean plus 0.5*N(0,1) per token.  Stands in for the
                       image self-attention of a 1024x1024 image at 64x64
                       tokens with 32 heads, whose trained weights are absent.
+* ``gqa_documents``   the ``gqa_causal`` tensors (same seed, same draws) as
+                      packed training sequences: each of the two 4096-token
+                      sequences is cut into 16 documents at 15 distinct cut
+                      points drawn uniformly from 1..4095 (ids 0..15 in order,
+                      ``meta["doc"]`` (B, S) int32); attention stays causal
+                      inside each document.
 * ``decode_split``    B=64 sequences, H=32, Hkv=8, one query per head, D=128,
                       lengths uniform in [512, 32768], cache padded to 32768,
                       n_splits=8, TILE_N=64.
@@ -178,6 +184,25 @@ def decode_paged(B=64, H=32, Hkv=8, D=128, smin=512, smax=32768, block_size=16,
                             num_blocks=num_blocks, max_blocks=max_blocks, seed=seed))
 
 
+def document_ids(B: int, S: int, n_docs: int, seed: int) -> torch.Tensor:
+    """(B, S) int32 ids of packed sequences: each of the B rows of S tokens is
+    cut into n_docs documents at n_docs - 1 distinct cut points drawn
+    uniformly from 1..S-1; the documents take ids 0, 1, ... in order."""
+    gen = torch.Generator().manual_seed(seed)
+    out = torch.empty(B, S, dtype=torch.int32)
+    for b in range(B):
+        cuts = torch.sort(torch.randperm(S - 1, generator=gen)[:n_docs - 1] + 1).values
+        edges = [0] + cuts.tolist() + [S]
+        for d, (a, c) in enumerate(zip(edges, edges[1:])):
+            out[b, a:c] = d
+    return out
+
+
+def documents_of(w: Prefill, n_docs: int = 16, seed: int = 9) -> torch.Tensor:
+    """The ``gqa_documents`` ids for a prefill of that shape, on its device."""
+    return document_ids(w.q.shape[0], w.k.shape[2], n_docs, seed).to(w.q.device)
+
+
 def make(name: str, device="cpu"):
     """The five named workloads at their full sizes."""
     if name == "tiny_f32":
@@ -190,6 +215,11 @@ def make(name: str, device="cpu"):
         return prefill_random(1, 32, 8, 2048, 16384, 128, torch.bfloat16, seed=3,
                               causal=True, window=4096, input_pos=14336,
                               k_lengths=[16384], device=device, name=name)
+    if name == "gqa_documents":
+        w = make("gqa_causal", device=device)
+        w.name = name
+        w.meta["doc"] = documents_of(w)
+        return w
     if name == "image_clustered":
         return image_clustered(device=device)
     if name == "decode_split":
@@ -199,5 +229,5 @@ def make(name: str, device="cpu"):
     raise KeyError(name)
 
 
-NAMES = ("tiny_f32", "gqa_causal", "window_offset", "image_clustered", "decode_split",
-         "decode_paged")
+NAMES = ("tiny_f32", "gqa_causal", "gqa_documents", "window_offset", "image_clustered",
+         "decode_split", "decode_paged")

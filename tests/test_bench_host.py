@@ -39,3 +39,23 @@ def test_multi_gpu_request_exits_with_message():
 def test_timing_stats_median_and_min():
     assert bench.timing_stats([3.0, 1.0, 2.0]) == {"mean": 2.0, "median": 2.0, "min": 1.0}
     assert bench.timing_stats([4.0, 1.0, 2.0, 3.0]) == {"mean": 2.5, "median": 2.5, "min": 1.0}
+
+
+def test_document_flops_matches_oracle_mask():
+    import torch
+    from scaled_dot_product_attn_amd import workloads as wl
+    doc = wl.document_ids(2, 300, 5, seed=3)
+    pairs = sum(int(ora.flex_mask(300, 300, True, doc_q=doc[b].numpy(),
+                                  doc_kv=doc[b].numpy()).sum()) for b in range(2))
+    assert bench.document_flops(doc, 3, 64) == 4 * 64 * 3 * pairs
+    # one document is plain causal attention
+    one = torch.zeros(1, 100, dtype=torch.int32)
+    assert bench.document_flops(one, 1, 1) == 4 * 100 * 101 // 2
+
+
+def test_document_ids_recipe():
+    from scaled_dot_product_attn_amd import workloads as wl
+    doc = wl.document_ids(2, 4096, 16, seed=9)
+    for row in doc.tolist():
+        assert row[0] == 0 and row[-1] == 15
+        assert all(b - a in (0, 1) for a, b in zip(row, row[1:]))
