@@ -58,6 +58,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 #include "../../include/attn.h"
 #include "attn_common.h"
 #include "attn_host.h"
@@ -1386,15 +1388,32 @@ __global__ __launch_bounds__(256) void attn_build_block_mask_kernel(
   const int j = kb * kFwdTileN + lane;
   const bool key_exists = j < Sk;
   const uint64_t exists = __builtin_amdgcn_ballot_w64(key_exists);
-  const int dkv = doc_kv && key_exists ? doc_kv[(size_t)b * Sk + j] : 0;
   const int r_end = min(kFwdTileN, Sq - qb * kFwdTileN);
-  bool some = false, every = true;
-  for (int r = 0; r < r_end; ++r) {
+  const int i_lane = qb * kFwdTileN + lane;  // this lane's row, for the row-side loads
+  const int dkv = doc_kv && key_exists ? doc_kv[(size_t)b * Sk + j] : 0;
+  const int dq_lane = doc_q && lane < r_end ? doc_q[(size_t)b * Sq + i_lane] : 0;
+  // Quick rejections, each a sufficient condition for no attending pair: no
+  // live row or key, or (documents) disjoint ranges of document ids.
+  bool empty = qb * kFwdTileN >= ql || kb * kFwdTileN >= kl;
+  if (doc_q && !empty) {
+    int qmin = lane < r_end ? dq_lane : INT_MAX, qmax = lane < r_end ? dq_lane : INT_MIN;
+    int kmin = key_exists ? dkv : INT_MAX, kmax = key_exists ? dkv : INT_MIN;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      qmin = min(qmin, __shfl_xor(qmin, o));
+      qmax = max(qmax, __shfl_xor(qmax, o));
+      kmin = min(kmin, __shfl_xor(kmin, o));
+      kmax = max(kmax, __shfl_xor(kmax, o));
+    }
+    empty = qmax < kmin || kmax < qmin;
+  }
+  bool some = false, every = !empty;
+  for (int r = 0; r < r_end && !empty; ++r) {
     const int i = qb * kFwdTileN + r;
     const long long p = (long long)input_pos + i;
     bool ok = (!causal || j <= p) && (window <= 0 || j >= p - window + 1);
     ok = (ok || j < prefix) && j < kl && i < ql;
-    if (doc_q) ok = ok && doc_q[(size_t)b * Sq + i] == dkv;
+    if (doc_q) ok = ok && __builtin_amdgcn_readlane(dq_lane, r) == dkv;
     const uint64_t m = __builtin_amdgcn_ballot_w64(ok && key_exists);
     some |= m != 0;
     every &= m == exists;

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn {
 
 namespace sparse {
@@ -28,6 +30,7 @@ constexpr int kBlock = 64;       // tokens per query / key block
 constexpr int kMaxBlocks = 4096; // key blocks per head the quantile sort holds
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -43,112 +46,163 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
+// One exchange step of the radius reduction (see attn_block_stats_kernel):
+// over lane bit O, keep CNT of the 2 CNT partials and add the partner's.
+template <int CNT, int O>
+__device__ inline void halve_sum(float* dist, int lane) {
+  if constexpr (O >= 1) {
+    const bool upper = (lane & O) != 0;
+#pragma unroll
+    for (int k = 0; k < CNT; ++k) {
+      const float keep = upper ? dist[k + CNT] : dist[k];
+      const float send = upper ? dist[k] : dist[k + CNT];
+      dist[k] = keep + __shfl_xor(send, O);
+    }
+    halve_sum<CNT / 2, O / 2>(dist, lane);
+  }
+}
+
 }  // namespace sparse
 
 using namespace sparse;
 
 // Per (key block, KV head, batch): centroid, per-dimension min / max, radius.
 // stats layout per (b, g): c (nk, D), lo (nk, D), hi (nk, D), r (nk).
-// One pass over the block: 16-byte loads with 16 (D = 128) or 8 (D = 64)
-// consecutive threads per row, each thread holding RPT rows x 8 d-values in
-// registers; per-dimension sums / min / max reduce over the rows by lane
-// shuffles and then across the four waves in LDS, row distances to the
-// centroid over the row's threads by shuffles.
+// One wave per key block, four blocks per workgroup: lane l holds the 16-byte
+// chunk l % CPR (8 d-values) of rows l / CPR + RPW i, all NI loads issued
+// before any arithmetic; per-dimension sums / min / max reduce over the
+// lanes of a chunk by shuffles, row distances to the centroid over a row's
+// lanes.  The wave also writes the bf16 operand planes of the score kernel
+// (the centroid, or for the box bound its midpoint and half-width, each as
+// three bf16 planes whose sum is the float32 value), once per block instead
+// of once per query-block workgroup.
 template <int D>
 __global__ __launch_bounds__(256) void attn_block_stats_kernel(
-    const __bf16* __restrict__ K, float* __restrict__ stats, int Hkv, int Sk,
-    int nk) {
-  constexpr int CPR = D / 8;           // 16-byte chunks per row
-  constexpr int RPP = 256 / CPR;       // rows one pass of the workgroup covers
-  constexpr int RPT = kBlock / RPP;    // rows per thread
-  __shared__ float s_part[3][4][D];
-  __shared__ float s_c[D];
-  __shared__ float s_r[4];
-  const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = tid % CPR;             // this thread's chunk: d = 8 c .. 8 c + 7
+    const __bf16* __restrict__ K, float* __restrict__ stats, __bf16* __restrict__ planes,
+    int B, int Hkv, int Sk, int nk, int box) {
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int RPW = 64 / CPR;     // rows one load instruction of the wave covers
+  constexpr int NI = kBlock / RPW;  // loads per lane
+  const int lane = threadIdx.x & 63;
+  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long long)B * Hkv * nk) return;
+  const int kb = (int)(w % nk);
+  const long long bg = w / nk;      // b * Hkv + g
+  const int c = lane % CPR, r0 = lane / CPR;
   const int j0 = kb * kBlock;
   const int n = min(kBlock, Sk - j0);
-  const __bf16* kp = K + ((size_t)(b * Hkv + g) * Sk + j0) * D;
-  float x[RPT][8];
+  const __bf16* kp = K + ((size_t)bg * Sk + j0) * D + c * 8;
+  u32x4_t v[NI];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = tid / CPR + i * RPP;
-    u32x4_t v = {0, 0, 0, 0};
-    if (r < n) v = *(const u32x4_t*)(kp + (size_t)r * D + c * 8);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      x[i][2 * w] = bf16_lo(v[w]);
-      x[i][2 * w + 1] = bf16_hi(v[w]);
-    }
+  for (int i = 0; i < NI; ++i) {
+    const int r = r0 + i * RPW;
+    v[i] = r < n ? *(const u32x4_t*)(kp + (size_t)r * D) : u32x4_t{0, 0, 0, 0};
   }
-  // per-dimension partials over this thread's rows, then over the wave's rows
-  float su[8], lo[8], hi[8];
+  auto elem = [&](int i, int e) {
+    return (e & 1) ? bf16_hi(v[i][e >> 1]) : bf16_lo(v[i][e >> 1]);
+  };
+  // rows past n load as zeros: they add nothing to the sums and are kept out
+  // of the minima / maxima and the radius by selects (no branches)
+  float su[8], lo[8], hi[8], cen[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     su[e] = 0.f;
     lo[e] = INFINITY;
     hi[e] = -INFINITY;
+  }
+  auto accumulate = [&](auto whole) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      if (tid / CPR + i * RPP < n) {
-        su[e] += x[i][e];
-        lo[e] = fminf(lo[e], x[i][e]);
-        hi[e] = fmaxf(hi[e], x[i][e]);
+    for (int i = 0; i < NI; ++i) {
+      const bool ok = whole || r0 + i * RPW < n;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = elem(i, e);
+        su[e] += x;
+        lo[e] = fminf(lo[e], ok ? x : INFINITY);
+        hi[e] = fmaxf(hi[e], ok ? x : -INFINITY);
       }
     }
+  };
+  if (n == kBlock)
+    accumulate(std::true_type{});
+  else
+    accumulate(false);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
 #pragma unroll
     for (int o = CPR; o < 64; o <<= 1) {
       su[e] += __shfl_xor(su[e], o);
       lo[e] = fminf(lo[e], __shfl_xor(lo[e], o));
       hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], o));
     }
+    cen[e] = su[e] / (float)n;
   }
+  float* base = stats + (size_t)bg * nk * (3 * D + 1);
   if (lane < CPR) {
+    float* cp = base + (size_t)kb * D + c * 8;
+    *(float4*)cp = make_float4(cen[0], cen[1], cen[2], cen[3]);
+    *(float4*)(cp + 4) = make_float4(cen[4], cen[5], cen[6], cen[7]);
+    float* lp = cp + (size_t)nk * D;
+    *(float4*)lp = make_float4(lo[0], lo[1], lo[2], lo[3]);
+    *(float4*)(lp + 4) = make_float4(lo[4], lo[5], lo[6], lo[7]);
+    float* hp = lp + (size_t)nk * D;
+    *(float4*)hp = make_float4(hi[0], hi[1], hi[2], hi[3]);
+    *(float4*)(hp + 4) = make_float4(hi[4], hi[5], hi[6], hi[7]);
+  }
+  // radius: the largest squared distance of a row to the centroid.  Row i's
+  // distance is the sum of its CPR lanes' partials; the NI partials of a
+  // lane reduce over those lanes by halving exchanges (at the step over lane
+  // bit o the lane keeps the half of its rows it is responsible for and adds
+  // the partner's partials of the same rows), so each lane ends with the
+  // whole distance of one row (NI >= CPR).
+  static_assert(NI >= CPR, "a row per lane after the exchanges");
+  float dist[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float t2 = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      s_part[0][wave][c * 8 + e] = su[e];
-      s_part[1][wave][c * 8 + e] = lo[e];
-      s_part[2][wave][c * 8 + e] = hi[e];
+      const float t = elem(i, e) - cen[e];
+      t2 = __builtin_fmaf(t, t, t2);
     }
+    dist[i] = r0 + i * RPW < n ? t2 : 0.f;
   }
-  __syncthreads();
-  float* base = stats + (size_t)(b * Hkv + g) * nk * (3 * D + 1);
-  if (tid < D) {
-    float sm = 0.f, l = INFINITY, h = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      sm += s_part[0][w][tid];
-      l = fminf(l, s_part[1][w][tid]);
-      h = fmaxf(h, s_part[2][w][tid]);
-    }
-    const float cen = sm / (float)n;
-    s_c[tid] = cen;
-    base[(size_t)kb * D + tid] = cen;
-    base[(size_t)nk * D + (size_t)kb * D + tid] = l;
-    base[(size_t)2 * nk * D + (size_t)kb * D + tid] = h;
-  }
-  __syncthreads();
-  // radius: the largest squared distance of a row to the centroid
+  halve_sum<NI / 2, CPR / 2>(dist, lane);
   float m = 0.f;
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    float dist = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = x[i][e] - s_c[c * 8 + e];
-      dist = __builtin_fmaf(t, t, dist);
-    }
-#pragma unroll
-    for (int o = 1; o < CPR; o <<= 1) dist += __shfl_xor(dist, o);
-    if (tid / CPR + i * RPP < n) m = fmaxf(m, dist);
-  }
+  for (int k = 0; k < NI / CPR; ++k) m = fmaxf(m, dist[k]);
   m = wave_max(m);
-  if (lane == 0) s_r[wave] = m;
-  __syncthreads();
-  if (tid == 0) {
-    const float r = fmaxf(fmaxf(s_r[0], s_r[1]), fmaxf(s_r[2], s_r[3]));
-    base[(size_t)3 * nk * D + kb] = sqrtf(r);
+  if (lane == 0) base[(size_t)3 * nk * D + kb] = sqrtf(m);
+  // operand planes: plane p of (b, g) is (nk, D) bf16 at planes + (bg * 6 + p) * nk * D
+  if (lane < CPR) {
+    __bf16* pp = planes + ((size_t)bg * 6 * nk + kb) * D + c * 8;
+    auto split3 = [&](const float (&x)[8], int p0) {
+      bf16x8_t q0, q1, q2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 h0 = (__bf16)x[e];
+        const float r1 = x[e] - (float)h0;
+        const __bf16 h1 = (__bf16)r1;
+        q0[e] = h0;
+        q1[e] = h1;
+        q2[e] = (__bf16)(r1 - (float)h1);
+      }
+      *(bf16x8_t*)(pp + (size_t)p0 * nk * D) = q0;
+      *(bf16x8_t*)(pp + (size_t)(p0 + 1) * nk * D) = q1;
+      *(bf16x8_t*)(pp + (size_t)(p0 + 2) * nk * D) = q2;
+    };
+    if (!box) {
+      split3(cen, 0);
+    } else {
+      float mid[8], rad[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        mid[e] = (lo[e] + hi[e]) * 0.5f;
+        rad[e] = (hi[e] - lo[e]) * 0.5f;
+      }
+      split3(mid, 0);
+      split3(rad, 3);
+    }
   }
 }
 
@@ -192,11 +246,12 @@ __global__ __launch_bounds__(256) void attn_block_quantile_kernel(
 
 // Block scores on the matrix cores.  A workgroup of four waves takes
 // four query blocks of one (query head, batch); wave w scores block 4x + w
-// against every key block.  Per chunk of 64 key blocks the workgroup stages
-// the centroids in LDS split into three bf16 planes, c = c0 + c1 + c2 (each
-// the bf16 rounding of what the previous ones leave), so that the bf16 MFMA
-// products q.c0 + q.c1 + q.c2 with exact bf16 q and float32 accumulation give
-// q.c to within 2^-27 |q||c| per term, float32 quality.  S = Q C^T comes out
+// against every key block.  Per chunk of 64 key blocks the workgroup copies
+// into LDS the centroids as three bf16 planes, c = c0 + c1 + c2 (each the
+// bf16 rounding of what the previous ones leave, written by the statistics
+// kernel), so that the bf16 MFMA products q.c0 + q.c1 + q.c2 with exact bf16
+// q and float32 accumulation give q.c to within 2^-27 |q||c| per term,
+// float32 quality.  S = Q C^T comes out
 // in the accumulator layout (lane: one key block, 16 query rows per 32 x 32
 // tile), so the log-sum-exp over the 64 query rows is in-lane plus one
 // exchange with lane ^ 32; the rescue term adds ||q_i|| r_b beta_b before
@@ -209,8 +264,8 @@ template <int D, bool BOX>
 __global__ __launch_bounds__(256) void attn_block_scores_kernel(
     float* __restrict__ base_out, float* __restrict__ rescue_out,
     const __bf16* __restrict__ Q, const float* __restrict__ stats,
-    const float* __restrict__ quant, int H, int Hkv, int Sq, int nq, int nk,
-    float scale) {
+    const __bf16* __restrict__ planes, const float* __restrict__ quant, int H, int Hkv,
+    int Sq, int nq, int nk, float scale) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   typedef float f32x16_t __attribute__((ext_vector_type(16)));
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -262,42 +317,36 @@ __global__ __launch_bounds__(256) void attn_block_scores_kernel(
   auto row_of = [&](int rt, int r) { return rt * 32 + (r >> 2) * 8 + half * 4 + (r & 3); };
 
   const float* st = stats + (size_t)(b * Hkv + g) * nk * (3 * D + 1);
-  // radius quantiles of the head (centroid scores only; the box bound has none)
-  const float r_low = BOX ? 0.f : quant[(size_t)(b * Hkv + g) * 2];
-  const float r_high = BOX ? 0.f : quant[(size_t)(b * Hkv + g) * 2 + 1];
+  const __bf16* pls = planes + (size_t)(b * Hkv + g) * 6 * nk * D;
+  // radius quantiles of the head (the rescue scores only)
+  const float r_low = !BOX && rescue_out ? quant[(size_t)(b * Hkv + g) * 2] : 0.f;
+  const float r_high = !BOX && rescue_out ? quant[(size_t)(b * Hkv + g) * 2 + 1] : 0.f;
   const size_t orow = ((size_t)(b * H + h) * nq + (live ? a : 0)) * nk;
 
   for (int c0 = 0; c0 < nk; c0 += kBlock) {
-    // stage centroids c0 .. c0 + 63 (zeros past nk) as three bf16 planes
+    // copy the planes of key blocks c0 .. c0 + 63 (zeros past nk) into LDS
     __syncthreads();  // the previous chunk's reads are done
-    auto split3 = [&](const f32x4_t c, char* dst) {
-      bf16x4_t p0, p1, p2;
+    // (in batches of three planes: a thread's loads of a batch are all in
+    // flight before its stores)
+    constexpr int CH = D / 8;                    // 16-byte chunks per row
+    constexpr int PER = 3 * kBlock * CH / 256;   // chunks per thread per batch
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const __bf16 h0 = (__bf16)c[e];
-        const float r1 = c[e] - (float)h0;
-        const __bf16 h1 = (__bf16)r1;
-        const float r2 = r1 - (float)h1;
-        p0[e] = h0;
-        p1[e] = h1;
-        p2[e] = (__bf16)r2;
+    for (int p0 = 0; p0 < NPL; p0 += 3) {
+      u32x4_t v[PER];
+#pragma unroll
+      for (int t = 0; t < PER; ++t) {
+        const int x = tid + t * 256;
+        const int pl = p0 + x / (kBlock * CH), rem = x % (kBlock * CH);
+        const int kb = rem / CH, ch = rem % CH;
+        v[t] = c0 + kb < nk ? *(const u32x4_t*)(pls + ((size_t)pl * nk + c0 + kb) * D + ch * 8)
+                            : u32x4_t{0, 0, 0, 0};
       }
-      *(bf16x4_t*)(dst) = p0;
-      *(bf16x4_t*)(dst + PLANE) = p1;
-      *(bf16x4_t*)(dst + 2 * PLANE) = p2;
-    };
-    for (int x = tid; x < kBlock * (D / 4); x += 256) {
-      const int kb = x / (D / 4), d4 = x % (D / 4);
-      const bool in = c0 + kb < nk;
-      char* dst = s_c + kb * ROW + d4 * 8;
-      const size_t off = (size_t)(c0 + kb) * D + d4 * 4;
-      if constexpr (BOX) {
-        const f32x4_t lo = in ? *(const f32x4_t*)(st + (size_t)nk * D + off) : f32x4_t{};
-        const f32x4_t hi = in ? *(const f32x4_t*)(st + (size_t)2 * nk * D + off) : f32x4_t{};
-        split3((lo + hi) * 0.5f, dst);
-        split3((hi - lo) * 0.5f, dst + 3 * PLANE);
-      } else {
-        split3(in ? *(const f32x4_t*)(st + off) : f32x4_t{}, dst);
+#pragma unroll
+      for (int t = 0; t < PER; ++t) {
+        const int x = tid + t * 256;
+        const int pl = p0 + x / (kBlock * CH), rem = x % (kBlock * CH);
+        const int kb = rem / CH, ch = rem % CH;
+        *(u32x4_t*)(s_c + pl * PLANE + kb * ROW + ch * 16) = v[t];
       }
     }
     __syncthreads();
@@ -330,33 +379,37 @@ __global__ __launch_bounds__(256) void attn_block_scores_kernel(
                                : fminf(fmaxf((r - r_low) / (r_high - r_low), 0.f), 1.f);
         w = r * beta;
       }
-      float m1 = -INFINITY, m2 = -INFINITY;
+      // log-sum-exp over the block's rows (rows past its end count as -inf),
+      // in base 2: exp2 and log2 are single instructions
+      constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.69314718055994531f;
+      const float sc = scale * kLog2e;
+      auto lse = [&](auto with_rescue) {
+        float t[2][16];
+        float mx = -INFINITY;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_of(rt, r);
-          if (row >= nrows) continue;
-          m1 = fmaxf(m1, acc[rt][r] * scale);
-          m2 = fmaxf(m2, __builtin_fmaf(s_qn[wave][row], w, acc[rt][r]) * scale);
-        }
-      m1 = fmaxf(m1, __shfl_xor(m1, 32));
-      m2 = fmaxf(m2, __shfl_xor(m2, 32));
-      float s1 = 0.f, s2 = 0.f;
+          for (int r = 0; r < 16; ++r) {
+            const int row = row_of(rt, r);
+            float x = acc[rt][r];
+            if constexpr (decltype(with_rescue)::value) x = __builtin_fmaf(s_qn[wave][row], w, x);
+            t[rt][r] = row < nrows ? x * sc : -INFINITY;
+            mx = fmaxf(mx, t[rt][r]);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float sm = 0.f;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_of(rt, r);
-          if (row >= nrows) continue;
-          s1 += __expf(acc[rt][r] * scale - m1);
-          s2 += __expf(__builtin_fmaf(s_qn[wave][row], w, acc[rt][r]) * scale - m2);
-        }
-      s1 += __shfl_xor(s1, 32);
-      s2 += __shfl_xor(s2, 32);
-      if (half == 0 && kb < nk) {
-        base_out[orow + kb] = m1 + __logf(s1);
-        if (!BOX && rescue_out) rescue_out[orow + kb] = m2 + __logf(s2);
+          for (int r = 0; r < 16; ++r) sm += __builtin_amdgcn_exp2f(t[rt][r] - mx);
+        sm += __shfl_xor(sm, 32);
+        return (mx + __builtin_amdgcn_logf(sm)) * kLn2;
+      };
+      const float l1 = lse(std::false_type{});
+      if (half == 0 && kb < nk) base_out[orow + kb] = l1;
+      if (!BOX && rescue_out) {
+        const float l2 = lse(std::true_type{});
+        if (half == 0 && kb < nk) rescue_out[orow + kb] = l2;
       }
     }
   }
@@ -364,14 +417,23 @@ __global__ __launch_bounds__(256) void attn_block_scores_kernel(
 
 // One wave per block-mask row (a query block of one head): relative (mode 0),
 // top-k (mode 1) or diagonal band (mode 2); with `accumulate` the result is
-// ORed into keep.
+// ORed into keep.  Top-k ranks each entry against the whole row, which the
+// wave first copies into its own LDS (rows up to kMaskRow entries).
+constexpr int kMaskRow = 1024;
 __global__ __launch_bounds__(256) void attn_block_mask_kernel(
     uint8_t* __restrict__ keep, const float* __restrict__ scores, long long rows,
     int nq, int nk, int mode, float ln_alpha, int k, int diagonal, int accumulate) {
+  __shared__ float s_row[4][kMaskRow];
   const long long rw = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (rw >= rows) return;
   const float* s = scores ? scores + rw * nk : nullptr;
+  // (the wave reads back only what it wrote; a wave's LDS accesses run in
+  // program order)
+  const bool staged = mode == 1 && nk <= kMaskRow;
+  float* row = s_row[threadIdx.x >> 6];
+  if (staged)
+    for (int j = lane; j < nk; j += 64) row[j] = s[j];
   uint8_t* out = keep + rw * nk;
   float thr = 0.f;
   if (mode == 0) {
@@ -387,9 +449,16 @@ __global__ __launch_bounds__(256) void attn_block_mask_kernel(
     } else if (mode == 1) {
       const float x = s[j];
       int rank = 0;
-      for (int t = 0; t < nk; ++t) {
-        const float y = s[t];
-        rank += (y > x) || (y == x && t < j);
+      if (staged) {
+        for (int t = 0; t < nk; ++t) {
+          const float y = row[t];
+          rank += (y > x) || (y == x && t < j);
+        }
+      } else {
+        for (int t = 0; t < nk; ++t) {
+          const float y = s[t];
+          rank += (y > x) || (y == x && t < j);
+        }
       }
       on = rank < k;
     } else {
@@ -399,10 +468,19 @@ __global__ __launch_bounds__(256) void attn_block_mask_kernel(
   }
 }
 
+// Workspace: the block statistics (float32), the radius quantiles, the bf16
+// operand planes (six per (b, g): enough for the box bound's two values).
+static size_t ws_stats_bytes(int B, int Hkv, size_t nk, int D) {
+  return ((size_t)B * Hkv * nk * (3 * D + 1) * sizeof(float) + 255) / 256 * 256;
+}
+static size_t ws_quant_bytes(int B, int Hkv) {
+  return ((size_t)B * Hkv * 2 * sizeof(float) + 255) / 256 * 256;
+}
+
 size_t block_scores_workspace_bytes(int B, int Hkv, int Sk, int D) {
   const size_t nk = (size_t)(Sk + kBlock - 1) / kBlock;
-  const size_t stats = (size_t)B * Hkv * nk * (3 * D + 1) * sizeof(float);
-  return (stats + 255) / 256 * 256 + ((size_t)B * Hkv * 2 * sizeof(float) + 255) / 256 * 256;
+  return ws_stats_bytes(B, Hkv, nk, D) + ws_quant_bytes(B, Hkv) +
+         ((size_t)B * Hkv * 6 * nk * D * 2 + 255) / 256 * 256;
 }
 
 template <int D>
@@ -412,26 +490,30 @@ static hipError_t launch_scores_d(float* base, float* rescue, const void* Q,
                                   void* ws, hipStream_t stream) {
   const int nq = (Sq + kBlock - 1) / kBlock, nk = (Sk + kBlock - 1) / kBlock;
   float* stats = (float*)ws;
-  const size_t sbytes = ((size_t)B * Hkv * nk * (3 * D + 1) * sizeof(float) + 255) / 256 * 256;
-  float* quant = (float*)((char*)ws + sbytes);
-  hipLaunchKernelGGL(attn_block_stats_kernel<D>, dim3(nk, Hkv, B), dim3(256), 0, stream,
-                     (const __bf16*)K, stats, Hkv, Sk, nk);
+  float* quant = (float*)((char*)ws + ws_stats_bytes(B, Hkv, nk, D));
+  __bf16* planes = (__bf16*)((char*)quant + ws_quant_bytes(B, Hkv));
+  const long long nblk = (long long)B * Hkv * nk;
+  hipLaunchKernelGGL(attn_block_stats_kernel<D>, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0,
+                     stream, (const __bf16*)K, stats, planes, B, Hkv, Sk, nk, kind == 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale = 1.f / sqrtf((float)D);
   if (kind == 1) {
     hipLaunchKernelGGL((attn_block_scores_kernel<D, true>), dim3((nq + 3) / 4, H, B), dim3(256),
                        0, stream, base, nullptr, (const __bf16*)Q, (const float*)stats,
-                       (const float*)nullptr, H, Hkv, Sq, nq, nk, scale);
+                       (const __bf16*)planes, (const float*)nullptr, H, Hkv, Sq, nq, nk, scale);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(attn_block_quantile_kernel, dim3(Hkv, B), dim3(256), 0, stream,
-                     stats, quant, Hkv, nk, D, low, high);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // the radius quantiles only weigh the rescue scores
+  if (rescue) {
+    hipLaunchKernelGGL(attn_block_quantile_kernel, dim3(Hkv, B), dim3(256), 0, stream,
+                       stats, quant, Hkv, nk, D, low, high);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((attn_block_scores_kernel<D, false>), dim3((nq + 3) / 4, H, B), dim3(256), 0,
                      stream, base, rescue, (const __bf16*)Q, (const float*)stats,
-                     (const float*)quant, H, Hkv, Sq, nq, nk, scale);
+                     (const __bf16*)planes, (const float*)quant, H, Hkv, Sq, nq, nk, scale);
   return hipGetLastError();
 }
 
