@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "prefill": ["scaled_dot_product_attn_amd/csrc/attn_fwd_bf16.hip",
                 "scaled_dot_product_attn_amd/csrc/attn_common.h"],
     "decode": ["scaled_dot_product_attn_amd/csrc/attn_decode.hip"],
+    "decode_paged": ["scaled_dot_product_attn_amd/csrc/attn_decode.hip"],
 }
 
 
@@ -578,7 +579,7 @@ def main():
             "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms["decode_paged"], 4),
             "config": "same sequences as decode, cache (num_blocks, 16, 8, 128) with "
                       "shuffled physical blocks",
-            "roofline": roof("hbm", gbs, PEAK_HBM_GBS, "GB/s", None),
+            "roofline": roof("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("decode_paged")),
         }
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")

@@ -160,9 +160,8 @@ typedef struct attn_flex {
   int block_mask_B;
 } attn_flex_t;
 
-/* Classes of a BlockMask entry (Tylo.jl "Primitives", BlockMask: the key
- * blocks holding any unmasked element, and which of those are fully
- * unmasked). */
+/* Classes of a BlockMask entry (Tylo.jl "Primitives", BlockMask): no pair
+ * of the (query block, key block) attends, some do, or all do. */
 #define ATTN_BLOCK_EMPTY 0
 #define ATTN_BLOCK_PARTIAL 1
 #define ATTN_BLOCK_FULL 2

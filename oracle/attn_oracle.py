@@ -515,8 +515,9 @@ def flex_ref(Q, K, V, causal: bool = False, window: int = 0, input_pos: int = 0,
 
 def block_mask_ref(ok, tile_m: int = 64, tile_n: int = 64) -> np.ndarray:
     """Coarse block classes of a boolean (..., Sq, Sk) pair mask (Tylo.jl
-    "Primitives", ``BlockMask`` / ``build_block_mask``: per query block, the key
-    blocks holding any unmasked element, and which of those are fully unmasked).
+    "Primitives", ``BlockMask`` / ``build_block_mask``): each (query block, key
+    block) pair is empty, partial or full according to how many of its pairs
+    attend.
 
     Query block qb covers the rows [qb * tile_m, (qb + 1) * tile_m) that exist
     (< Sq), key block kb the keys [kb * tile_n, (kb + 1) * tile_n) that exist

@@ -7,9 +7,12 @@
 // sliding_window_mask with -inf at blocked positions).
 //
 // Work decomposition
-//   One workgroup = 8 waves = 256 query rows of one (batch, head); each wave
-//   owns 32 rows.  The workgroup walks the 64-key tiles its rows can see
-//   (empty tiles are never visited).
+//   One workgroup = 8 waves = 256 query rows; each wave owns 32 rows.  With
+//   grouped-query attention the rows are hp query heads (the largest power
+//   of two up to 8 dividing H / Hkv) of one KV head at 256 / hp positions, so
+//   the heads share every K/V tile.  The workgroup walks the 64-key tiles its
+//   rows can see (empty tiles are never visited); a persistent workgroup
+//   loads the next item's queries and first tiles during its last product.
 //
 // Ping-pong between two wave groups.  Waves 0-3 (group A) and 4-7 (group B)
 // sit one per SIMD each, so every SIMD holds one wave of each group.  Each
@@ -46,7 +49,11 @@
 // and the mask extended by a prefix (prefix_lm = CausalMask | PrefixMask),
 // per-batch query lengths (q_lengths) and document ids (DocumentMask).  The
 // bias tile of a lane's row is loaded at the start of the M-phase that computes
-// the tile's scores, document ids of the keys are loaded into LDS with K.
+// the tile's scores, document ids of the keys are loaded into LDS with K.  The
+// mask extensions (XM) have an instantiation of their own: a precomputed
+// BlockMask (Tylo.jl "Primitives", BlockMask / build_block_mask: empty key
+// blocks are skipped, fully unmasked ones need no document mask) and a prefix
+// beside a sliding window (two key intervals per row).
 //
 // The block-sparse instantiation (SPARSE) keeps register staging: four waves
 // without groups, K and V^T written to two-tile rings by the threads.
