@@ -59,6 +59,42 @@ constexpr int kQTile = 64;         // query rows per step of the dK/dV kernel
 constexpr int kDqRows = 128;       // query rows per dQ workgroup
 constexpr int kDqKeys = 32;        // keys per step of the dQ kernel
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, out-of-range reads = 0
+
+// Direct global-to-LDS 16-byte load issued from inline assembly: lane l of
+// the wave fills the 16 bytes at LDS address lds_addr + 16 l from byte
+// voffset of the buffer.  With the compiler's builtin for this instruction the
+// compiler, which cannot tell these LDS writes from the kernel's LDS reads,
+// waits for every outstanding load before the next LDS read, i.e. for the
+// whole next stage in the middle of a step; here the kernels wait themselves,
+// before the barrier that publishes the stage.  Five wait states first: the
+// descriptor may have just been written by a vector instruction, which a
+// memory instruction may read only five wait states later, and no wait is
+// inserted before an instruction inside inline assembly (M0, written just
+// before, needs one).
+__device__ inline void lds_load16(u32x4_t rsrc, uint32_t lds_addr, int voffset) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr)
+      : "memory");
+}
+
+// A raw buffer descriptor (no stride, num_records bytes, out-of-range reads
+// return zero) in four scalar registers, for lds_load16.
+__device__ inline u32x4_t buffer_desc_s(const void* base, int num_records) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4_t d;
+  d[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+  d[2] = __builtin_amdgcn_readfirstlane((uint32_t)num_records);
+  d[3] = (uint32_t)kRsrcWord3;
+  return d;
+}
+
+__device__ inline uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
 #ifndef KBWD_OP_DEPTH
 #define KBWD_OP_DEPTH 4
 #endif
@@ -250,10 +286,11 @@ void attn_bwd_dkdv8_kernel(
   // (s / 64) % 8, lane s % 64, and holds row s / CPR at chunk s % CPR: the
   // lane loads the logical chunk that the swizzle puts there.  Rows past Sq
   // read zeros through the resource's range check.  L2 and delta (64 floats
-  // each) go through registers.
+  // each) come the same way, by 16 lanes of the last wave; rows past Sq read
+  // zeros there too, and contribute nothing (their Q and dO rows are zero, so
+  // dP = 0, dS = P (0 - 0) = 0 and dO^T P = 0).
   constexpr int NCH = kQTile * CPR / kThreads8;
   static_assert(NCH * kThreads8 == kQTile * CPR, "whole tiles per stage");
-  float sl = 0.f, sd = 0.f;
   auto advance = [&](int& hh, int& q) {
     if (++q == nq) {
       q = 0;
@@ -264,10 +301,8 @@ void attn_bwd_dkdv8_kernel(
     const int h = g * G + hh;
     const int i0 = (qt_lo + q) * kQTile;
     const size_t rb = (size_t)(b * H + h) * Sq;
-    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(Q + rb * D), (short)0, Sq * D * 2, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(dO + rb * D), (short)0, Sq * D * 2, kRsrcWord3);
+    const u32x4_t qrs = buffer_desc_s(Q + rb * D, Sq * D * 2);
+    const u32x4_t ors = buffer_desc_s(dO + rb * D, Sq * D * 2);
     char* st = smem + L::kOffStage + buf * L::kStage;
 #pragma unroll
     for (int n = 0; n < NCH; ++n) {
@@ -276,25 +311,19 @@ void attn_bwd_dkdv8_kernel(
       const int c = (slot % CPR) ^ bwd_swizzle<D>(r);
       const int off = ((i0 + r) * D + c * 8) * 2;
       const int at = (n * 8 + wave_u) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          qrs, (__attribute__((address_space(3))) void*)(st + L::kOffQ + at), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ors, (__attribute__((address_space(3))) void*)(st + L::kOffO + at), 16, off, 0, 0, 0);
+      lds_load16(qrs, lds_addr_of(st + L::kOffQ + at), off);
+      lds_load16(ors, lds_addr_of(st + L::kOffO + at), off);
     }
-    if (tid < kQTile) {
-      const int i = i0 + tid;
-      sl = i < Sq ? L2[rb + i] : INFINITY;
-      sd = i < Sq ? delta[rb + i] : 0.f;
+    if (wave_u == kThreads8 / 64 - 1 && lane < kQTile / 4) {
+      const u32x4_t lrs = buffer_desc_s(L2 + rb, Sq * 4);
+      const u32x4_t drs = buffer_desc_s(delta + rb, Sq * 4);
+      lds_load16(lrs, lds_addr_of(st + L::kOffL), (i0 + lane * 4) * 4);
+      lds_load16(drs, lds_addr_of(st + L::kOffDel), (i0 + lane * 4) * 4);
     }
   };
-  auto stash = [&](int buf) {
-    char* st = smem + L::kOffStage + buf * L::kStage;
-    if (tid < kQTile) {
-      ((float*)(st + L::kOffL))[tid] = sl;
-      ((float*)(st + L::kOffDel))[tid] = sd;
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  };
+  // this thread's loads of the stage complete (the barrier that follows
+  // publishes it)
+  auto stash = [&](int) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   const float sl2 = scale * kLog2e;
   if (n_items > 0) fetch(0, 0, 0);
@@ -555,11 +584,6 @@ void attn_bwd_dq_kernel(
   }
   const int nvalid = geo.union_hi - geo.union_lo;
   const size_t valid_base = ((size_t)(b * Hkv + g) * Sk + geo.union_lo) * D;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(K + valid_base), (short)0, nvalid * D * 2, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(V + valid_base), (short)0, nvalid * D * 2, kRsrcWord3);
-
   // staging: K and V rows go from global memory straight into LDS
   // (buffer_load ... lds, as in the dK/dV kernel): slot s of a tensor is
   // written by instruction s / 256, wave (s / 64) % 4, lane s % 64 and holds
@@ -567,6 +591,8 @@ void attn_bwd_dq_kernel(
   constexpr int NCH = kDqKeys * CPR / kThreads;
   static_assert(NCH * kThreads == kDqKeys * CPR, "whole tiles per stage");
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const u32x4_t kds = buffer_desc_s(K + valid_base, nvalid * D * 2);
+  const u32x4_t vds = buffer_desc_s(V + valid_base, nvalid * D * 2);
   auto fetch = [&](int kt, int buf) {
     const int rel0 = kt * kDqKeys - geo.union_lo;
     char* st = smem + buf * L::kStage;
@@ -577,10 +603,8 @@ void attn_bwd_dq_kernel(
       const int c = (slot % CPR) ^ bwd_swizzle<D>(r);
       const int off = ((rel0 + r) * D + c * 8) * 2;
       const int at = (n * 4 + wave_u) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          krs, (__attribute__((address_space(3))) void*)(st + L::kOffK + at), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vrs, (__attribute__((address_space(3))) void*)(st + L::kOffV + at), 16, off, 0, 0, 0);
+      lds_load16(kds, lds_addr_of(st + L::kOffK + at), off);
+      lds_load16(vds, lds_addr_of(st + L::kOffV + at), off);
     }
   };
   // this thread's direct loads complete (the barrier that follows publishes the stage)

@@ -6,7 +6,8 @@ this architecture a memory instruction may read a scalar register written by
 a vector instruction (v_readlane, v_readfirstlane, ...) only five wait states
 later, and the compiler inserts no wait before an instruction it cannot see
 inside an asm block; a descriptor reloaded just before such a load would be
-read stale.  The test compiles the forward source and checks every such load.
+read stale.  The test compiles the sources that issue them and checks every
+such load.
 """
 import os
 import re
@@ -63,11 +64,12 @@ def test_hazard_scan_finds_a_planted_case():
 
 
 @pytest.mark.timeout(600)
-def test_direct_to_lds_loads_wait_for_scalar_operands():
-    src = os.path.join(_build.CSRC, "attn_fwd_bf16.hip")
+@pytest.mark.parametrize("source", ["attn_fwd_bf16.hip", "attn_bwd.hip"])
+def test_direct_to_lds_loads_wait_for_scalar_operands(source):
+    src = os.path.join(_build.CSRC, source)
     flags = [f for f in _build.CFLAGS if f != "-fPIC"]
     with tempfile.TemporaryDirectory() as d:
-        out = os.path.join(d, "fwd.s")
+        out = os.path.join(d, "k.s")
         subprocess.run([_build.HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", out],
                        check=True, capture_output=True)
         lines = open(out).read().split("\n")
