@@ -606,6 +606,13 @@ FLEX_CASES = {
                              mods=dict(prefix=70, q_lengths=[300])),
     "prefix_window_offset": dict(shape=(2, 4, 2, 200, 500, 128), window=96, input_pos=300,
                                  k_lengths=[500, 420], mods=dict(prefix=70, docs=3)),
+    # the mask-extension instantiation with the bias tile and every score mod
+    "prefix_window_everything": dict(shape=(2, 8, 2, 330, 330, 128), window=100, input_pos=20,
+                                     k_lengths=[330, 290], qscale=2.0,
+                                     mods=dict(prefix=50, softcap=15.0, alibi=True,
+                                               bias=(2, 1), docs=3, q_lengths=[300, 330])),
+    "prefix_window_d64_g1": dict(shape=(1, 4, 4, 300, 300, 64), window=40,
+                                 mods=dict(prefix=90, softcap=5.0)),
     "everything": dict(shape=(2, 8, 2, 300, 330, 128), input_pos=30, k_lengths=[330, 250],
                        qscale=2.0,
                        mods=dict(softcap=15.0, alibi=True, bias=(2, 1), docs=4, prefix=40,
@@ -710,6 +717,24 @@ def test_build_block_mask_bitexact(name):
     ref = _oracle_block_mask(*shape, mods, kw)
     np.testing.assert_array_equal(bm.cpu().numpy(), ref)
     assert (ref == 0).any() and (ref == 2).any()
+
+
+def test_flex_block_mask_with_score_mods():
+    # BlockMask + bias tile + soft-cap + ALiBi (the BIAS + XM instantiation)
+    _say("flex block_mask with bias, soft-cap, ALiBi")
+    B, H, Hkv, S, D = 2, 8, 2, 330, 128
+    w = _flex_inputs(B, H, Hkv, S, S, D, seed=67, qscale=2.0)
+    docs = _docs(B, S, 5, 68)
+    g = torch.Generator().manual_seed(69)
+    mods = dict(doc_q=docs, doc_kv=docs, softcap=15.0,
+                alibi_slopes=-torch.rand(H, generator=g) * 0.1,
+                bias=torch.randn(B, 1, S, S, generator=g))
+    kw = dict(causal=True, window=0, input_pos=0, k_lengths=None)
+    bm = _gpu_block_mask(B, S, S, dict(doc_q=docs, doc_kv=docs), kw)
+    O, L = _run_flex(w, **kw, **mods, block_mask=bm)
+    _check_flex(w, O, L, **kw, **mods)
+    O0, L0 = _run_flex(w, **kw, **mods)
+    assert torch.equal(O, O0) and torch.equal(L, L0)
 
 
 @pytest.mark.parametrize("name", list(BLOCK_MASK_CASES))
