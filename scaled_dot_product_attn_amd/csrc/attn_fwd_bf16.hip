@@ -89,6 +89,7 @@ constexpr int kFwdThreads = kFwdWaves * 64;
 constexpr int kFwdTileM = kFwdWaves * 32;  // query rows per workgroup
 constexpr int kFwdTileN = 64;              // keys per tile
 constexpr float kLazyRescale = 8.0f;       // log2 headroom before m is raised
+constexpr float kOptSum = 65536.0f;        // largest half-row sum of P the optimistic step keeps
 constexpr int kFwdOpDepth = KFWD_OP_DEPTH; // LDS operand reads in flight per wave
 // Word 3 of a gfx9-family buffer resource (32-bit data format, no swizzle):
 // a raw buffer whose out-of-range reads return zero.
@@ -175,6 +176,18 @@ __device__ inline void lds_load16(u32x4_t rsrc, uint32_t lds_addr, int voffset) 
   // (M0, written just before, needs one).
   asm volatile(
       "s_nop 4\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr)
+      : "memory");
+}
+
+// The same load when the descriptor registers were written long before (by
+// the time of the item's first loads): only M0, written by a scalar
+// instruction just before, needs its one wait state.
+__device__ inline void lds_load16_m0(u32x4_t rsrc, uint32_t lds_addr, int voffset) {
+  asm volatile(
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %0, %1, 0 offen lds"
       :
       : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr)
@@ -278,10 +291,15 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // empty, bit 15 set for FULL
   __shared__ int16_t s_blist[XM ? kSparseMaxTiles : 1];
   __shared__ int s_ntiles;
+  // per item parity: the sequence number of an item on which some wave's
+  // optimistic softmax step failed
+  __shared__ int s_fail[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // (uniform per wave; the block-sparse kernel keeps the plain form, whose
+  // registers the compiler allocates better there)
+  const int wave = PP ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int grp = PP ? wave >> 2 : 0;     // 0: group A, 1: group B
   const int gtid = tid & (GT - 1);        // thread index within the group
   const int lrow = lane & 31;  // query row (within the wave) this lane owns
@@ -430,7 +448,37 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   bf16x8_t qreg[KSTEPS];
   int pf_round = -1;  // the round whose Q and first tiles are already loaded
   int t0 = 0;         // tiles walked so far: ring slot of tile idx is t0 + idx
-  for (int round = 0; round < rounds; ++round) {
+  // Optimistic softmax bookkeeping (ping-pong kernels): items are numbered
+  // in the order they are walked (seq); a wave whose optimistic step fails
+  // on an item records its number in s_fail, read by every wave after the
+  // next barrier that follows the item (the next item's prologue, or the
+  // end).  A failed item is walked again with exact steps only, as is every
+  // later item of the workgroup (opt_ok).
+  bool opt_ok = true;
+  int seq = 0;
+  int pending = -1, pending_round = 0;  // the item not yet checked, if any
+  if (tid == 0) s_fail[0] = s_fail[1] = -1;
+  auto pending_failed = [&]() -> bool {
+    const bool f = pending >= 0 &&
+                   __builtin_amdgcn_readfirstlane(s_fail[pending & 1]) == pending;
+    pending = -1;
+    return f;
+  };
+  for (int round = 0;; ++round) {
+  if (round >= rounds) {
+    // the last item's check; walk it again if it failed
+    if (PP && pending >= 0) {
+      const int pr = pending_round;
+      __syncthreads();
+      if (pending_failed()) {
+        opt_ok = false;
+        pf_round = -1;
+        round = pr - 1;
+        continue;
+      }
+    }
+    break;
+  }
   const int lid = lid_of(round);
   if (lid < 0) continue;
   const ItemGeo itg = item_geo(lid);
@@ -561,32 +609,37 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       (void*)(V + valid_base), (short)0, nvalid * D * 2, kBufferRsrcWord3);
 
   // ---- direct-to-LDS staging (ping-pong kernels) ----
-  // A tile's K rows are kInstrK instructions, its V rows kInstrV; wave w
-  // issues instructions w, w + 8, ...  Lane l of instruction n fills the 16
-  // bytes at the instruction's LDS address + 16 l, so each lane fetches the
-  // chunk the layout puts in that slot: for K, slot s holds row s / kChunksK,
-  // chunk s % kChunksK (the pad chunk re-reads the row's last chunk); for V,
-  // row s / (D / 8) and the chunk the swizzle stores there.
+  // A tile's K rows are kInstrK instructions, its V rows kInstrV = kInstrK - 1.
+  // Wave w issues the K instructions w + 8 t and the V instructions w + 8 t
+  // (t < DMA_KV), and wave 0 also the last K instruction, so the sequence of
+  // each wave is fixed and needs no branch.  Lane l of an instruction fills
+  // the 16 bytes at the instruction's LDS address + 16 l, so each lane
+  // fetches the chunk the layout puts in that slot: for K, slot s holds row
+  // s / kChunksK, chunk s % kChunksK (the pad chunk re-reads the row's last
+  // chunk); for V, row s / (D / 8) and the chunk the swizzle stores there.
   constexpr int NDMA = L::kInstrK + L::kInstrV;
-  constexpr int DMA_PER_WAVE = (NDMA + kFwdWaves - 1) / kFwdWaves;
-  int dma_voff[DMA_PER_WAVE];
+  constexpr int DMA_KV = L::kInstrV / kFwdWaves;
+  static_assert(L::kInstrV % kFwdWaves == 0 && L::kInstrK == L::kInstrV + 1,
+                "every wave issues DMA_KV K and DMA_KV V instructions, wave 0 one more");
+  auto k_off = [&](int n) {
+    const int sl = n * 64 + lane;
+    const int r = sl / L::kChunksK;
+    const int c = min(sl % L::kChunksK, L::kChunksK - 2);
+    return (r * D + c * 8) * 2;
+  };
+  auto v_off = [&](int n) {
+    const int sl = n * 64 + lane;
+    const int r = sl / (D / 8);
+    const int c = (sl % (D / 8)) ^ v_swizzle<D>(r);
+    return (r * D + c * 8) * 2;
+  };
+  int dma_koff[DMA_KV], dma_voff[DMA_KV];
 #pragma unroll
-  for (int t = 0; t < DMA_PER_WAVE; ++t) {
-    const int n = wave + kFwdWaves * t;
-    int off = 0;
-    if (n < L::kInstrK) {
-      const int sl = n * 64 + lane;
-      const int r = sl / L::kChunksK;
-      const int c = min(sl % L::kChunksK, L::kChunksK - 2);
-      off = (r * D + c * 8) * 2;
-    } else if (n < NDMA) {
-      const int sl = (n - L::kInstrK) * 64 + lane;
-      const int r = sl / (D / 8);
-      const int c = (sl % (D / 8)) ^ v_swizzle<D>(r);
-      off = (r * D + c * 8) * 2;
-    }
-    dma_voff[t] = off;
+  for (int t = 0; t < DMA_KV; ++t) {
+    dma_koff[t] = k_off(wave + kFwdWaves * t);
+    dma_voff[t] = v_off(wave + kFwdWaves * t);
   }
+  const int dma_klast = k_off(L::kInstrK - 1);
   // V^T operand reads: lane l of a transposing read points at 4 d-values of
   // one row; per 32-wide d block db its offset inside a 16-row slice
   int vt_off[DBLK];
@@ -721,24 +774,31 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // (kt: the key tile; slot: its place in the rings; ulo: the first key of
   // the range the descriptors cover)
   auto dma_issue = [&](const u32x4_t& kd, const u32x4_t& vd, const u32x4_t& dd, bool doc,
-                       int ulo, int kt, int slot) {
+                       int ulo, int kt, int slot, bool fresh) {
     const int rel = (kt * kFwdTileN - ulo) * D * 2;  // in the valid range
     const uint32_t kdst = lds_addr_of(smem + (slot % L::kRingK) * L::kBytesK);
     const uint32_t vdst = lds_addr_of(smem + L::kOffVd + (slot % L::kRingV) * L::kBytesVd);
+    // Descriptors built just before (the next item's first tiles) need the
+    // full wait before the first load; in the mask-extension kernels the
+    // compiler reloads descriptors spilled to vector lanes before each load.
+    auto load = [&](bool full, const u32x4_t& d, uint32_t dst, int off) {
+      if (full || XM) lds_load16(d, dst, off);
+      else lds_load16_m0(d, dst, off);
+    };
+    load(fresh, kd, kdst + wave_u * 1024, dma_koff[0] + rel);
 #pragma unroll
-    for (int t = 0; t < DMA_PER_WAVE; ++t) {
-      const int n = wave_u + kFwdWaves * t;
-      if (n < L::kInstrK)
-        lds_load16(kd, kdst + n * 1024, dma_voff[t] + rel);
-      else if (n < NDMA)
-        lds_load16(vd, vdst + (n - L::kInstrK) * 1024, dma_voff[t] + rel);
-    }
+    for (int t = 1; t < DMA_KV; ++t)
+      load(false, kd, kdst + (wave_u + kFwdWaves * t) * 1024, dma_koff[t] + rel);
+#pragma unroll
+    for (int t = 0; t < DMA_KV; ++t)
+      load(false, vd, vdst + (wave_u + kFwdWaves * t) * 1024, dma_voff[t] + rel);
+    if (wave_u == 0) load(false, kd, kdst + (L::kInstrK - 1) * 1024, dma_klast + rel);
     if (FLEX && doc && wave_u == kFwdWaves - 1 && lane < kFwdTileN / 4)
       lds_load16(dd, lds_addr_of(smem + L::kOffDocD + (slot % L::kRingV) * L::kBytesDoc),
                  (kt * kFwdTileN - ulo + lane * 4) * 4);
   };
   auto dma_tile = [&](int idx) {
-    dma_issue(kdesc, vdesc, ddesc, has_doc, itg.vlo, tile_at(idx), t0 + idx);
+    dma_issue(kdesc, vdesc, ddesc, has_doc, itg.vlo, tile_at(idx), t0 + idx, false);
   };
   // Wait until this wave's loads of the tile after the current one have
   // landed, leaving those of the tile after that in flight (loads complete in
@@ -1000,6 +1060,15 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // flex scores are already in base-2 units
   const float sl2 = FLEX ? (transform ? 1.f : fx.qk_scale * kLog2e) : scale_log2;
 
+  // optimistic softmax steps on this item (ALiBi raises the scores tile
+  // after tile towards the diagonal: exact steps only)
+  const bool opt_item = opt_ok && !(FLEX && has_alibi);
+  // lanes of this wave whose P exceeded the optimistic bound (or was not a
+  // number) on some tile of the item
+  uint64_t fail_bits = 0;
+  // m is raised when the tile max exceeds it by more than this (exact steps:
+  // 2^8; optimistic steps: only a row without one takes its first max)
+  const float raise_above = opt_item ? 1e30f : kLazyRescale;
   auto v_phase = [&](int idx) {
     if constexpr (PP) {
       // group A's V(idx) runs in window idx, group B's in window idx + 1:
@@ -1051,22 +1120,32 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
           }
       }
     }
-    // row max as a tree of three-input maxima (v_max3_f32)
-    float m16[11];
+    // The running max m.  Optimistic step (opt_item): a row takes its first
+    // tile max as m and keeps it; the tile max is taken only while some row
+    // of the wave has none yet.  Each row's result then depends only on its
+    // own scores (tiles it sees nothing of change nothing), whichever tiles
+    // the walk visits.  A P of a half row above kOptSum (checked below) makes
+    // the item fail; it is walked again with exact steps: m raised whenever
+    // the tile max exceeds it by more than 2^8 (P <= 256).
+    float mt = m_run;
+    if (!opt_item || __builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
+      // row max as a tree of three-input maxima (v_max3_f32)
+      float m16[11];
 #pragma unroll
-    for (int t = 0; t < 10; ++t) {
-      const int a = 3 * t, b = a + 1, c = a + 2;
-      m16[t] = __builtin_fmaxf(__builtin_fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]),
-                               s[c >> 4][c & 15]);
+      for (int t = 0; t < 10; ++t) {
+        const int a = 3 * t, b = a + 1, c = a + 2;
+        m16[t] = __builtin_fmaxf(__builtin_fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]),
+                                 s[c >> 4][c & 15]);
+      }
+      m16[10] = __builtin_fmaxf(s[1][14], s[1][15]);
+      float mx = __builtin_fmaxf(__builtin_fmaxf(m16[0], m16[1]), m16[2]);
+      mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[3]), m16[4]);
+      mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[5]), m16[6]);
+      mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[7]), m16[8]);
+      mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[9]), m16[10]);
+      mt = pair_max(mx) * sl2;
     }
-    m16[10] = __builtin_fmaxf(s[1][14], s[1][15]);
-    float mx = __builtin_fmaxf(__builtin_fmaxf(m16[0], m16[1]), m16[2]);
-    mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[3]), m16[4]);
-    mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[5]), m16[6]);
-    mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[7]), m16[8]);
-    mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[9]), m16[10]);
-    const float mt = pair_max(mx) * sl2;
-    const bool need = mt > m_run + kLazyRescale;
+    const bool need = mt > m_run + raise_above;
     if (__builtin_amdgcn_ballot_w64(need)) {
       // need == false leaves the lane unchanged (and avoids -inf - -inf)
       const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
@@ -1103,6 +1182,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < w; ++r) q16[r] = q16[r] + q16[r + w];
     const float psum = q16[0];
+    fail_bits |= __builtin_amdgcn_ballot_w64(!(psum <= kOptSum));
     l_run += psum;
     // Pin P here: left alone, the compiler sinks the exponentials past the
     // barrier into the next MFMA phase (their only user), which serialises
@@ -1117,6 +1197,17 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     }
   };
 
+  if (PP && n_tiles == 0 && pending >= 0) {
+    // (an item without tiles has no prologue barrier: one for the check)
+    const int pr = pending_round;
+    __syncthreads();
+    if (pending_failed()) {
+      opt_ok = false;
+      pf_round = -1;
+      round = pr - 1;
+      continue;
+    }
+  }
   if (n_tiles > 0) {
     if constexpr (PP) {
       // prologue: the first two tiles (group B also the third) in LDS,
@@ -1129,6 +1220,17 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      // the previous item's check: if it failed, walk it again (this item's
+      // loads have landed and nothing else of it has started)
+      {
+        const int pr = pending_round;
+        if (pending_failed()) {
+          opt_ok = false;
+          pf_round = -1;
+          round = pr - 1;
+          continue;
+        }
+      }
     } else {
       // prologue: the first tile in LDS, the second in flight
       fetch(tile_at(0));
@@ -1183,7 +1285,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
               has_doc ? nval * 4 : 0);
           const int cnt = min(group_b ? 3 : 2, nx.nwalk);
           for (int t = 0; t < cnt; ++t)
-            dma_issue(kd, vd, dd, has_doc, nx.vlo, walk_tile(nx, t), t0 + n_tiles + t);
+            dma_issue(kd, vd, dd, has_doc, nx.vlo, walk_tile(nx, t), t0 + n_tiles + t, t == 0);
         }
         pf_round = nr;
       }
@@ -1276,10 +1378,27 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
                           : -INFINITY;
     LSE[(size_t)(b * H + h) * Sq + qi] = lse;
   }
+  // (a P above the optimistic bound, or not a number: the item fails)
+  if (opt_item && fail_bits != 0 && lane == 0) s_fail[seq & 1] = seq;
   if constexpr (PP) {
-    t0 += n_tiles;
+    // (checked after the next barrier)
+    if (opt_item && n_tiles > 0) {
+      pending = seq;
+      pending_round = round;
+    }
+    ++seq;
+    t0 = __builtin_amdgcn_readfirstlane(t0 + n_tiles);
   } else {
     __syncthreads();  // LDS is reused by the next item
+    // (the item's check: every wave is past its softmax steps)
+    if (opt_item) {
+      pending = seq++;
+      if (pending_failed()) {
+        opt_ok = false;
+        --round;
+        continue;
+      }
+    }
   }
   }
 }

@@ -249,6 +249,80 @@ F32_CASES = [
 ]
 
 
+# ---------------------------------------------------------------------------
+# scores that rise from tile to tile
+# ---------------------------------------------------------------------------
+
+def _rising(w, step, every=1):
+    """All-ones queries and keys constant within each 64-key tile, so that the
+    scaled score rises by ``step`` (natural units) from one tile to the next:
+    in every ``every``-th KV head and its query heads (the others keep their
+    random values).  Past a rise of ~7.6 per tile the kernels' optimistic
+    softmax steps fail (a P above 2^16) and the item is walked again with
+    exact steps; past ~89 the exponentials overflow."""
+    B, H, Sq, D = w.q.shape
+    Hkv, Sk = w.k.shape[1], w.k.shape[2]
+    G = H // Hkv
+    a = (torch.arange(Sk) // 64).float() * (step / math.sqrt(D))
+    for g in range(0, Hkv, every):
+        w.k[:, g] = a[:, None].expand(Sk, D).to(w.k.dtype)
+        w.q[:, g * G:(g + 1) * G] = 1.0
+    return w
+
+
+# (B, H, Hkv, Sq, Sk, D, causal, window, input_pos, step, every)
+RISING_CASES = [
+    (1, 4, 2, 256, 256, 128, True, 0, 0, 12.0, 1),
+    (1, 4, 2, 300, 300, 128, False, 0, 0, 100.0, 1),      # exponentials overflow
+    (2, 8, 2, 333, 333, 64, True, 100, 0, 10.0, 2),       # window; rising and random heads
+    (1, 8, 1, 200, 456, 128, True, 0, 256, 3.0, 1),       # P x 2^4.3 per tile: fails late
+    (1, 8, 8, 130, 390, 128, False, 0, 0, 9.0, 3),
+]
+
+
+@pytest.mark.parametrize("case", RISING_CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"s{c[9]}")
+def test_prefill_rising_scores(case):
+    B, H, Hkv, Sq, Sk, D, causal, window, ip, step, every = case
+    _say(f"prefill rising scores {case}")
+    w = _rising(wl.prefill_random(B, H, Hkv, Sq, Sk, D, torch.bfloat16, seed=13, causal=causal,
+                                  window=window, input_pos=ip), step, every)
+    O, L = _run_prefill(w)
+    assert torch.isfinite(O.float()).all()
+    _check_prefill(w, O, L, TOL_BF16)
+
+
+def test_prefill_rising_scores_persistent():
+    # 512 work items, two per workgroup on a 256-CU GPU: an item that fails is
+    # walked again after the next item has started; every other KV head rises
+    _say("prefill rising scores, persistent schedule")
+    B, H, Hkv, S, D = 1, 64, 64, 2048, 64
+    w = _rising(wl.prefill_random(B, H, Hkv, S, S, D, torch.bfloat16, seed=14, causal=True),
+                20.0, 2)
+    O, L = _run_prefill(w)
+    assert torch.isfinite(O.float()).all()
+    rows = sorted(set(range(0, 70)) | set(range(S // 2 - 40, S // 2 + 40)) |
+                  set(range(S - 70, S)))
+    _check_prefill(w, O, L, TOL_BF16, rows=rows, threads=True)
+
+
+def test_flex_rising_scores():
+    # the flex instantiations (documents; bias and soft-cap) and the BlockMask one
+    B, H, Hkv, S, D = 2, 8, 2, 300, 128
+    w = _rising(_flex_inputs(B, H, Hkv, S, S, D, seed=15), 12.0)
+    docs = _docs(B, S, 3, 16)
+    g = torch.Generator().manual_seed(17)
+    kw = dict(causal=True, window=0, input_pos=0, k_lengths=None)
+    for mods in (dict(doc_q=docs, doc_kv=docs),
+                 dict(bias=torch.randn(B, 1, S, S, generator=g), softcap=400.0)):
+        _say(f"flex rising scores {sorted(mods)}")
+        O, L = _run_flex(w, **kw, **mods)
+        assert torch.isfinite(O.float()).all()
+        _check_flex(w, O, L, **kw, **mods)
+    bm = _gpu_block_mask(B, S, S, dict(doc_q=docs, doc_kv=docs), kw)
+    O1, L1 = _run_flex(w, **kw, doc_q=docs, doc_kv=docs, block_mask=bm)
+    _check_flex(w, O1, L1, **kw, doc_q=docs, doc_kv=docs)
+
+
 @pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "x".join(map(str, c[:6])))
 def test_prefill_f32_parity(case):
     B, H, Hkv, Sq, Sk, D, causal, window, ip, kl = case
