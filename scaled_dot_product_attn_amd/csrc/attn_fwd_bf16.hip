@@ -1060,9 +1060,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // flex scores are already in base-2 units
   const float sl2 = FLEX ? (transform ? 1.f : fx.qk_scale * kLog2e) : scale_log2;
 
+  // With a soft-cap of at most 60 / log2(e) every base-2 score lies in
+  // [-C, C], C = cap log2(e), and C serves as every row's running max from
+  // the start: P <= 1, and P >= 2^-2C is still a normal number.
+  const bool fixed_ref = FLEX && has_cap && fx.softcap * kLog2e <= 60.f;
   // optimistic softmax steps on this item (ALiBi raises the scores tile
-  // after tile towards the diagonal: exact steps only)
-  const bool opt_item = opt_ok && !(FLEX && has_alibi);
+  // after tile towards the diagonal: exact steps only, unless capped)
+  const bool opt_item = opt_ok && (!(FLEX && has_alibi) || fixed_ref);
+  if (opt_item && fixed_ref) m_run = fx.softcap * kLog2e;
   // lanes of this wave whose P exceeded the optimistic bound (or was not a
   // number) on some tile of the item
   uint64_t fail_bits = 0;

@@ -660,6 +660,9 @@ def _docs(B, S, n_docs, seed):
 FLEX_CASES = {
     "softcap": dict(shape=(2, 8, 2, 257, 257, 128), qscale=4.0, mods=dict(softcap=20.0)),
     "softcap_d64": dict(shape=(1, 4, 4, 300, 300, 64), qscale=4.0, mods=dict(softcap=5.0)),
+    # a cap above 60 / log2(e) (no fixed softmax reference) with ALiBi
+    "softcap_large_alibi": dict(shape=(1, 4, 2, 300, 300, 128), qscale=6.0,
+                                mods=dict(softcap=50.0, alibi=True)),
     "alibi_offset": dict(shape=(1, 8, 2, 200, 456, 128), causal=True, input_pos=256,
                          mods=dict(alibi=True)),
     "bias_full": dict(shape=(2, 4, 2, 257, 300, 128), causal=False, mods=dict(bias=(2, 4))),
