@@ -26,7 +26,8 @@
 //
 // Staging: K and V tiles go from HBM straight into LDS (buffer loads with the
 // LDS bit, issued by all eight waves two windows ahead of their use, at the
-// start of a V-phase), K into a three-slot ring of padded rows, V into a
+// start of a V-phase, each wave a fixed sequence without branches), K into a
+// three-slot ring of padded rows, V into a
 // four-slot ring of row-major rows read as V^T by transposing LDS reads.  K(k)
 // is read in window k, V(k) in window k+1, so a slot is rewritten only after
 // the barrier that ends its last reader's window; each wave waits for its own
@@ -58,10 +59,14 @@
 // The block-sparse instantiation (SPARSE) keeps register staging: four waves
 // without groups, K and V^T written to two-tile rings by the threads.
 //
-// Online softmax in base 2: t = s * log2(e) / sqrt(D), p = exp2(t - m).  The
-// running max m is only raised when a tile's max exceeds it by more than
-// 2^8 (p <= 256 otherwise), so the O rescale is skipped on almost all tiles;
-// O / l and m + log2 l are unchanged by which m is used.
+// Online softmax in base 2: t = s * log2(e) / sqrt(D), p = exp2(t - m); O / l
+// and m + log2 l are unchanged by which m is used, as long as no p overflows
+// or all of a row's underflow.  Optimistic steps: a row takes its first tile
+// max as m and keeps it, so the tile max is computed only while some row of
+// the wave has none; an item on which a half row's sum of p passes 2^16 (or
+// is not a number) is walked again with exact steps, which raise m whenever a
+// tile max exceeds it by more than 2^8.  Under a soft-cap of at most
+// 60 / log2(e) the cap itself bounds every score and serves as m.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
