@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_host.h"
 
@@ -399,28 +401,36 @@ void attn_bwd_dkdv8_kernel(
     // P = exp2(s * scale * log2e - L2), dS = P (dP - delta); lane's queries are
     // i0 + 32 qh + 8*(r/4) + 4*half + r%4
     u32x4_t pk[2], dsk[2];  // packed bf16, one 16-query k-step each
+    // (a separate copy for the steps that mask, so that the others carry no
+    // compare and select per element)
+    auto p_and_ds = [&](auto masked) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int qo = qh * 32 + r4 * 8 + half * 4;
-      const f32x4_t l4 = *(const f32x4_t*)(st + L::kOffL + qo * 4);
-      const f32x4_t d4 = *(const f32x4_t*)(st + L::kOffDel + qo * 4);
-      const int t0 = i0 + qo - r_lo;
-      float pv[4], dv[4];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int qo = qh * 32 + r4 * 8 + half * 4;
+        const f32x4_t l4 = *(const f32x4_t*)(st + L::kOffL + qo * 4);
+        const f32x4_t d4 = *(const f32x4_t*)(st + L::kOffDel + qo * 4);
+        const int t0 = i0 + qo - r_lo;
+        float pv[4], dv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = r4 * 4 + e;
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[e]));
-        if (partial) p = (unsigned)(t0 + e) < r_width ? p : 0.f;
-        pv[e] = p;
-        dv[e] = p * (dp[r] - d4[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = r4 * 4 + e;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[e]));
+          if constexpr (decltype(masked)::value) p = (unsigned)(t0 + e) < r_width ? p : 0.f;
+          pv[e] = p;
+          dv[e] = p * (dp[r] - d4[e]);
+        }
+        const int kq = r4 >> 1;
+        const int w = (r4 & 1) * 2;
+        pk[kq][w] = pack_bf16x2(pv[0], pv[1]);
+        pk[kq][w + 1] = pack_bf16x2(pv[2], pv[3]);
+        dsk[kq][w] = pack_bf16x2(dv[0], dv[1]);
+        dsk[kq][w + 1] = pack_bf16x2(dv[2], dv[3]);
       }
-      const int kq = r4 >> 1;
-      const int w = (r4 & 1) * 2;
-      pk[kq][w] = pack_bf16x2(pv[0], pv[1]);
-      pk[kq][w + 1] = pack_bf16x2(pv[2], pv[3]);
-      dsk[kq][w] = pack_bf16x2(dv[0], dv[1]);
-      dsk[kq][w + 1] = pack_bf16x2(dv[2], dv[3]);
-    }
+    };
+    if (partial)
+      p_and_ds(std::true_type{});
+    else
+      p_and_ds(std::false_type{});
     // the next tile's rows stream into the other stage during the rest
     if (it + 1 < n_items) fetch(nxt_hh, nxt_q, (it + 1) & 1);
     // dV^T += dO^T P, dK^T += Q^T dS (d x keys), k over this wave's 32
@@ -663,22 +673,29 @@ void attn_bwd_dq_kernel(
     const int t_lo = rr.lo - (j0 + half * 4);
     const unsigned width = (unsigned)max(rr.hi - rr.lo, 0);
     u32x4_t dsk[2 * KB];
+    // (a separate copy for the tiles that mask)
+    auto ds_of = [&](auto masked) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float dv[2];
+        for (int r = 0; r < 16; r += 2) {
+          float dv[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + e], sl2, -l2));
-          if (partial) {
-            const int c = kb * 32 + ((r + e) >> 2) * 8 + ((r + e) & 3);
-            p = (unsigned)(c - t_lo) < width ? p : 0.f;
+          for (int e = 0; e < 2; ++e) {
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + e], sl2, -l2));
+            if constexpr (decltype(masked)::value) {
+              const int c = kb * 32 + ((r + e) >> 2) * 8 + ((r + e) & 3);
+              p = (unsigned)(c - t_lo) < width ? p : 0.f;
+            }
+            dv[e] = p * (dp[kb][r + e] - del);
           }
-          dv[e] = p * (dp[kb][r + e] - del);
+          dsk[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dv[0], dv[1]);
         }
-        dsk[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dv[0], dv[1]);
-      }
+    };
+    if (partial)
+      ds_of(std::true_type{});
+    else
+      ds_of(std::false_type{});
     // dQ^T (d x queries) += K^T (d x keys) dS^T (keys x queries); operand i:
     // d block i / (2 KB), key k-step i % (2 KB).  K^T comes from the K rows by
     // transposing reads (tr_operand), in the key order dS^T has in the S^T
