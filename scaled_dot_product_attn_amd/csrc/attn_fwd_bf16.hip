@@ -1008,6 +1008,17 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // into the per-element FMAs.  Without bias, ALiBi and cap the factor goes
   // into the exponent instead (no pass over the scores).
   constexpr float kLog2e = 1.4426950408889634f;
+  // With a soft-cap of at most 60 / log2(e) every base-2 score lies in
+  // [-C, C], C = cap log2(e), and C serves as every row's running max from
+  // the start: P <= 1, and P >= 2^-2C is still a normal number.
+  const bool fixed_ref = FLEX && has_cap && fx.softcap * kLog2e <= 60.f;
+  // optimistic softmax steps on this item (ALiBi raises the scores tile
+  // after tile towards the diagonal: exact steps only, unless capped)
+  const bool opt_item = opt_ok && (!(FLEX && has_alibi) || fixed_ref);
+  // With C as the reference the transform yields the exponent's argument
+  // directly: A - B / (e + 1) - C = -B / (e + 1), one product instead of an
+  // FMA here and another in the softmax step.
+  const bool pre_shift = opt_item && fixed_ref;
   const bool transform = has_bias || has_alibi || has_cap;
   const float u = has_cap ? 2.f * kLog2e / fx.softcap : kLog2e;
   const float k_s = fx.qk_scale * u;
@@ -1037,7 +1048,15 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r)
           s[kb2][r] = __builtin_fmaf(bias_t[kb2][r], u, s[kb2][r]);
     }
-    if (has_cap) {
+    if (has_cap && pre_shift) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(s[kb2][r]);
+          s[kb2][r] = -cap_b * __builtin_amdgcn_rcpf(e + 1.f);
+        }
+    } else if (has_cap) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -1065,13 +1084,6 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
   // flex scores are already in base-2 units
   const float sl2 = FLEX ? (transform ? 1.f : fx.qk_scale * kLog2e) : scale_log2;
 
-  // With a soft-cap of at most 60 / log2(e) every base-2 score lies in
-  // [-C, C], C = cap log2(e), and C serves as every row's running max from
-  // the start: P <= 1, and P >= 2^-2C is still a normal number.
-  const bool fixed_ref = FLEX && has_cap && fx.softcap * kLog2e <= 60.f;
-  // optimistic softmax steps on this item (ALiBi raises the scores tile
-  // after tile towards the diagonal: exact steps only, unless capped)
-  const bool opt_item = opt_ok && (!(FLEX && has_alibi) || fixed_ref);
   if (opt_item && fixed_ref) m_run = fx.softcap * kLog2e;
   // lanes of this wave whose P exceeded the optimistic bound (or was not a
   // number) on some tile of the item
@@ -1137,44 +1149,50 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     // the walk visits.  A P of a half row above kOptSum (checked below) makes
     // the item fail; it is walked again with exact steps: m raised whenever
     // the tile max exceeds it by more than 2^8 (P <= 256).
-    float mt = m_run;
-    if (!opt_item || __builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
-      // row max as a tree of three-input maxima (v_max3_f32)
-      float m16[11];
+    // (with a fixed reference there is no max to take and nothing to rescale)
+    if (!(FLEX && pre_shift)) {
+      float mt = m_run;
+      if (!opt_item || __builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
+        // row max as a tree of three-input maxima (v_max3_f32)
+        float m16[11];
 #pragma unroll
-      for (int t = 0; t < 10; ++t) {
-        const int a = 3 * t, b = a + 1, c = a + 2;
-        m16[t] = __builtin_fmaxf(__builtin_fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]),
-                                 s[c >> 4][c & 15]);
+        for (int t = 0; t < 10; ++t) {
+          const int a = 3 * t, b = a + 1, c = a + 2;
+          m16[t] = __builtin_fmaxf(__builtin_fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]),
+                                   s[c >> 4][c & 15]);
+        }
+        m16[10] = __builtin_fmaxf(s[1][14], s[1][15]);
+        float mx = __builtin_fmaxf(__builtin_fmaxf(m16[0], m16[1]), m16[2]);
+        mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[3]), m16[4]);
+        mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[5]), m16[6]);
+        mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[7]), m16[8]);
+        mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[9]), m16[10]);
+        mt = pair_max(mx) * sl2;
       }
-      m16[10] = __builtin_fmaxf(s[1][14], s[1][15]);
-      float mx = __builtin_fmaxf(__builtin_fmaxf(m16[0], m16[1]), m16[2]);
-      mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[3]), m16[4]);
-      mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[5]), m16[6]);
-      mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[7]), m16[8]);
-      mx = __builtin_fmaxf(__builtin_fmaxf(mx, m16[9]), m16[10]);
-      mt = pair_max(mx) * sl2;
-    }
-    const bool need = mt > m_run + raise_above;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      // need == false leaves the lane unchanged (and avoids -inf - -inf)
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
-      m_run = need ? mt : m_run;
-      l_run *= alpha;
+      const bool need = mt > m_run + raise_above;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        // need == false leaves the lane unchanged (and avoids -inf - -inf)
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+        m_run = need ? mt : m_run;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db)
+        for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
     }
     const float mref = m_run == -INFINITY ? 0.f : m_run;
     // Wide schedule: only this wave of its SIMD runs vector work now, so the
     // latency of each dependent step must be covered by independent work:
     // all 32 exponents' arguments, then the 32 exponentials, then packing and
     // a tree of partial sums.
+    // (scores already relative to a fixed reference need no shift)
+    if (!(FLEX && pre_shift)) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb2][r] = __builtin_fmaf(s[kb2][r], sl2, -mref);
+        for (int r = 0; r < 16; ++r) s[kb2][r] = __builtin_fmaf(s[kb2][r], sl2, -mref);
+    }
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
