@@ -7,7 +7,9 @@ One step = one pass of the whole hot path over resident synthetic inputs:
     in [512, 32768] (cache 32768), n_splits=8               (attn_decode_ws)
 both launched on the same stream.  ``value`` is the prefill rate in TFLOP/s of
 algorithmic work (4*D flops per allowed (query, key) pair) divided by the
-prefill kernel's mean duration from HIP events over the timed steps; the
+prefill kernel's mean duration from HIP events over the timed steps (recorded
+with a device-scope release, so that an interval holds the kernel and not the
+L2 writeback a system-scope event forces after it); the
 decode rate in GB/s (K/V bytes of the valid keys, once per KV head, plus Q and
 O) is reported beside it.  The window/offset and clustered-image workloads are
 timed too, as extra lines of context, and so is the same decode batch stored
@@ -132,6 +134,52 @@ def device_info(torch) -> dict:
         info["peak_bf16_tflops_at_clock"] = round(
             info["cus"] * FLOP_PER_CLK_PER_CU_BF16 * info["clock_khz"] * 1e3 / 1e12, 1)
     return info
+
+
+class DeviceEvent:
+    """A timing event recorded with a device-scope release (hipEventCreateWithFlags
+    with hipEventReleaseToDevice).  A default event's record is a system-scope
+    release: it writes the L2's dirty lines back to HBM, so the interval it closes
+    also holds the writeback of what the kernel before it wrote (the prefill's
+    67 MB of O).  Work between two of these events is timed as the kernels take
+    it, as the profiler's kernel trace times it; the host sees results only after
+    a full synchronization, as before."""
+    _hip = None
+    RELEASE_TO_DEVICE = 0x40000000  # hipEventReleaseToDevice (hip_runtime_api.h)
+
+    def __init__(self):
+        import ctypes
+        if DeviceEvent._hip is None:
+            h = ctypes.CDLL("libamdhip64.so")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            DeviceEvent._hip = h
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        rc = DeviceEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.h),
+                                                      DeviceEvent.RELEASE_TO_DEVICE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags returned {rc}")
+
+    def record(self, stream):
+        rc = DeviceEvent._hip.hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord returned {rc}")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both recorded and completed)."""
+        ms = self._ct.c_float(0.0)
+        rc = DeviceEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime returned {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self.h and DeviceEvent._hip is not None:
+            DeviceEvent._hip.hipEventDestroy(self.h)
 
 
 def cpu_baseline(w, seconds: float):
@@ -302,7 +350,7 @@ def profile_prefill(torch, attn, w, args):
     torch.cuda.synchronize()
     ev = []
     for _ in range(args.steps):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s, e = DeviceEvent(), DeviceEvent()
         s.record(stream)
         run()
         e.record(stream)
@@ -438,7 +486,7 @@ def main():
         marks = {}
         for n in names:
             if record:
-                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s, e = DeviceEvent(), DeviceEvent()
                 s.record(stream)
             if n == "prefill":
                 run_prefill(pre, O, LSE)
