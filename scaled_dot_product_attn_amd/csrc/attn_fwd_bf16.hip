@@ -1245,8 +1245,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         dma_tile(0);
         if (n_tiles > 1) dma_tile(1);
         if (gb && n_tiles > 2) dma_tile(2);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // (a prefetched item's loads were waited for before the previous
+      // item's stores, which need no wait)
       __syncthreads();
       // the previous item's check: if it failed, walk it again (this item's
       // loads have landed and nothing else of it has started)
@@ -1316,10 +1318,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
             dma_issue(kd, vd, dd, has_doc, nx.vlo, walk_tile(nx, t), t0 + n_tiles + t, t == 0);
         }
         pf_round = nr;
+        // (the queries: the last products below take none)
+        load_q(qreg, nx);
       }
       m_phase(n_tiles, true, false);
-      // (the queries only once the last product has freed their registers)
-      if (nr < rounds) load_q(qreg, nx);
+      // The next item's loads have landed before this item's stores go out:
+      // a wait for them later would wait for the stores as well (one counter
+      // for both on this architecture).  vmcnt(0), expcnt and lgkmcnt left.
+      if (nr < rounds) __builtin_amdgcn_s_waitcnt(0x0F70);
     } else {
       for (int idx = 0; idx < n_tiles; ++idx) {
         m_phase(idx, idx > 0, true);
