@@ -1322,10 +1322,6 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
         load_q(qreg, nx);
       }
       m_phase(n_tiles, true, false);
-      // The next item's loads have landed before this item's stores go out:
-      // a wait for them later would wait for the stores as well (one counter
-      // for both on this architecture).  vmcnt(0), expcnt and lgkmcnt left.
-      if (nr < rounds) __builtin_amdgcn_s_waitcnt(0x0F70);
     } else {
       for (int idx = 0; idx < n_tiles; ++idx) {
         m_phase(idx, idx > 0, true);
@@ -1367,6 +1363,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
             *(u32x2_t*)(ost + lrow * L::kRowOh + d * 2) = w;
           }
         __builtin_amdgcn_wave_barrier();
+        // The next item's loads have landed before this item's stores go out
+        // (the staging above overlapped them): a wait for them later would
+        // wait for the stores as well (one counter for both on this
+        // architecture).
+        if (hd == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         constexpr int CHUNKS = D / 16;  // 16-byte chunks per half row
 #pragma unroll
         for (int i = 0; i < 32 * CHUNKS / 64; ++i) {
