@@ -59,3 +59,14 @@ def test_document_ids_recipe():
     for row in doc.tolist():
         assert row[0] == 0 and row[-1] == 15
         assert all(b - a in (0, 1) for a, b in zip(row, row[1:]))
+
+
+def test_timing_event_flag_is_the_device_scope_release():
+    # the bench's timing events are recorded with a device-scope release; the
+    # flag's value must be the runtime header's hipEventReleaseToDevice
+    import re
+    hdr = "/opt/rocm/include/hip/hip_runtime_api.h"
+    if not os.path.exists(hdr):
+        pytest.skip("no HIP headers")
+    m = re.search(r"#define\s+hipEventReleaseToDevice\s+(0x[0-9a-fA-F]+)", open(hdr).read())
+    assert m and int(m.group(1), 16) == bench.DeviceEvent.RELEASE_TO_DEVICE
